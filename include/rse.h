@@ -1,0 +1,278 @@
+/*
+ * rse.h -- C ABI of the MI355X (gfx950) sparse-embedding training hot path.
+ *
+ * The library implements one training step of dynamic sparse embeddings as
+ * four calls:
+ *
+ *   idmap_find_or_insert     feature ID -> row offset, inserting new IDs
+ *   blocks_grow              add a chunk of rows to the embedding blocks
+ *   embedding_bag_fwd        pooled gather (sum or mean) over CSR bags
+ *   embedding_bag_bwd_update merge duplicate-row gradients (sort + segmented
+ *                            reduction, no floating-point atomics) and apply
+ *                            a row-wise SGD / Adagrad / Adam update to the
+ *                            rows seen in the batch only
+ *
+ * Where the operations come from (web pages; title and section):
+ *  - "RecIS：阿里开源推荐系统统一训练框架" (pomoai.com), "Embedding Engine":
+ *    a dynamic two-level table -- an IDMap from feature ID to memory offset
+ *    over EmbeddingBlocks, contiguous chunked blocks that hold parameters and
+ *    optimizer state and grow without reallocating; same-attribute tables may
+ *    be merged into one.  "代码架构": a fused sparse-gradient update kernel
+ *    with fewer atomics and vectorised memory access for the lookup.
+ *  - "阿里 RecIS：搜广推训练的背景与难点" (muyuuuu.github.io): IDs are
+ *    arbitrary and sparse over a huge range (a dense or modulo-indexed table
+ *    either wastes memory or makes distinct IDs share a row); a lookup reads
+ *    only the indexed row and backward updates only that row.
+ *  - "DLRM模型的核心价值与工业落地挑战" (mokono.cn), section 2.1: EmbeddingBag
+ *    sum pooling over variable-length inputs with sparse gradients.
+ *  - "DLRM — Meta 把工业推荐模型拆成 4 个标准积木" (estelledc.github.io),
+ *    "踩过的坑" item 4: a sparse optimizer that updates only the rows seen.
+ *
+ * Conventions for every call:
+ *  - Every function returns an int status: RSE_OK (0) or a negative
+ *    RSE_ERR_* code; rse_status_str() names it.  No C++ exception crosses
+ *    the ABI.
+ *  - Pointers named d_* are device (HBM) pointers owned by the caller; the
+ *    library never allocates or frees device memory and writes only into
+ *    buffers it is given.  Other pointers are host pointers.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls enqueue work on it and return without synchronising, except the
+ *    query calls documented as synchronising.  All calls that touch one
+ *    map or one blocks object must be ordered on one stream (or the caller
+ *    synchronises between streams).
+ *  - Host-detectable errors (null pointer, negative size, workspace too
+ *    small, unsupported dim or dtype, too many tables) return at once and
+ *    enqueue nothing.  Conditions only the device can see (map full, not
+ *    enough free rows, malformed offsets) leave a sticky status in the
+ *    object (read with rse_idmap_status / rse_blocks_status) and commit
+ *    nothing from that call.
+ *  - Layouts: ids, row offsets and CSR offsets are int64.  A batch holds
+ *    n_tables * batch bags, table-major: bag j = t * batch + b spans
+ *    ids[bag_offsets[j] .. bag_offsets[j+1]).  Pooled outputs and upstream
+ *    gradients are fp32 [batch, n_tables, dim], sample-major.
+ */
+#ifndef RSE_H
+#define RSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status --- */
+enum {
+    RSE_OK = 0,
+    RSE_ERR_INVALID_ARG = -1,     /* null pointer, negative size, bad enum */
+    RSE_ERR_UNSUPPORTED = -2,     /* dim / dtype / optimizer not built */
+    RSE_ERR_WORKSPACE = -3,       /* workspace smaller than *_workspace_size */
+    RSE_ERR_IDMAP_FULL = -4,      /* a table's keys would exceed max_load */
+    RSE_ERR_NEED_GROW = -5,       /* not enough free rows: call blocks_grow */
+    RSE_ERR_CHUNK_TOO_SMALL = -6, /* chunk smaller than rows_per_chunk rows */
+    RSE_ERR_MAX_CHUNKS = -7,      /* chunk table full */
+    RSE_ERR_HIP = -8,             /* a HIP runtime call failed */
+    RSE_ERR_BAD_INPUT = -9,       /* device saw malformed offsets or ids */
+    RSE_ERR_TOO_MANY_ROWS = -10   /* more than RSE_MAX_ROWS rows */
+};
+
+#define RSE_MAX_TABLES 1024
+#define RSE_MAX_MERGED_TABLES 128           /* table id must fit in 7 bits */
+#define RSE_MAX_ROWS 4294967294LL            /* row offsets fit in 32 bits */
+
+enum { RSE_F32 = 0, RSE_BF16 = 1 };               /* weight storage type */
+enum { RSE_SGD = 0, RSE_ADAGRAD = 1, RSE_ADAM = 2 };
+enum { RSE_SUM = 0, RSE_MEAN = 1 };
+
+/* Name of a status code (static string). */
+const char* rse_status_str(int status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int rse_version(void);
+
+/* Opaque host-side handles.  Each refers to caller device memory that must
+ * outlive it. */
+typedef struct rse_idmap rse_idmap;
+typedef struct rse_blocks rse_blocks;
+
+/* --------------------------------------------------- EmbeddingBlocks --- */
+/*
+ * EmbeddingBlocks ("RecIS", "Embedding Engine"): rows of weights plus
+ * optimizer state in chunks of 2^rows_per_chunk_log2 rows.  Row r lives in
+ * chunk r >> rows_per_chunk_log2 at index r & (2^rows_per_chunk_log2 - 1);
+ * a row never moves once written, and adding a chunk leaves existing rows
+ * in place.
+ *
+ * Row layout (row_bytes, a multiple of 16): weights [dim] in the storage type,
+ * then fp32 state: Adagrad acc[dim]; Adam m[dim] then v[dim]; SGD none.
+ *
+ * A new row is initialised from its key: column c of a row with key k in
+ * map table t is q * 2^-27 (fp32, q = (h >> 40) - 2^23) or q * 2^-11 (bf16,
+ * q = (h >> 56) - 128), where h is the SplitMix64 output function applied to
+ * (k XOR ((seed + t) * 0x9E3779B97F4A7C15)) + (c + 1) * 0x9E3779B97F4A7C15,
+ * all mod 2^64; state starts at 0.  (t is 0 for a merged map.)
+ */
+
+/* Bytes of one row (host only; no GPU needed). */
+int rse_blocks_row_bytes(int32_t dim, int32_t w_dtype, int32_t optim, int64_t* row_bytes_out);
+
+/* Device bytes the caller must provide for the blocks' metadata (row counter,
+ * status, chunk pointer table). */
+int rse_blocks_meta_size(int32_t max_chunks, size_t* bytes_out);
+
+/* Create a blocks object over caller memory d_meta (meta_bytes >=
+ * rse_blocks_meta_size).  Supported dims: 4, 8, ..., 256 (powers of two) for
+ * fp32 and 8, ..., 256 for bf16.  rows_per_chunk_log2 in [4, 32].  Clears
+ * the metadata on `stream`. */
+int rse_blocks_create(rse_blocks** out, void* d_meta, size_t meta_bytes, int32_t dim,
+                      int32_t w_dtype, int32_t optim, int32_t rows_per_chunk_log2,
+                      int32_t max_chunks, uint64_t init_seed, void* stream);
+int rse_blocks_destroy(rse_blocks* blocks);
+
+/* Register one more chunk (caller device memory, 256-byte aligned, at least
+ * 2^rows_per_chunk_log2 * row_bytes bytes).  Existing rows do not move.
+ * Errors: RSE_ERR_CHUNK_TOO_SMALL, RSE_ERR_MAX_CHUNKS, RSE_ERR_TOO_MANY_ROWS,
+ * RSE_ERR_INVALID_ARG (null or misaligned). */
+int blocks_grow(rse_blocks* blocks, void* d_chunk, size_t chunk_bytes, void* stream);
+
+/* Host-known capacity (no synchronisation). */
+int rse_blocks_capacity(const rse_blocks* blocks, int64_t* rows_capacity_out,
+                        int64_t* rows_per_chunk_out, int32_t* n_chunks_out);
+
+/* Rows in use and sticky status (synchronises `stream`). */
+int rse_blocks_status(rse_blocks* blocks, int64_t* rows_used_out, int32_t* status_out,
+                      void* stream);
+
+/* Copy rows d_offs[0..n) out: weights widened to fp32 into d_w_out [n, dim],
+ * optimizer state into d_state_out [n, k * dim] (k = 0, 1, 2 for SGD,
+ * Adagrad, Adam; may be NULL).  Offsets must be < rows used. */
+int rse_blocks_read_rows(const rse_blocks* blocks, const int64_t* d_offs, int64_t n,
+                         float* d_w_out, float* d_state_out, void* stream);
+
+/* ------------------------------------------------------------- IDMap --- */
+/*
+ * IDMap ("RecIS", "Embedding Engine"): an open-addressing hash map from a
+ * 64-bit feature ID to a row offset.  Each table has its own region of
+ * 16-byte slots {key, value}, probed in buckets of 8 slots (one 128-byte
+ * line) from the bucket chosen by a 64-bit mix of the key; inserts are
+ * lock-free (64-bit compare-and-swap).  Every int64 is a legal key: the
+ * value used to mark an empty slot is kept in a per-table side slot.
+ *
+ * merged = 1 ("RecIS": merging same-attribute tables): one region for all
+ * logical tables, keyed by (t << 56) | id; ids must lie in [0, 2^56) and
+ * there may be at most RSE_MAX_MERGED_TABLES logical tables.
+ */
+
+/* Device bytes for a map with n_tables regions (slots_per_table: host array,
+ * each rounded up to a multiple of 8 slots). */
+int rse_idmap_mem_size(int32_t n_tables, const int64_t* slots_per_table, size_t* bytes_out);
+
+/* Create a map over caller memory d_mem and clear it on `stream`.
+ * max_load in (0, 0.95]: a table refuses inserts beyond max_load * slots.
+ * For merged = 1, n_tables must be 1 (one region). */
+int rse_idmap_create(rse_idmap** out, void* d_mem, size_t mem_bytes, int32_t n_tables,
+                     const int64_t* slots_per_table, double max_load, int32_t merged,
+                     uint64_t hash_seed, void* stream);
+int rse_idmap_destroy(rse_idmap* map);
+
+/* Workspace bytes for one idmap_find_or_insert over n_ids lookups. */
+int rse_idmap_workspace_size(int64_t n_ids, size_t* bytes_out);
+
+/*
+ * Map every lookup to its row offset, inserting missing keys if
+ * insert_missing != 0.
+ *
+ * Table t's lookups are d_ids[d_bounds[t*stride] .. d_bounds[(t+1)*stride])
+ * for t in [0, n_tables); with d_bounds = the bag offsets and stride = batch
+ * this is the table-major bag layout.  d_bounds[0] must be 0 and
+ * d_bounds[n_tables*stride] must equal n_ids.
+ *
+ * New keys receive consecutive offsets from the blocks' row counter in order
+ * of first sight (lookup index order); their rows are initialised (see
+ * EmbeddingBlocks) and the row counter advances by the number of new keys,
+ * written to *d_n_new_out (device int64).  A missing key without insert
+ * gives offset -1, which pooling and backward skip.
+ *
+ * If the new keys would exceed a table's max_load (RSE_ERR_IDMAP_FULL) or
+ * the free rows (RSE_ERR_NEED_GROW), nothing is inserted, missing keys get
+ * -1, *d_n_new_out is 0 and the map's sticky status is set; the caller may
+ * grow and repeat the call with identical results.
+ *
+ * d_ws: rse_idmap_workspace_size(n_ids) bytes of device scratch.
+ */
+int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids,
+                         int64_t n_ids, const int64_t* d_bounds, int64_t stride,
+                         int32_t n_tables, int32_t insert_missing, int64_t* d_row_off_out,
+                         int64_t* d_n_new_out, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Sticky status and per-table key counts (host array of the map's n_tables,
+ * may be NULL).  Synchronises `stream`. */
+int rse_idmap_status(rse_idmap* map, int32_t* status_out, int64_t* n_keys_out, void* stream);
+
+/* Reset the sticky status of a map or blocks object to RSE_OK. */
+int rse_idmap_clear_status(rse_idmap* map, void* stream);
+int rse_blocks_clear_status(rse_blocks* blocks, void* stream);
+
+/* Copy the live entries (any order) into d_keys_out / d_table_out /
+ * d_off_out, at most `capacity` of them; the number of live entries is
+ * written to *d_count_out.  In merged mode keys are (t << 56) | id and the
+ * table index is 0. */
+int rse_idmap_export(rse_idmap* map, int64_t* d_keys_out, int32_t* d_table_out,
+                     int64_t* d_off_out, int64_t capacity, int64_t* d_count_out, void* stream);
+
+/* ------------------------------------------------- pooled forward ----- */
+/*
+ * out[b, t, :] = sum over the rows of bag j = t*batch + b ("DLRM ... 2.1":
+ * EmbeddingBag sum), divided by the bag length for RSE_MEAN.  Rows are
+ * accumulated in fp64 in bag order and rounded once to fp32; an empty bag
+ * gives 0; offset -1 contributes nothing.  n_ids must equal
+ * bag_offsets[n_tables*batch].
+ */
+int embedding_bag_fwd(const rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
+                      const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
+                      int32_t pooling, float* d_out, void* stream);
+
+/* ------------------------------------------ sparse backward + update -- */
+typedef struct rse_optim {
+    int32_t kind;   /* RSE_SGD | RSE_ADAGRAD | RSE_ADAM */
+    int32_t reserved;
+    double lr;
+    double eps;     /* Adagrad, Adam */
+    double beta1;   /* Adam */
+    double beta2;   /* Adam */
+    int64_t step;   /* Adam: 1-based global step of this update */
+} rse_optim;
+
+/* Workspace bytes for one embedding_bag_bwd_update. */
+int rse_bwd_workspace_size(int64_t n_ids, int32_t n_tables, int64_t batch, int32_t dim,
+                           size_t* bytes_out);
+
+/*
+ * Sparse backward and row-wise update ("RecIS", "代码架构": fused sparse
+ * gradient update; "DLRM", "踩过的坑" 4: sparse optimizer).
+ *
+ * Lookup i of bag j = t*batch + b contributes g_i = grad[b, t, :] (divided
+ * by the bag length for RSE_MEAN) to row d_row_off[i].  The (row, bag)
+ * pairs are radix-sorted by row (stable), so each touched row's g is the
+ * fp64 sum of its contributions in lookup order (segments longer than 128
+ * are summed in 64-lookup pieces and the pieces added in a fixed tree); no
+ * floating-point atomics are used and the result is run-to-run identical.
+ * Then, once per touched row, in fp64 and rounded once to the storage type:
+ *   SGD:     w -= lr * g
+ *   Adagrad: a = fp32(a + g*g);  w -= lr * (g / (sqrt(a) + eps))
+ *   Adam:    m = fp32(b1 m + (1-b1) g);  v = fp32(b2 v + (1-b2) g g);
+ *            w -= lr * ((m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps))
+ * (Adam is the lazy form of Kingma & Ba 2015, Algorithm 1).  bf16 weights
+ * round to nearest even.  Rows not in the batch are not read or written.
+ * The number of distinct touched rows is written to *d_n_unique_out.
+ */
+int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
+                             const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
+                             int32_t pooling, const float* d_grad, const rse_optim* opt,
+                             int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RSE_H */

@@ -1,0 +1,88 @@
+"""ctypes declarations of librse.so (the C ABI in include/rse.h)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librse.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "rse.h")
+
+RSE_OK = 0
+STATUS = {
+    0: "RSE_OK", -1: "RSE_ERR_INVALID_ARG", -2: "RSE_ERR_UNSUPPORTED", -3: "RSE_ERR_WORKSPACE",
+    -4: "RSE_ERR_IDMAP_FULL", -5: "RSE_ERR_NEED_GROW", -6: "RSE_ERR_CHUNK_TOO_SMALL",
+    -7: "RSE_ERR_MAX_CHUNKS", -8: "RSE_ERR_HIP", -9: "RSE_ERR_BAD_INPUT", -10: "RSE_ERR_TOO_MANY_ROWS",
+}
+
+
+class RseError(RuntimeError):
+    def __init__(self, what: str, code: int):
+        super().__init__(f"{what}: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class RseOptim(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lr", ctypes.c_double),
+                ("eps", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _U64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+_SZ = ctypes.c_size_t
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PSZ = ctypes.POINTER(ctypes.c_size_t)
+
+# name -> argument types (all return int except where noted)
+SIGNATURES = {
+    "rse_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "rse_version": ([], ctypes.c_int),
+    "rse_blocks_row_bytes": ([_I32, _I32, _I32, _PI64], ctypes.c_int),
+    "rse_blocks_meta_size": ([_I32, _PSZ], ctypes.c_int),
+    "rse_blocks_create": ([ctypes.POINTER(_P), _P, _SZ, _I32, _I32, _I32, _I32, _I32, _U64, _P], ctypes.c_int),
+    "rse_blocks_destroy": ([_P], ctypes.c_int),
+    "blocks_grow": ([_P, _P, _SZ, _P], ctypes.c_int),
+    "rse_blocks_capacity": ([_P, _PI64, _PI64, _PI32], ctypes.c_int),
+    "rse_blocks_status": ([_P, _PI64, _PI32, _P], ctypes.c_int),
+    "rse_blocks_read_rows": ([_P, _P, _I64, _P, _P, _P], ctypes.c_int),
+    "rse_blocks_clear_status": ([_P, _P], ctypes.c_int),
+    "rse_idmap_mem_size": ([_I32, _PI64, _PSZ], ctypes.c_int),
+    "rse_idmap_create": ([ctypes.POINTER(_P), _P, _SZ, _I32, _PI64, ctypes.c_double, _I32, _U64, _P], ctypes.c_int),
+    "rse_idmap_destroy": ([_P], ctypes.c_int),
+    "rse_idmap_workspace_size": ([_I64, _PSZ], ctypes.c_int),
+    "idmap_find_or_insert": ([_P, _P, _P, _I64, _P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "rse_idmap_status": ([_P, _PI32, _PI64, _P], ctypes.c_int),
+    "rse_idmap_clear_status": ([_P, _P], ctypes.c_int),
+    "rse_idmap_export": ([_P, _P, _P, _P, _I64, _P, _P], ctypes.c_int),
+    "embedding_bag_fwd": ([_P, _P, _I64, _P, _I32, _I64, _I32, _P, _P], ctypes.c_int),
+    "rse_bwd_workspace_size": ([_I64, _I32, _I64, _I32, _PSZ], ctypes.c_int),
+    "embedding_bag_bwd_update": ([_P, _P, _I64, _P, _I32, _I64, _I32, _P, ctypes.POINTER(RseOptim), _P,
+                                  _P, _SZ, _P], ctypes.c_int),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load librse.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m recommender_sparse_embedding_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def check(rc: int, what: str):
+    if rc != RSE_OK:
+        raise RseError(what, rc)

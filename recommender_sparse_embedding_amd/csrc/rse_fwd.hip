@@ -1,0 +1,280 @@
+// rse_fwd.hip -- pooled embedding gather (EmbeddingBag forward, "DLRM模型的核心
+// 价值与工业落地挑战" section 2.1: sum pooling over variable-length bags;
+// "RecIS：阿里开源推荐系统统一训练框架", "代码架构": vectorised lookup loads).
+//
+// HBM-bound: each lookup reads one row (dim * 4 or dim * 2 bytes) and each
+// bag writes one fp32 row.  A row is read by a group of LPR lanes with one
+// 16-byte load per lane (dwordx4), so a 64-lane wave reads 64/LPR rows per
+// instruction with every byte of each 64-byte segment used.  Rows are
+// accumulated in fp64 (cheap: the kernel moves ~4 bytes per flop) in bag
+// order, so the pooled value is the exactly rounded fp32 of the sum in all
+// but pathological cases.
+//
+// Two schedules:
+//  - group-per-bags: each group owns BPG consecutive bags and walks their
+//    lookups as one flat range, UNROLL rows in flight, closing a bag whenever
+//    the range crosses its end offset (short bags, one-hot);
+//  - wave-per-bag: the wave's groups split one bag's lookups round-robin and
+//    combine with xor-shuffles in a fixed tree (long bags).
+#include "rse_host.h"
+
+using namespace rse;
+using namespace rse_host;
+
+namespace {
+
+constexpr int FWD_BLOCK = 256;
+
+template <int D, bool BF16>
+struct Geo {
+    static constexpr int VEC = BF16 ? 8 : 4;    // elements per lane (16 bytes)
+    static constexpr int LPR = D / VEC;         // lanes per row
+    static constexpr int GROUPS = WAVE / LPR;   // rows per wave-wide load
+    static_assert(LPR >= 1 && LPR <= WAVE && (WAVE % LPR) == 0, "dim");
+};
+
+template <bool BF16>
+__device__ __forceinline__ void widen_add(double* acc, const uint4& q) {
+    if (!BF16) {
+        acc[0] += (double)__uint_as_float(q.x);
+        acc[1] += (double)__uint_as_float(q.y);
+        acc[2] += (double)__uint_as_float(q.z);
+        acc[3] += (double)__uint_as_float(q.w);
+    } else {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc[2 * k] += (double)__uint_as_float(w[k] << 16);
+            acc[2 * k + 1] += (double)__uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_out(float* dst, const double* acc, double scale, bool mean) {
+    float f[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) f[k] = (float)(mean ? acc[k] / scale : acc[k]);
+#pragma unroll
+    for (int k = 0; k < VEC; k += 4)
+        *reinterpret_cast<float4*>(dst + k) = make_float4(f[k], f[k + 1], f[k + 2], f[k + 3]);
+}
+
+struct FwdArgs {
+    RowsView rv;
+    const int64_t* row_off;
+    const int64_t* bag_off;
+    int64_t n_bags;
+    int64_t batch;
+    int64_t n_ids;
+    int64_t capacity;          // rows addressable through the chunk table
+    int32_t* status;           // blocks' sticky status
+    int32_t n_tables;
+    int32_t mean;
+    float* out;
+};
+
+// Offsets outside [0, n_ids] or decreasing, and rows beyond the capacity, are
+// malformed input: the bag is skipped (or the row ignored) and the sticky
+// status set, so nothing is read out of bounds.
+__device__ __forceinline__ void flag_bad(const FwdArgs& a) {
+    atomicCAS(a.status, 0, (int32_t)RSE_ERR_BAD_INPUT);
+}
+
+// ----------------------------------------------------- group per bags ----
+template <int D, bool BF16, int BPG, int UNROLL>
+__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
+    using G = Geo<D, BF16>;
+    constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    const int lane = lane_id();
+    const int g = lane / LPR;
+    const int li = lane % LPR;
+    const int64_t gid = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE * GROUPS + g;
+    const int64_t n_groups = (int64_t)gridDim.x * (FWD_BLOCK / WAVE) * GROUPS;
+    const int64_t W_BYTES = (int64_t)D * (BF16 ? 2 : 4);
+    (void)W_BYTES;
+
+    for (int64_t jb = gid * BPG; jb < a.n_bags; jb += n_groups * BPG) {
+        const int64_t je = jb + BPG < a.n_bags ? jb + BPG : a.n_bags;
+        {
+            bool ok = true;
+            int64_t prev = a.bag_off[jb];
+            if (prev < 0 || prev > a.n_ids) ok = false;
+            for (int64_t jj = jb + 1; jj <= je; ++jj) {
+                const int64_t o = a.bag_off[jj];
+                if (o < prev || o > a.n_ids) ok = false;
+                prev = o;
+            }
+            if (!ok) {
+                if (li == 0) flag_bad(a);
+                continue;
+            }
+        }
+        int64_t j = jb;
+        int64_t bag_start = a.bag_off[jb];
+        int64_t bag_end = a.bag_off[jb + 1];
+        const int64_t last = a.bag_off[je];
+        double acc[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
+
+        auto close_bag = [&](int64_t jj, int64_t len) {
+            const int64_t t = jj / a.batch;
+            const int64_t b = jj - t * a.batch;
+            float* dst = a.out + (b * a.n_tables + t) * D + li * VEC;
+            store_out<VEC>(dst, acc, (double)len, a.mean && len > 0);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
+        };
+
+        for (int64_t i = bag_start; i < last; i += UNROLL) {
+            int64_t r[UNROLL];
+            uint4 q[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                r[u] = (i + u < last) ? a.row_off[i + u] : -1;
+                if (r[u] >= a.capacity) {
+                    if (li == 0) flag_bad(a);
+                    r[u] = -1;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (r[u] >= 0) q[u] = *reinterpret_cast<const uint4*>(a.rv.row(r[u]) + li * 16);
+                else q[u] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t ii = i + u;
+                if (ii >= last) break;
+                while (ii >= bag_end) {      // close finished (possibly empty) bags
+                    close_bag(j, bag_end - bag_start);
+                    ++j;
+                    bag_start = bag_end;
+                    bag_end = a.bag_off[j + 1];
+                }
+                if (r[u] >= 0) widen_add<BF16>(acc, q[u]);
+            }
+        }
+        // close the remaining bags of the run (including trailing empty ones)
+        while (j < je) {
+            close_bag(j, bag_end - bag_start);
+            ++j;
+            if (j < je) {
+                bag_start = bag_end;
+                bag_end = a.bag_off[j + 1];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------- wave per bag ----
+template <int D, bool BF16, int UNROLL>
+__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
+    using G = Geo<D, BF16>;
+    constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    const int lane = lane_id();
+    const int g = lane / LPR;
+    const int li = lane % LPR;
+    const int64_t wid = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE;
+    const int64_t n_waves = (int64_t)gridDim.x * (FWD_BLOCK / WAVE);
+    for (int64_t j = wid; j < a.n_bags; j += n_waves) {
+        const int64_t s = a.bag_off[j];
+        const int64_t e = a.bag_off[j + 1];
+        if (s < 0 || e < s || e > a.n_ids) {
+            if (lane == 0) flag_bad(a);
+            continue;
+        }
+        double acc[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
+        for (int64_t i = s + g; i < e; i += (int64_t)GROUPS * UNROLL) {
+            int64_t r[UNROLL];
+            uint4 q[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t ii = i + (int64_t)u * GROUPS;
+                r[u] = ii < e ? a.row_off[ii] : -1;
+                if (r[u] >= a.capacity) {
+                    if (li == 0) flag_bad(a);
+                    r[u] = -1;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (r[u] >= 0) q[u] = *reinterpret_cast<const uint4*>(a.rv.row(r[u]) + li * 16);
+                else q[u] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (r[u] >= 0) widen_add<BF16>(acc, q[u]);
+        }
+        // fixed xor tree across the groups
+#pragma unroll
+        for (int m = LPR; m < WAVE; m <<= 1) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[k] += shfl_xor_f64(acc[k], m);
+        }
+        if (g == 0) {
+            const int64_t t = j / a.batch;
+            const int64_t b = j - t * a.batch;
+            const int64_t len = e - s;
+            store_out<VEC>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, (double)len,
+                           a.mean && len > 0);
+        }
+    }
+}
+
+template <int D, bool BF16>
+int launch_fwd(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
+    using G = Geo<D, BF16>;
+    const double avg = a.n_bags > 0 ? (double)n_ids / (double)a.n_bags : 0.0;
+    if (avg >= 2.0 * G::GROUPS && G::GROUPS > 1) {
+        const int blocks = fill_blocks(a.n_bags, FWD_BLOCK / WAVE, 256 * 32);
+        hipLaunchKernelGGL((k_fwd_wave<D, BF16, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
+    } else {
+        constexpr int BPG = 4;
+        const int64_t groups = (a.n_bags + BPG - 1) / BPG;
+        const int blocks = fill_blocks(groups, (FWD_BLOCK / WAVE) * G::GROUPS, 256 * 32);
+        hipLaunchKernelGGL((k_fwd_groups<D, BF16, BPG, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" int embedding_bag_fwd(const rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
+                                 const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
+                                 int32_t pooling, float* d_out, void* stream) {
+    if (!blocks || !d_bag_offsets || n_ids < 0 || n_tables <= 0 || batch < 0)
+        return RSE_ERR_INVALID_ARG;
+    if (pooling != RSE_SUM && pooling != RSE_MEAN) return RSE_ERR_INVALID_ARG;
+    if (n_ids > 0 && !d_row_off) return RSE_ERR_INVALID_ARG;
+    const int64_t n_bags = (int64_t)n_tables * batch;
+    if (n_bags == 0) return RSE_OK;
+    if (!d_out) return RSE_ERR_INVALID_ARG;
+    FwdArgs a;
+    a.rv = blocks->view();
+    a.row_off = d_row_off;
+    a.bag_off = d_bag_offsets;
+    a.n_bags = n_bags;
+    a.batch = batch;
+    a.n_ids = n_ids;
+    a.capacity = blocks->capacity();
+    a.status = &blocks->header()->status;
+    a.n_tables = n_tables;
+    a.mean = pooling == RSE_MEAN;
+    a.out = d_out;
+    hipStream_t s = as_stream(stream);
+    const bool bf = blocks->w_dtype == RSE_BF16;
+    switch (blocks->dim) {
+        case 4: return bf ? RSE_ERR_UNSUPPORTED : launch_fwd<4, false>(a, n_ids, s);
+        case 8: return bf ? launch_fwd<8, true>(a, n_ids, s) : launch_fwd<8, false>(a, n_ids, s);
+        case 16: return bf ? launch_fwd<16, true>(a, n_ids, s) : launch_fwd<16, false>(a, n_ids, s);
+        case 32: return bf ? launch_fwd<32, true>(a, n_ids, s) : launch_fwd<32, false>(a, n_ids, s);
+        case 64: return bf ? launch_fwd<64, true>(a, n_ids, s) : launch_fwd<64, false>(a, n_ids, s);
+        case 128: return bf ? launch_fwd<128, true>(a, n_ids, s) : launch_fwd<128, false>(a, n_ids, s);
+        case 256: return bf ? launch_fwd<256, true>(a, n_ids, s) : launch_fwd<256, false>(a, n_ids, s);
+        default: return RSE_ERR_UNSUPPORTED;
+    }
+}

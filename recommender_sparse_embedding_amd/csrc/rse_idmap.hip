@@ -1,0 +1,858 @@
+// rse_idmap.hip -- IDMap: feature ID -> row offset ("RecIS：阿里开源推荐系统统一
+// 训练框架", "Embedding Engine": the first level of the two-level table;
+// "阿里 RecIS：搜广推训练的背景与难点": raw IDs over a huge sparse range need
+// a map, not a dense or modulo-indexed table).
+//
+// Layout: per table a region of 16-byte slots {key, value} in buckets of 8
+// slots (128 bytes, one cache line).  A lookup is served by 8 lanes of a
+// wavefront that read one bucket with one 16-byte load each and compare by
+// ballot; a 64-lane wave therefore probes 8 lookups at once.  Buckets are
+// probed linearly from the bucket chosen by a salted 64-bit mix.
+//
+// find_or_insert runs as a fixed chain of kernels on one stream:
+//   reset -> probe (hits resolved; misses CAS-claim a slot and record their
+//   lookup index as a pending value with atomicMin, so the slot ends up
+//   holding the FIRST lookup of that key) -> mark first-sight lookups ->
+//   exclusive scan over lookups (rank of each first sight in lookup order)
+//   -> decide (capacity / load checks, single block) -> commit (or roll
+//   back every pending slot) -> resolve pending lookups -> init new rows.
+// New offsets are therefore rows_used + rank, identical to inserting the
+// keys one by one in lookup order, and independent of thread timing.  Only
+// integer atomics are used.  Kernels after the probe exit at once when the
+// batch has no miss.
+#include <new>
+
+#include "rse_host.h"
+
+using namespace rse;
+using namespace rse_host;
+
+rse::Slot* rse_idmap::d_slots() const {
+    return reinterpret_cast<rse::Slot*>(
+        d_mem + align_up(sizeof(MapHeader) + (size_t)n_tables * sizeof(TableDir), 256));
+}
+
+namespace {
+
+constexpr int PROBE_BLOCK = 256;
+constexpr int SCAN_TILE = 4096;          // lookups per scan block (256 x 16)
+constexpr uint32_t SIDE_MARK = 0xFFFFFFFFu;   // slot index meaning "side slot"
+
+// Workspace of one call.
+struct Ws {
+    unsigned long long* ctr;   // [0] misses [1] overflow [2] bad input [3] ok
+                               // [4] rows_used before [5] new keys [6] status code
+    uint32_t* miss_list;       // lookup indices that missed (any order)
+    uint32_t* slot_of;         // per lookup: claimed slot (SIDE_MARK for the side slot)
+    uint32_t* flag;            // per lookup: 0 hit, 1 pending, 2 first sight
+    uint32_t* rank;            // per first-sight lookup: new-row rank
+    uint32_t* tile_sum;        // per scan tile
+    uint64_t* new_key;         // per new row (by rank): key
+    uint32_t* new_tab;         // per new row: table index used by the init
+};
+
+Ws carve(void* base, int64_t n_ids, size_t* total) {
+    Carver c(base);
+    Ws w;
+    const size_t n = (size_t)(n_ids > 0 ? n_ids : 1);
+    const size_t tiles = (n + SCAN_TILE - 1) / SCAN_TILE;
+    w.ctr = c.take<unsigned long long>(32);
+    w.miss_list = c.take<uint32_t>(n);
+    w.slot_of = c.take<uint32_t>(n);
+    w.flag = c.take<uint32_t>(n);
+    w.rank = c.take<uint32_t>(n);
+    w.tile_sum = c.take<uint32_t>(tiles + 1);
+    w.new_key = c.take<uint64_t>(n);
+    w.new_tab = c.take<uint32_t>(n);
+    if (total) *total = c.size();
+    return w;
+}
+
+struct ProbeArgs {
+    Slot* slots;
+    TableDir* dir;
+    const int64_t* ids;
+    int64_t n_ids;
+    const int64_t* bounds;
+    int64_t stride;
+    int32_t n_tables;       // logical tables of the call
+    int32_t merged;
+    int32_t insert;
+    int32_t pad;
+    int64_t* row_off;
+    Ws ws;
+};
+
+// -------------------------------------------------------------- reset ----
+__global__ void k_reset(Ws ws, TableDir* dir, int32_t n_regions) {
+    const int tid = threadIdx.x;
+    if (tid < 32) ws.ctr[tid] = 0;
+    for (int r = tid; r < n_regions; r += blockDim.x) dir[r].new_keys = 0;
+}
+
+// Table of lookup i: the t with bounds[t] <= i < bounds[t+1] (bounds in LDS,
+// possibly with empty tables).
+__device__ __forceinline__ int table_of(const int64_t* sb, int n_tables, int64_t i) {
+    int lo = 0, hi = n_tables;            // invariant: sb[lo] <= i < sb[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sb[mid] <= i) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Loads the table bounds into LDS and checks them (same verdict in every
+// block).  Returns false if malformed.
+__device__ bool load_bounds(int64_t* sb, const int64_t* bounds, int64_t stride, int n_tables,
+                            int64_t n_ids) {
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    for (int t = threadIdx.x; t <= n_tables; t += blockDim.x) {
+        sb[t] = bounds[(int64_t)t * stride];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < n_tables; t += blockDim.x)
+        if (sb[t + 1] < sb[t]) s_bad = 1;
+    if (threadIdx.x == 0 && (sb[0] != 0 || sb[n_tables] != n_ids)) s_bad = 1;
+    __syncthreads();
+    return s_bad == 0;
+}
+
+// -------------------------------------------------------------- probe ----
+// 8 lanes per lookup; each wave handles 8 lookups per iteration.
+__global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const bool ok_bounds = load_bounds(sb, a.bounds, a.stride, a.n_tables, a.n_ids);
+    if (!ok_bounds) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.ctr[2] = 1;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_ids;
+             i += (int64_t)gridDim.x * blockDim.x) {
+            a.row_off[i] = -1;
+            a.ws.flag[i] = 0;
+        }
+        return;
+    }
+    const int lane = lane_id();
+    const int g = lane >> 3;           // group within the wave
+    const int sub = lane & 7;          // slot within the bucket
+    const int gshift = g * 8;
+    const int64_t wave_global = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+
+    for (int64_t base = wave_global * 8; base < a.n_ids; base += n_waves * 8) {
+        const int64_t i = base + g;
+        const bool active = i < a.n_ids;
+        // result of this lookup: 0 hit, 1 pending (miss, inserted), 2 absent,
+        // 3 overflow, 4 bad id
+        int kind = 2;
+        uint64_t val = 0;
+        uint32_t slot_idx = 0;
+        if (active) {
+            const int t = table_of(sb, a.n_tables, i);
+            uint64_t key = (uint64_t)a.ids[i];
+            int region = t;
+            bool bad = false;
+            if (a.merged) {
+                if (key >= (1ull << 56)) bad = true;   // also rejects negative ids
+                key = ((uint64_t)t << 56) | key;
+                region = 0;
+            }
+            if (bad) {
+                kind = 4;
+            } else if (key == EMPTY_KEY) {
+                // the empty marker itself: a per-table side slot
+                uint64_t v = a.dir[region].side_val;
+                if (v < PENDING_BASE) {
+                    kind = 0;
+                    val = v;
+                } else if (a.insert) {
+                    if (sub == 0) atomicMin((unsigned long long*)&a.dir[region].side_val,
+                                            (unsigned long long)(PENDING_BASE + (uint64_t)i));
+                    kind = 1;
+                    slot_idx = SIDE_MARK;
+                } else {
+                    kind = 2;
+                }
+            } else {
+                const TableDir d = a.dir[region];
+                int64_t b = reduce_range(fmix64(key ^ d.salt), d.n_buckets);
+                int64_t probes = 0;
+                while (true) {
+                    const int64_t sidx = d.slot_base + b * BUCKET;
+                    const Slot s = a.slots[sidx + sub];
+                    const uint32_t m = (uint32_t)(__ballot(s.key == key) >> gshift) & 0xFFu;
+                    if (m) {
+                        const int src = __ffs(m) - 1;
+                        const uint64_t v = shfl_idx(s.val, gshift + src);
+                        if (v < PENDING_BASE) {
+                            kind = 0;
+                            val = v;
+                        } else {
+                            // inserted by another lookup of this batch: join it
+                            if (sub == 0)
+                                atomicMin((unsigned long long*)&a.slots[sidx + src].val,
+                                          (unsigned long long)(PENDING_BASE + (uint64_t)i));
+                            kind = 1;
+                            slot_idx = (uint32_t)(sidx + src);
+                        }
+                        break;
+                    }
+                    const uint32_t e = (uint32_t)(__ballot(s.key == EMPTY_KEY) >> gshift) & 0xFFu;
+                    if (e) {
+                        if (!a.insert) {
+                            kind = 2;
+                            break;
+                        }
+                        // Claim the first truly empty slot of the bucket, in slot
+                        // order.  A slot never returns to empty within the call,
+                        // so slots seen as non-empty are skipped safely; a CAS
+                        // that returns our key means another lookup got there first.
+                        int claimed = -1;
+                        if (sub == 0) {
+                            uint32_t rem = e;
+                            while (rem) {
+                                const int q = __ffs(rem) - 1;
+                                rem &= rem - 1;
+                                const unsigned long long old = atomicCAS(
+                                    (unsigned long long*)&a.slots[sidx + q].key,
+                                    (unsigned long long)EMPTY_KEY, (unsigned long long)key);
+                                if (old == EMPTY_KEY || old == key) {
+                                    atomicMin((unsigned long long*)&a.slots[sidx + q].val,
+                                              (unsigned long long)(PENDING_BASE + (uint64_t)i));
+                                    claimed = q;
+                                    break;
+                                }
+                            }
+                        }
+                        claimed = shfl_idx(claimed, gshift);
+                        if (claimed >= 0) {
+                            kind = 1;
+                            slot_idx = (uint32_t)(sidx + claimed);
+                            break;
+                        }
+                        // bucket filled up meanwhile: continue with the next one
+                    }
+                    if (++probes >= d.n_buckets) {
+                        kind = 3;
+                        break;
+                    }
+                    b = (b + 1 == d.n_buckets) ? 0 : b + 1;
+                }
+            }
+        }
+        // write results (one lane per group) and append misses to the list
+        const bool leader = active && sub == 0;
+        const bool is_miss = leader && kind == 1;
+        const unsigned long long mm = __ballot(is_miss);
+        unsigned long long pos0 = 0;
+        if (mm) {
+            if (lane == __ffsll((long long)mm) - 1)
+                pos0 = atomicAdd(&a.ws.ctr[0], (unsigned long long)__popcll(mm));
+            pos0 = __shfl(pos0, __ffsll((long long)mm) - 1, WAVE);
+        }
+        if (leader) {
+            if (kind == 0) {
+                a.row_off[i] = (int64_t)val;
+                a.ws.flag[i] = 0;
+            } else if (kind == 1) {
+                const unsigned long long below = mm & ((1ull << lane) - 1);
+                a.ws.miss_list[pos0 + __popcll(below)] = (uint32_t)i;
+                a.ws.slot_of[i] = slot_idx;
+                a.ws.flag[i] = 1;
+                a.row_off[i] = -1;
+            } else {
+                a.row_off[i] = -1;
+                a.ws.flag[i] = 0;
+                if (kind == 3) a.ws.ctr[1] = 1;
+                if (kind == 4) a.ws.ctr[2] = 1;
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------- mark heads --
+__device__ __forceinline__ int region_of_slot(const TableDir* dir, int n_regions, uint32_t s) {
+    int lo = 0, hi = n_regions;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((uint64_t)dir[mid].slot_base <= s) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+struct MarkArgs {
+    Slot* slots;
+    TableDir* dir;
+    int32_t n_regions;
+    int32_t merged;
+    const int64_t* ids;
+    const int64_t* bounds;
+    int64_t stride;
+    int32_t n_tables;
+    int32_t pad;
+    Ws ws;
+};
+
+// A pending lookup is the first sight of its key iff the slot's pending value
+// names it.  First sights are counted per region for the load check.
+__global__ void k_mark(MarkArgs a) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const unsigned long long n_miss = a.ws.ctr[0];
+    if (n_miss == 0) return;
+    for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    __syncthreads();
+    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
+         q += (unsigned long long)gridDim.x * blockDim.x) {
+        const uint32_t i = a.ws.miss_list[q];
+        const uint32_t s = a.ws.slot_of[i];
+        int region;
+        uint64_t v;
+        if (s == SIDE_MARK) {
+            region = a.merged ? 0 : table_of(sb, a.n_tables, i);
+            v = a.dir[region].side_val;
+        } else {
+            region = region_of_slot(a.dir, a.n_regions, s);
+            v = a.slots[s].val;
+        }
+        if (v == PENDING_BASE + (uint64_t)i) {
+            a.ws.flag[i] = 2;
+            atomicAdd((unsigned long long*)&a.dir[region].new_keys, 1ull);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- scan ---
+// Exclusive scan of (flag == 2) over all lookups: reduce per tile, scan the
+// tile sums in one block, then rescan each tile.
+__global__ __launch_bounds__(256) void k_scan_reduce(Ws ws, int64_t n) {
+    if (ws.ctr[0] == 0) return;
+    const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
+    uint32_t c = 0;
+    for (int k = 0; k < SCAN_TILE / 256; ++k) {
+        const int64_t i = base + k * 256 + threadIdx.x;
+        if (i < n) c += ws.flag[i] == 2;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = c;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) ws.tile_sum[blockIdx.x] = red[0];
+}
+
+// Block-wide exclusive scan of 1024 values (one per thread); returns the total.
+__device__ uint32_t block_exclusive_scan_1024(uint32_t v, uint32_t* out_excl) {
+    __shared__ uint32_t wsum[16];
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t x = v;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t wprefix = 0, total = 0;
+    for (int k = 0; k < 16; ++k) {
+        if (k < w) wprefix += wsum[k];
+        total += wsum[k];
+    }
+    __syncthreads();
+    *out_excl = wprefix + x - v;
+    return total;
+}
+
+struct DecideArgs {
+    TableDir* dir;
+    int32_t n_regions;
+    int32_t pad;
+    BlocksHeader* bh;
+    MapHeader* mh;
+    int64_t capacity;
+    int64_t* n_new_out;
+    int64_t n_tiles;
+    Ws ws;
+};
+
+// Single block of 1024 threads: scans the tile sums, then decides whether the
+// call commits and advances the counters.
+__global__ __launch_bounds__(1024) void k_decide(DecideArgs a) {
+    __shared__ int s_fail;
+    __shared__ uint32_t s_carry;
+    const bool any_miss = a.ws.ctr[0] != 0;
+    uint32_t total = 0;
+    if (any_miss) {
+        if (threadIdx.x == 0) s_carry = 0;
+        __syncthreads();
+        for (int64_t base = 0; base < a.n_tiles; base += 1024) {
+            const int64_t k = base + threadIdx.x;
+            const uint32_t v = k < a.n_tiles ? a.ws.tile_sum[k] : 0;
+            uint32_t ex;
+            const uint32_t t = block_exclusive_scan_1024(v, &ex);
+            const uint32_t carry = s_carry;
+            if (k < a.n_tiles) a.ws.tile_sum[k] = carry + ex;
+            __syncthreads();
+            if (threadIdx.x == 0) s_carry = carry + t;
+            __syncthreads();
+        }
+        total = s_carry;
+    }
+    if (threadIdx.x == 0) s_fail = 0;
+    __syncthreads();
+    // per-region load check
+    for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) {
+        const TableDir d = a.dir[r];
+        if (d.n_keys + d.new_keys > d.max_keys) atomicCAS(&s_fail, 0, (int)RSE_ERR_IDMAP_FULL);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int fail = 0;
+        if (a.ws.ctr[2]) fail = RSE_ERR_BAD_INPUT;
+        else if (a.ws.ctr[1] || s_fail) fail = RSE_ERR_IDMAP_FULL;
+        const int64_t used = a.bh->rows_used;
+        if (!fail && used + (int64_t)total > a.capacity) fail = RSE_ERR_NEED_GROW;
+        a.ws.ctr[4] = (unsigned long long)used;
+        a.ws.ctr[5] = total;
+        if (!fail) {
+            a.ws.ctr[3] = 1;
+            a.bh->rows_used = used + (int64_t)total;
+            *a.n_new_out = (int64_t)total;
+        } else {
+            a.ws.ctr[3] = 0;
+            *a.n_new_out = 0;
+            atomicCAS(&a.mh->status, 0, fail);
+        }
+    }
+    __syncthreads();
+    if (a.ws.ctr[3]) {
+        for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) {
+            a.dir[r].n_keys += a.dir[r].new_keys;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_scan_down(Ws ws, int64_t n) {
+    if (ws.ctr[0] == 0 || ws.ctr[3] == 0) return;
+    const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
+    // each thread owns 16 consecutive lookups
+    const int64_t i0 = base + (int64_t)threadIdx.x * 16;
+    uint32_t f[16];
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t i = i0 + k;
+        f[k] = (i < n && ws.flag[i] == 2) ? 1u : 0u;
+        c += f[k];
+    }
+    // block exclusive scan of c (256 threads)
+    __shared__ uint32_t wsum[4];
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t x = c;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = ws.tile_sum[blockIdx.x];
+    for (int k = 0; k < w; ++k) pre += wsum[k];
+    uint32_t r = pre + x - c;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (f[k]) ws.rank[i0 + k] = r;
+        r += f[k];
+    }
+}
+
+// ------------------------------------------------------------ commit -----
+struct CommitArgs {
+    Slot* slots;
+    TableDir* dir;
+    int32_t n_regions;
+    int32_t merged;
+    const int64_t* ids;
+    const int64_t* bounds;
+    int64_t stride;
+    int32_t n_tables;
+    int32_t pad;
+    Ws ws;
+};
+
+// First sights publish their offset (or, on failure, release the slot).
+__global__ void k_commit(CommitArgs a) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const unsigned long long n_miss = a.ws.ctr[0];
+    if (n_miss == 0) return;
+    for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    __syncthreads();
+    const bool ok = a.ws.ctr[3] != 0;
+    const uint64_t used = a.ws.ctr[4];
+    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
+         q += (unsigned long long)gridDim.x * blockDim.x) {
+        const uint32_t i = a.ws.miss_list[q];
+        if (a.ws.flag[i] != 2) continue;
+        const uint32_t s = a.ws.slot_of[i];
+        const int t = table_of(sb, a.n_tables, i);
+        const int region = a.merged ? 0 : t;
+        if (ok) {
+            const uint32_t rk = a.ws.rank[i];
+            const uint64_t off = used + rk;
+            uint64_t key = (uint64_t)a.ids[i];
+            if (a.merged) key = ((uint64_t)t << 56) | key;
+            if (s == SIDE_MARK) a.dir[region].side_val = off;
+            else a.slots[s].val = off;
+            a.ws.new_key[rk] = key;
+            a.ws.new_tab[rk] = (uint32_t)region;
+        } else {
+            if (s == SIDE_MARK) {
+                a.dir[region].side_val = EMPTY_VAL;
+            } else {
+                a.slots[s].key = EMPTY_KEY;
+                a.slots[s].val = EMPTY_VAL;
+            }
+        }
+    }
+}
+
+// Every pending lookup reads its key's final offset.
+__global__ void k_resolve(Slot* slots, TableDir* dir, int32_t merged, const int64_t* bounds,
+                          int64_t stride, int32_t n_tables, Ws ws, int64_t* row_off) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const unsigned long long n_miss = ws.ctr[0];
+    if (n_miss == 0) return;
+    for (int t = threadIdx.x; t <= n_tables; t += blockDim.x) sb[t] = bounds[(int64_t)t * stride];
+    __syncthreads();
+    const bool ok = ws.ctr[3] != 0;
+    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
+         q += (unsigned long long)gridDim.x * blockDim.x) {
+        const uint32_t i = ws.miss_list[q];
+        int64_t v = -1;
+        if (ok) {
+            const uint32_t s = ws.slot_of[i];
+            if (s == SIDE_MARK) {
+                const int region = merged ? 0 : table_of(sb, n_tables, i);
+                v = (int64_t)dir[region].side_val;
+            } else {
+                v = (int64_t)slots[s].val;
+            }
+        }
+        row_off[i] = v;
+    }
+}
+
+// New rows: weights from the key hash, state zero.  One thread per 16 bytes
+// of a row; rows are consecutive so the writes are contiguous.
+template <bool BF16>
+__global__ void k_init_rows(RowsView rv, int dim, int64_t row_bytes, uint64_t seed, Ws ws) {
+    if (ws.ctr[3] == 0) return;
+    const uint64_t n_new = ws.ctr[5];
+    if (n_new == 0) return;
+    const uint64_t used = ws.ctr[4];
+    const int64_t q_per_row = row_bytes / 16;
+    const int64_t w_q = (int64_t)dim * (BF16 ? 2 : 4) / 16;   // 16-byte units of weights
+    const int per_q = BF16 ? 8 : 4;
+    const uint64_t total = n_new * (uint64_t)q_per_row;
+    for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t r = e / (uint64_t)q_per_row;
+        const int64_t qi = (int64_t)(e - r * (uint64_t)q_per_row);
+        char* row = rv.row((int64_t)(used + r));
+        uint4 out = make_uint4(0, 0, 0, 0);
+        if (qi < w_q) {
+            const uint64_t key = ws.new_key[r];
+            const uint32_t tab = ws.new_tab[r];
+            uint32_t wv[4];
+            if (!BF16) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    wv[k] = __float_as_uint(init_value(key, tab, (int)(qi * per_q + k), seed, false));
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = f32_to_bf16_exact(init_value(key, tab, (int)(qi * per_q + 2 * k), seed, true));
+                    const uint32_t hi = f32_to_bf16_exact(init_value(key, tab, (int)(qi * per_q + 2 * k + 1), seed, true));
+                    wv[k] = lo | (hi << 16);
+                }
+            }
+            out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+        reinterpret_cast<uint4*>(row)[qi] = out;
+    }
+}
+
+// ------------------------------------------------------------ create -----
+__global__ void k_clear_slots(Slot* slots, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        slots[i].key = EMPTY_KEY;
+        slots[i].val = EMPTY_VAL;
+    }
+}
+
+__global__ void k_clear_header(MapHeader* h, int32_t n_tables, int32_t merged) {
+    if (threadIdx.x == 0) {
+        h->status = 0;
+        h->n_tables = n_tables;
+        h->merged = merged;
+    }
+}
+
+__global__ void k_clear_status(MapHeader* h) { h->status = 0; }
+
+// ------------------------------------------------------------ export -----
+__global__ void k_export(const Slot* slots, const TableDir* dir, int32_t n_regions, int64_t total_slots,
+                         int64_t* keys, int32_t* tabs, int64_t* offs, int64_t capacity,
+                         unsigned long long* count) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t s = tid; s < total_slots; s += stride) {
+        const Slot sl = slots[s];
+        if (sl.key == EMPTY_KEY) continue;
+        const unsigned long long p = atomicAdd(count, 1ull);
+        if ((int64_t)p < capacity) {
+            keys[p] = (int64_t)sl.key;
+            tabs[p] = region_of_slot(dir, n_regions, (uint32_t)s);
+            offs[p] = (int64_t)sl.val;
+        }
+    }
+    for (int64_t r = tid; r < n_regions; r += stride) {
+        const uint64_t v = dir[r].side_val;
+        if (v >= PENDING_BASE) continue;
+        const unsigned long long p = atomicAdd(count, 1ull);
+        if ((int64_t)p < capacity) {
+            keys[p] = (int64_t)EMPTY_KEY;
+            tabs[p] = (int32_t)r;
+            offs[p] = (int64_t)v;
+        }
+    }
+}
+
+__global__ void k_zero_u64(unsigned long long* p) { *p = 0; }
+
+}  // namespace
+
+extern "C" {
+
+int rse_idmap_mem_size(int32_t n_tables, const int64_t* slots_per_table, size_t* bytes_out) {
+    if (!bytes_out || !slots_per_table || n_tables <= 0 || n_tables > RSE_MAX_TABLES)
+        return RSE_ERR_INVALID_ARG;
+    int64_t total = 0;
+    for (int t = 0; t < n_tables; ++t) {
+        if (slots_per_table[t] <= 0) return RSE_ERR_INVALID_ARG;
+        total += (int64_t)align_up((size_t)slots_per_table[t], BUCKET);
+    }
+    if (total > (int64_t)0xFFFFF000ll) return RSE_ERR_INVALID_ARG;   // slot index fits 32 bits
+    *bytes_out = align_up(sizeof(MapHeader) + (size_t)n_tables * sizeof(TableDir), 256) +
+                 (size_t)total * sizeof(Slot);
+    return RSE_OK;
+}
+
+int rse_idmap_create(rse_idmap** out, void* d_mem, size_t mem_bytes, int32_t n_tables,
+                     const int64_t* slots_per_table, double max_load, int32_t merged,
+                     uint64_t hash_seed, void* stream) {
+    if (!out || !d_mem) return RSE_ERR_INVALID_ARG;
+    if (!(max_load > 0.0 && max_load <= 0.95)) return RSE_ERR_INVALID_ARG;
+    if (merged && n_tables != 1) return RSE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(d_mem) % 256) return RSE_ERR_INVALID_ARG;
+    size_t need = 0;
+    int rc = rse_idmap_mem_size(n_tables, slots_per_table, &need);
+    if (rc) return rc;
+    if (mem_bytes < need) return RSE_ERR_WORKSPACE;
+    rse_idmap* m = new (std::nothrow) rse_idmap();
+    if (!m) return RSE_ERR_INVALID_ARG;
+    m->n_tables = n_tables;
+    m->merged = merged ? 1 : 0;
+    m->max_load = max_load;
+    m->d_mem = static_cast<char*>(d_mem);
+    m->dir.resize(n_tables);
+    int64_t base = 0;
+    uint64_t sm = hash_seed;
+    for (int t = 0; t < n_tables; ++t) {
+        const int64_t slots = (int64_t)align_up((size_t)slots_per_table[t], BUCKET);
+        TableDir& d = m->dir[t];
+        d.slot_base = base;
+        d.n_buckets = slots / BUCKET;
+        d.max_keys = (int64_t)(max_load * (double)slots);
+        // per-table salt: successive SplitMix64 outputs of the seed
+        sm += SM64_GAMMA;
+        uint64_t z = sm;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        d.salt = z ^ (z >> 31);
+        d.n_keys = 0;
+        d.side_val = EMPTY_VAL;
+        d.new_keys = 0;
+        d.pad = 0;
+        base += slots;
+    }
+    m->total_slots = base;
+    hipStream_t s = as_stream(stream);
+    if (hipMemcpyAsync(m->d_dir(), m->dir.data(), sizeof(TableDir) * n_tables, hipMemcpyHostToDevice,
+                       s) != hipSuccess) {
+        delete m;
+        return RSE_ERR_HIP;
+    }
+    hipLaunchKernelGGL(k_clear_header, dim3(1), dim3(64), 0, s, m->header(), n_tables, m->merged);
+    hipLaunchKernelGGL(k_clear_slots, dim3(fill_blocks(base, 256, 8192)), dim3(256), 0, s, m->d_slots(),
+                       base);
+    rc = launch_status();
+    if (rc) {
+        delete m;
+        return rc;
+    }
+    // the host copy of the directory is the source of an async copy: keep it
+    // alive by keeping the handle; make sure it has landed before returning
+    if (hipStreamSynchronize(s) != hipSuccess) {
+        delete m;
+        return RSE_ERR_HIP;
+    }
+    *out = m;
+    return RSE_OK;
+}
+
+int rse_idmap_destroy(rse_idmap* map) {
+    delete map;
+    return RSE_OK;
+}
+
+int rse_idmap_workspace_size(int64_t n_ids, size_t* bytes_out) {
+    if (!bytes_out || n_ids < 0) return RSE_ERR_INVALID_ARG;
+    carve(nullptr, n_ids, bytes_out);
+    return RSE_OK;
+}
+
+int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids, int64_t n_ids,
+                         const int64_t* d_bounds, int64_t stride, int32_t n_tables,
+                         int32_t insert_missing, int64_t* d_row_off_out, int64_t* d_n_new_out,
+                         void* d_ws, size_t ws_bytes, void* stream) {
+    if (!map || !blocks || !d_bounds || !d_n_new_out || !d_ws) return RSE_ERR_INVALID_ARG;
+    if (n_ids < 0 || stride <= 0 || n_tables <= 0) return RSE_ERR_INVALID_ARG;
+    if (n_ids > 0 && (!d_ids || !d_row_off_out)) return RSE_ERR_INVALID_ARG;
+    if (n_ids > (int64_t)0xFFFFFFFFll) return RSE_ERR_INVALID_ARG;
+    if (map->merged) {
+        if (n_tables > RSE_MAX_MERGED_TABLES) return RSE_ERR_INVALID_ARG;
+    } else if (n_tables != map->n_tables) {
+        return RSE_ERR_INVALID_ARG;
+    }
+    size_t need = 0;
+    Ws ws = carve(d_ws, n_ids, &need);
+    if (ws_bytes < need) return RSE_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+
+    hipLaunchKernelGGL(k_reset, dim3(1), dim3(256), 0, s, ws, map->d_dir(), map->n_tables);
+
+    ProbeArgs pa;
+    pa.slots = map->d_slots();
+    pa.dir = map->d_dir();
+    pa.ids = d_ids;
+    pa.n_ids = n_ids;
+    pa.bounds = d_bounds;
+    pa.stride = stride;
+    pa.n_tables = n_tables;
+    pa.merged = map->merged;
+    pa.insert = insert_missing ? 1 : 0;
+    pa.pad = 0;
+    pa.row_off = d_row_off_out;
+    pa.ws = ws;
+    // 8 lookups per wave per iteration; enough waves to fill 256 CUs
+    const int probe_blocks = fill_blocks((n_ids + 7) / 8, PROBE_BLOCK / 64, 256 * 16);
+    hipLaunchKernelGGL(k_probe, dim3(probe_blocks), dim3(PROBE_BLOCK), 0, s, pa);
+
+    const int miss_blocks = fill_blocks(n_ids, 256, 2048);
+    MarkArgs ma;
+    ma.slots = pa.slots;
+    ma.dir = pa.dir;
+    ma.n_regions = map->n_tables;
+    ma.merged = map->merged;
+    ma.ids = d_ids;
+    ma.bounds = d_bounds;
+    ma.stride = stride;
+    ma.n_tables = n_tables;
+    ma.pad = 0;
+    ma.ws = ws;
+    hipLaunchKernelGGL(k_mark, dim3(miss_blocks), dim3(256), 0, s, ma);
+
+    const int64_t n_tiles = (n_ids + SCAN_TILE - 1) / SCAN_TILE;
+    const dim3 tiles_grid((unsigned)(n_tiles > 0 ? n_tiles : 1));
+    hipLaunchKernelGGL(k_scan_reduce, tiles_grid, dim3(256), 0, s, ws, n_ids);
+    DecideArgs da;
+    da.dir = pa.dir;
+    da.n_regions = map->n_tables;
+    da.pad = 0;
+    da.bh = blocks->header();
+    da.mh = map->header();
+    da.capacity = blocks->capacity();
+    da.n_new_out = d_n_new_out;
+    da.n_tiles = n_tiles;
+    da.ws = ws;
+    hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, s, da);
+    hipLaunchKernelGGL(k_scan_down, tiles_grid, dim3(256), 0, s, ws, n_ids);
+
+    CommitArgs ca;
+    ca.slots = pa.slots;
+    ca.dir = pa.dir;
+    ca.n_regions = map->n_tables;
+    ca.merged = map->merged;
+    ca.ids = d_ids;
+    ca.bounds = d_bounds;
+    ca.stride = stride;
+    ca.n_tables = n_tables;
+    ca.pad = 0;
+    ca.ws = ws;
+    hipLaunchKernelGGL(k_commit, dim3(miss_blocks), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(k_resolve, dim3(miss_blocks), dim3(256), 0, s, pa.slots, pa.dir, map->merged,
+                       d_bounds, stride, n_tables, ws, d_row_off_out);
+    const int64_t init_work = n_ids * (blocks->row_bytes / 16);
+    const dim3 init_grid(fill_blocks(init_work, 256, 8192));
+    if (blocks->w_dtype == RSE_BF16)
+        hipLaunchKernelGGL(k_init_rows<true>, init_grid, dim3(256), 0, s, blocks->view(), blocks->dim,
+                           blocks->row_bytes, blocks->seed, ws);
+    else
+        hipLaunchKernelGGL(k_init_rows<false>, init_grid, dim3(256), 0, s, blocks->view(), blocks->dim,
+                           blocks->row_bytes, blocks->seed, ws);
+    return launch_status();
+}
+
+int rse_idmap_status(rse_idmap* map, int32_t* status_out, int64_t* n_keys_out, void* stream) {
+    if (!map) return RSE_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    MapHeader h;
+    if (hipMemcpyAsync(&h, map->header(), sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return RSE_ERR_HIP;
+    std::vector<TableDir> dir(map->n_tables);
+    if (n_keys_out && hipMemcpyAsync(dir.data(), map->d_dir(), sizeof(TableDir) * map->n_tables,
+                                     hipMemcpyDeviceToHost, s) != hipSuccess)
+        return RSE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return RSE_ERR_HIP;
+    if (status_out) *status_out = h.status;
+    if (n_keys_out)
+        for (int t = 0; t < map->n_tables; ++t) n_keys_out[t] = dir[t].n_keys;
+    return RSE_OK;
+}
+
+int rse_idmap_clear_status(rse_idmap* map, void* stream) {
+    if (!map) return RSE_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, as_stream(stream), map->header());
+    return launch_status();
+}
+
+int rse_idmap_export(rse_idmap* map, int64_t* d_keys_out, int32_t* d_table_out, int64_t* d_off_out,
+                     int64_t capacity, int64_t* d_count_out, void* stream) {
+    if (!map || !d_count_out || capacity < 0) return RSE_ERR_INVALID_ARG;
+    if (capacity > 0 && (!d_keys_out || !d_table_out || !d_off_out)) return RSE_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    unsigned long long* cnt = reinterpret_cast<unsigned long long*>(d_count_out);
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, s, cnt);
+    hipLaunchKernelGGL(k_export, dim3(fill_blocks(map->total_slots, 256, 8192)), dim3(256), 0, s,
+                       map->d_slots(), map->d_dir(), map->n_tables, map->total_slots, d_keys_out,
+                       d_table_out, d_off_out, capacity, cnt);
+    return launch_status();
+}
+
+}  // extern "C"

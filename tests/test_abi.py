@@ -1,0 +1,96 @@
+"""C ABI: the library loads without a GPU, exports every symbol rse.h
+declares, and its host-only calls (sizes, status names, argument checks)
+behave as documented.  No device work is issued here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rse.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from recommender_sparse_embedding_amd import _lib
+
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from recommender_sparse_embedding_amd import _lib
+
+    names = _declared()
+    assert {"idmap_find_or_insert", "embedding_bag_fwd", "embedding_bag_bwd_update", "blocks_grow"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings(lib):
+    from recommender_sparse_embedding_amd import _lib
+
+    for code, name in _lib.STATUS.items():
+        assert lib.rse_status_str(code).decode() == name
+    assert lib.rse_status_str(-99).decode() == "RSE_ERR_UNKNOWN"
+
+
+def _row_bytes(lib, dim, dt, opt):
+    out = ctypes.c_int64()
+    rc = lib.rse_blocks_row_bytes(dim, dt, opt, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_row_bytes_and_page_sizing(lib):
+    # row = weights + optimizer state, 16-byte aligned
+    assert _row_bytes(lib, 128, 0, 1) == (0, 1024)      # click-log: w + Adagrad acc
+    assert _row_bytes(lib, 64, 0, 2) == (0, 768)        # w + Adam m, v
+    assert _row_bytes(lib, 32, 1, 1) == (0, 192)        # bf16 w + fp32 acc
+    assert _row_bytes(lib, 16, 0, 0) == (0, 64)
+    assert _row_bytes(lib, 8, 1, 0) == (0, 16)
+    # "阿里 RecIS：搜广推训练的背景与难点": 1e9 ids x 64 fp32 ~ 256 GB (weights only)
+    assert _row_bytes(lib, 64, 0, 0)[1] * 10**9 == 256 * 10**9
+    # the same table with Adam state: 2e8 live rows ~ 153.6 GB, within 288 GB of HBM
+    assert _row_bytes(lib, 64, 0, 2)[1] * 2 * 10**8 == 153_600_000_000
+    # "DLRM ...", 案例 1: 1e8 x 64 fp32 = 25.6 GB
+    assert _row_bytes(lib, 64, 0, 0)[1] * 10**8 == 25_600_000_000
+    assert _row_bytes(lib, 3, 0, 0)[0] == -2            # unsupported dim
+    assert _row_bytes(lib, 4, 1, 0)[0] == -2            # bf16 needs dim >= 8
+    assert _row_bytes(lib, 16, 0, 7)[0] == -1           # bad optimizer
+
+
+def test_sizes_are_host_only_and_monotone(lib):
+    sz = ctypes.c_size_t()
+    slots = (ctypes.c_int64 * 2)(100, 9)
+    assert lib.rse_idmap_mem_size(2, slots, ctypes.byref(sz)) == 0
+    assert sz.value == 256 + 256 + (104 + 16) * 16        # header, 2 dir entries (padded), slots
+    assert lib.rse_idmap_mem_size(0, slots, ctypes.byref(sz)) == -1
+    assert lib.rse_idmap_mem_size(2000, slots, ctypes.byref(sz)) == -1
+    prev = 0
+    for n in (0, 1, 4096, 10**6):
+        assert lib.rse_idmap_workspace_size(n, ctypes.byref(sz)) == 0
+        assert sz.value >= prev
+        prev = sz.value
+    prev = 0
+    for n in (1, 4096, 10**6):
+        assert lib.rse_bwd_workspace_size(n, 26, 65536, 128, ctypes.byref(sz)) == 0
+        assert sz.value >= 16 * n and sz.value >= prev
+        prev = sz.value
+    assert lib.rse_bwd_workspace_size(-1, 1, 1, 16, ctypes.byref(sz)) == -1
+    assert lib.rse_blocks_meta_size(16, ctypes.byref(sz)) == 0 and sz.value == 512   # 256 + 128, 256-aligned
+
+
+def test_null_handles_rejected_without_gpu_work(lib):
+    assert lib.blocks_grow(None, None, 0, None) == -1
+    assert lib.embedding_bag_fwd(None, None, 0, None, 1, 1, 0, None, None) == -1
+    assert lib.idmap_find_or_insert(None, None, None, 0, None, 1, 1, 1, None, None, None, 0, None) == -1
+    assert lib.embedding_bag_bwd_update(None, None, 0, None, 1, 1, 0, None, None, None, None, 0, None) == -1
+    assert lib.rse_version() == 100

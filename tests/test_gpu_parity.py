@@ -1,0 +1,274 @@
+"""HIP path vs the CPU oracle, element by element, on seeded inputs.
+
+Bar: bit-exact for row offsets, new-key counts, map contents, unique-row
+counts and untouched rows; pooled outputs and updated rows within
+1e-5 (fp32 storage) / 1e-2 (bf16 storage) of the oracle's magnitude bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import GpuTables, assert_close, compare_rows, make_oracle, pooled_magnitude, rtol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64):
+    wl = synth.Workload(cfg)
+    orc = make_oracle(cfg)
+    L_est = cfg.n_bags * (cfg.bag[2] if cfg.bag[0] == "uniform" else
+                          cfg.bag[1] * 2 if cfg.bag[0] == "poisson" else cfg.bag[1])
+    max_rows = int(wl.card.sum() if cfg.prepopulate else 0) + (max_new or L_est * steps) + 1024
+    extra = (max_new or L_est * steps) if (cfg.fresh_frac > 0 or not cfg.prepopulate) else 0
+    gpu = GpuTables(cfg, wl.card, max_rows, extra_keys=extra)
+    rtol = rtol_for(cfg.wdtype)
+    for ids, bounds in wl.prepopulation(prepop_chunk):
+        ro_r, nn_r = orc.find_or_insert(ids, bounds, 1)
+        ro_g, nn_g = gpu.find_or_insert(ids, bounds, 1)
+        assert nn_g == nn_r
+        assert np.array_equal(ro_g.cpu().numpy(), ro_r)
+    rng = np.random.default_rng(5)
+    for step in range(steps):
+        _say(f"  step {step}")
+        ids, bo = wl.batch_inputs(step)
+        ro_r, nn_r = orc.find_or_insert(ids, bo, cfg.batch)
+        ro_g, nn_g = gpu.find_or_insert(ids, bo, cfg.batch)
+        assert nn_g == nn_r, (nn_g, nn_r)
+        assert np.array_equal(ro_g.cpu().numpy(), ro_r), "row offsets"
+        out_g = gpu.fwd(ro_g, bo)
+        out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
+        assert_close(out_g.cpu().numpy(), out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol, "pooled output")
+        if cfg.grad == "sumsq":           # loss = sum of squared pooled outputs
+            G_r = (2.0 * out_r).astype(np.float32)
+            G_g = 2.0 * out_g
+        else:
+            G_r = wl.grad(step)
+            G_g = torch.from_numpy(G_r).to(gpu.dev)
+        offs = np.unique(ro_r[ro_r >= 0])
+        prev_w, _ = orc.get_rows(offs)
+        n_rows = orc.n_rows
+        U_r = orc.bwd_update(ro_r, bo, cfg.batch, G_r, cfg.pooling)
+        U_g = gpu.bwd(ro_g, bo, G_g)
+        assert U_g == U_r == len(offs)
+        compare_rows(gpu, orc, prev_w, offs, rtol, f"step {step}")
+        if check_untouched and n_rows > len(offs):
+            untouched = np.setdiff1d(rng.choice(n_rows, min(n_rows, check_untouched * 4), replace=False), offs)
+            untouched = untouched[:check_untouched]
+            w_g, s_g = gpu.rows(untouched)
+            w_r, s_r = orc.get_rows(untouched)
+            assert np.array_equal(w_g.view(np.uint32), w_r.view(np.uint32)), "untouched rows changed"
+            assert np.array_equal(s_g.view(np.uint32), s_r.view(np.uint32))
+    return gpu, orc
+
+
+def test_toy_example():
+    """10-row dim-4 table, ids {2,5,7}, loss sum(e^2), SGD 0.1."""
+    cfg = synth.config(1, n_tables=1, batch=3, dim=4, bag=("fixed", 1), prepopulate=False)
+    orc = make_oracle(cfg)
+    gpu = GpuTables(cfg, [10], 64)
+    keys = np.arange(10, dtype=np.int64)
+    ro_g, n_g = gpu.find_or_insert(keys, np.array([0, 10]), 1)
+    ro_r, n_r = orc.find_or_insert(keys, [0, 10])
+    assert n_g == n_r == 10 and np.array_equal(ro_g.cpu().numpy(), ro_r)
+    W0_g, _ = gpu.rows(np.arange(10))
+    W0_r, _ = orc.get_rows(np.arange(10))
+    assert np.array_equal(W0_g.view(np.uint32), W0_r.view(np.uint32)), "initial rows"
+    ids = np.array([2, 5, 7], np.int64)
+    bo = np.arange(4, dtype=np.int64)
+    ro_g, _ = gpu.find_or_insert(ids, bo, 3)
+    out = gpu.fwd(ro_g, bo)
+    assert np.array_equal(out.cpu().numpy()[:, 0], W0_r[ids])
+    assert gpu.bwd(ro_g, bo, 2.0 * out) == 3
+    W1, _ = gpu.rows(np.arange(10))
+    rest = [0, 1, 3, 4, 6, 8, 9]
+    assert np.array_equal(W1[rest].view(np.uint32), W0_r[rest].view(np.uint32))
+    ref = (W0_r[ids].astype(np.float64) - 0.1 * (2.0 * W0_r[ids].astype(np.float64))).astype(np.float32)
+    assert np.array_equal(W1[ids], ref)
+
+
+@pytest.mark.parametrize("merged", [False, True])
+def test_idmap_edge_keys_bit_exact(merged):
+    """Sentinel-valued key, extremes, the modulo-collision pair, duplicates,
+    the same key in several tables; a crowded map (load 0.9)."""
+    T = 3
+    cfg = synth.config(1, n_tables=T, batch=1, dim=8, merged=merged, prepopulate=False)
+    orc = make_oracle(cfg)
+    rng = np.random.default_rng(0)
+    hi = 2**56 if merged else 2**63
+    special = [0, 1, 1180210, 721458, hi - 1]
+    if not merged:
+        special += [-(2**63), -1, 2**63 - 1, -(2**62)]
+    n_per = 3000
+    ids_t = []
+    for t in range(T):
+        base = rng.integers(0, hi, n_per - len(special) - 200, dtype=np.int64)
+        dup = rng.choice(base, 200)
+        x = np.concatenate([special, base, dup]).astype(np.int64)
+        rng.shuffle(x)
+        ids_t.append(x)
+    ids = np.concatenate(ids_t)
+    bounds = np.array([0, n_per, 2 * n_per, 3 * n_per], np.int64)
+    gpu = GpuTables(cfg, [n_per] * T, 4 * T * n_per, load=0.85)
+    ro_r, n_r = orc.find_or_insert(ids, bounds, 1)
+    ro_g, n_g = gpu.find_or_insert(ids, bounds, 1)
+    assert n_g == n_r
+    assert np.array_equal(ro_g.cpu().numpy(), ro_r)
+    # a second pass: everything hits; plus a few unseen keys without insert
+    probe = np.concatenate([ids[:100], np.array([12345678901, 98765], np.int64), ids[-100:]])
+    pb = np.array([0, 100, 102, 202], np.int64)
+    r1, nn1 = orc.find_or_insert(probe, pb, 1, insert_missing=False)
+    g1, ng1 = gpu.find_or_insert(probe, pb, 1, insert=False)
+    assert nn1 == ng1 == 0 and np.array_equal(g1.cpu().numpy(), r1)
+    assert (r1 == -1).sum() >= 1
+    # map contents
+    keys_r, tabs_r = orc.map_dump()
+    k, tb, off, cnt = gpu.map.export(len(keys_r) + 10)
+    assert cnt == len(keys_r)
+    order = np.argsort(off.cpu().numpy())
+    assert np.array_equal(off.cpu().numpy()[order], np.arange(len(keys_r)))
+    assert np.array_equal(k.cpu().numpy()[order], keys_r)
+    assert np.array_equal(tb.cpu().numpy()[order], tabs_r)
+    # initial rows are the key-derived values
+    offs = np.arange(0, len(keys_r), 7)
+    w_g, _ = gpu.rows(offs)
+    w_r, _ = orc.get_rows(offs)
+    assert np.array_equal(w_g.view(np.uint32), w_r.view(np.uint32))
+
+
+@pytest.mark.parametrize("dim,wdtype,pooling", [
+    (4, 0, 0), (16, 0, 0), (32, 1, 0), (64, 0, 1), (128, 0, 0), (256, 0, 1), (8, 1, 1), (256, 1, 0)])
+def test_forward_variants(dim, wdtype, pooling):
+    """Short and long bags (both schedules), empty bags, duplicates."""
+    for bag in (("uniform", 0, 6), ("uniform", 20, 140)):
+        cfg = synth.config(1, n_tables=3, batch=300, dim=dim, wdtype=wdtype, pooling=pooling, bag=bag,
+                           cardinality=("fixed", 500), prepopulate=True, zipf_a=1.1)
+        run_steps(cfg, 1)
+
+
+@pytest.mark.parametrize("optim", [0, 1, 2])
+@pytest.mark.parametrize("wdtype", [0, 1])
+def test_update_variants(optim, wdtype):
+    """Every optimizer x storage type, hot keys with segments far beyond one
+    piece, mean pooling for Adam."""
+    cfg = synth.config(3, n_tables=2, batch=512, dim=32, wdtype=wdtype, optim=optim,
+                       lr=[0.05, 0.01, 1e-3][optim], cardinality=("fixed", 20000), bag=("uniform", 1, 40),
+                       fresh_frac=0.01, pooling=1 if optim == 2 else 0)
+    run_steps(cfg, 3)
+
+
+def test_config1_multi_hot_sgd_full():
+    """8 tables, dim 16, batch 1024, bags U[1,8], Zipf(1.05) over 1e5 keys,
+    sum-of-squares loss, SGD 0.1, tables start empty: 10 free-running steps."""
+    run_steps(synth.config(1), 10)
+
+
+def test_config2_click_log_twin():
+    """26 one-hot tables, dim 128, Adagrad; batch 2048, cardinalities
+    log-uniform in [10, 2e5]."""
+    run_steps(synth.config(2, batch=2048, cardinality=("loguniform", 10, 200_000)), 3, prepop_chunk=100_000)
+
+
+def test_config3_sequence_mean_adam_twin():
+    run_steps(synth.config(3, batch=256, cardinality=("fixed", 50_000)), 3)
+
+
+def test_config4_uniform_int64_twin():
+    run_steps(synth.config(4, batch=1024, cardinality=("fixed", 200_000)), 2)
+
+
+def test_config5_merged_bf16_twin():
+    run_steps(synth.config(5, batch=128, cardinality=("fixed", 10_000)), 2)
+
+
+def test_run_to_run_bit_identical():
+    cfg = synth.config(2, n_tables=4, batch=4096, cardinality=("fixed", 3000))
+    res = []
+    for _ in range(2):
+        gpu, orc = run_steps(cfg, 2, check_untouched=0)
+        w, s = gpu.rows(np.arange(orc.n_rows))
+        res.append((w.view(np.uint32).copy(), s.view(np.uint32).copy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+# ----------------------------------------------------------- failures ----
+def test_need_grow_commits_nothing_and_retry_matches():
+    cfg = synth.config(1, n_tables=1, batch=40, dim=16, bag=("fixed", 1), prepopulate=False)
+    import recommender_sparse_embedding_amd as rse
+
+    gpu = GpuTables(cfg, [1000], 16, rows_per_chunk_log2=4)     # one chunk of 16 rows
+    orc = make_oracle(cfg)
+    ids = np.arange(100, 140, dtype=np.int64)                   # 40 new keys > 16 rows
+    ro, n = gpu.find_or_insert(ids, np.array([0, 40]), 1)
+    assert n == 0 and np.all(ro.cpu().numpy() == -1)
+    st, nkeys = gpu.map.status()
+    assert st == -5 and nkeys == [0]
+    assert gpu.map.export(100)[3] == 0
+    gpu.blocks.grow(2)
+    gpu.map.clear_status()
+    ro, n = gpu.find_or_insert(ids, np.array([0, 40]), 1)
+    ro_r, n_r = orc.find_or_insert(ids, [0, 40])
+    assert n == n_r == 40 and np.array_equal(ro.cpu().numpy(), ro_r)
+    assert gpu.map.status()[0] == 0
+    w_g, _ = gpu.rows(np.arange(40))
+    w_r, _ = orc.get_rows(np.arange(40))
+    assert np.array_equal(w_g, w_r)
+
+
+def test_idmap_full_commits_nothing():
+    cfg = synth.config(1, n_tables=1, batch=1, dim=8, prepopulate=False)
+    import recommender_sparse_embedding_amd as rse
+
+    m = rse.IdMap([16], max_load=0.5, device="cuda")             # at most 8 keys
+    b = rse.EmbeddingBlocks(8, 0, 0, 6, device="cuda").grow(1)
+    n_new = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ids = torch.arange(10, dtype=torch.int64, device="cuda")
+    ro = torch.empty_like(ids)
+    rse.idmap_find_or_insert(m, b, ids, torch.tensor([0, 10], device="cuda"), 1, 1, ro, n_new)
+    assert int(n_new.item()) == 0 and bool((ro == -1).all())
+    assert m.status() == (-4, [0])
+    assert b.status() == (0, 0)
+    m.clear_status()
+    rse.idmap_find_or_insert(m, b, ids[:6], torch.tensor([0, 6], device="cuda"), 1, 1, ro[:6], n_new)
+    assert int(n_new.item()) == 6 and ro[:6].tolist() == list(range(6))
+    assert m.status() == (0, [6]) and b.status() == (6, 0)
+    del cfg
+
+
+def test_bad_inputs_are_reported_not_faulted():
+    import recommender_sparse_embedding_amd as rse
+
+    # merged map: an id >= 2^56 is rejected, nothing inserted
+    m = rse.IdMap([64], max_load=0.7, merged=True, device="cuda")
+    b = rse.EmbeddingBlocks(8, 0, 0, 6, device="cuda").grow(1)
+    n_new = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ids = torch.tensor([5, 2**56, 7], dtype=torch.int64, device="cuda")
+    ro = torch.empty_like(ids)
+    rse.idmap_find_or_insert(m, b, ids, torch.tensor([0, 3], device="cuda"), 1, 1, ro, n_new)
+    assert int(n_new.item()) == 0 and m.status()[0] == -9 and bool((ro == -1).all())
+    # forward with decreasing offsets and an out-of-range row: status, no fault
+    m.clear_status()
+    ro = torch.tensor([0, 1, 5000], dtype=torch.int64, device="cuda")
+    rse.idmap_find_or_insert(m, b, ids[[0, 2]].contiguous(), torch.tensor([0, 2], device="cuda"), 1, 1,
+                             ro[:2], n_new)
+    out = torch.zeros((2, 1, 8), dtype=torch.float32, device="cuda")
+    rse.embedding_bag_fwd(b, ro, torch.tensor([0, 3, 1], device="cuda"), 1, 2, 0, out)
+    torch.cuda.synchronize()
+    assert b.status()[1] == -9
+    b.clear_status()
+    rse.embedding_bag_fwd(b, ro, torch.tensor([0, 2, 3], device="cuda"), 1, 2, 0, out)
+    assert b.status()[1] == -9                                  # row 5000 >= capacity 64
+    b.clear_status()
+    g = torch.ones((2, 1, 8), dtype=torch.float32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int64, device="cuda")
+    w0, _ = b.read_rows(torch.tensor([0, 1], device="cuda"))
+    rse.embedding_bag_bwd_update(b, ro, torch.tensor([0, 2, 3], device="cuda"), 1, 2, 0, g,
+                                 rse.Optim(0, 0.1), 1, nu)
+    assert b.status()[1] == -9 and int(nu.item()) == 0
+    w1, _ = b.read_rows(torch.tensor([0, 1], device="cuda"))
+    assert torch.equal(w0, w1)                                  # nothing updated
