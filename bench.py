@@ -1,0 +1,288 @@
+"""Benchmark: one training step of the sparse-embedding hot path on one MI355X.
+
+A step = idmap_find_or_insert -> embedding_bag_fwd -> embedding_bag_bwd_update
+over one batch of the click-log workload: 26 one-hot tables, dim 128 fp32,
+batch 65536, per-table cardinality log-uniform in [10, 4e7] (55.8M live rows
+for the seed used), Zipf(1.1) lookups over random 63-bit keys, Adagrad (lr
+0.01, eps 1e-8) with fp32 accumulator rows, N(0,1) upstream gradients.
+Inputs are synthetic, seeded, and resident in HBM before timing starts.
+
+Prints one JSON line: lookups/s (the metric), plus updated rows/s, the step's
+compulsory HBM bytes per second against the 8 TB/s peak, a roofline entry for
+the dominant kernel (timed live with HIP events on the library's stream) and
+the CPU oracle timed on the host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2, help="workload number (2 = click-log, the headline)")
+    p.add_argument("--batches", type=int, default=4, help="distinct batches cycled through")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-steps", type=int, default=2)
+    p.add_argument("--map-load", type=float, default=0.5)
+    return p.parse_args()
+
+
+def compulsory_bytes(cfg, L, U, n_new, row_bytes):
+    """Bytes the step must move at least once: ids, bag offsets, one map slot
+    per distinct key, read+write of every touched row (weights + state), the
+    pooled output write and the upstream-gradient read, new-row init."""
+    TB = cfg.n_tables * cfg.batch
+    return (L * 8 + (TB + 1) * 8 + U * 16 + U * row_bytes * 2 + TB * cfg.dim * 4 * 2
+            + n_new * row_bytes)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import recommender_sparse_embedding_amd as rse
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config(args.config)
+    wl = synth.Workload(cfg)
+    T, B, D = cfg.n_tables, cfg.batch, cfg.dim
+    t0 = time.time()
+
+    # ---------------------------------------------------------- setup ----
+    total_keys = int(wl.card.sum())
+    if cfg.merged:
+        slots = [int(total_keys / args.map_load) + 1024]
+    else:
+        slots = [int(c / args.map_load) + 1024 for c in wl.card]
+    idm = rse.IdMap(slots, max_load=0.9, merged=cfg.merged, hash_seed=12345, device=dev)
+    chunk_log2 = 20
+    blk = rse.EmbeddingBlocks(D, cfg.wdtype, cfg.optim, chunk_log2, max_chunks=4096, seed=cfg.seed,
+                              device=dev)
+    # rows the timed steps can add: never-seen keys (fresh fraction, or every
+    # key when tables start empty), bounded by the lookups of all steps
+    max_bag = {"fixed": cfg.bag[1], "uniform": cfg.bag[-1], "poisson": 3 * cfg.bag[1]}[cfg.bag[0]]
+    new_frac = 1.0 if not cfg.prepopulate else cfg.fresh_frac
+    headroom = int(new_frac * cfg.n_bags * max_bag * (args.steps + args.warmup)) + (1 << chunk_log2)
+    blk.grow(-(-(total_keys + headroom) // (1 << chunk_log2)))
+    opt = rse.Optim(cfg.optim, cfg.lr, cfg.eps, cfg.beta1, cfg.beta2)
+    n_new = torch.zeros(1, dtype=torch.int64, device=dev)
+    pre_ws = idm.workspace(1 << 24)
+    for ids, bounds in wl.prepopulation(chunk=1 << 24):
+        t_ids = torch.from_numpy(ids).to(dev)
+        ro = torch.empty_like(t_ids)
+        rse.idmap_find_or_insert(idm, blk, t_ids, torch.from_numpy(bounds).to(dev), 1, T, ro, n_new,
+                                 ws=pre_ws)
+    torch.cuda.synchronize()
+    used, st = blk.status()
+    assert st == 0 and used == total_keys, (used, st)
+    log(f"prepopulated {total_keys} keys in {time.time() - t0:.1f}s")
+
+    batches = []
+    for k in range(args.batches):
+        ids, bo = wl.batch_inputs(k)
+        # distinct (table, key) pairs = rows the step updates (all keys are live)
+        tab = np.repeat(np.arange(T), np.diff(bo[::B]))
+        U = len(np.unique(np.stack([tab, ids], 1), axis=0)) if len(ids) else 0
+        g = torch.from_numpy(wl.grad(k)).to(dev) if cfg.grad == "normal" else None
+        batches.append(dict(ids=torch.from_numpy(ids).to(dev), bo=torch.from_numpy(bo).to(dev),
+                            grad=g, L=len(ids), U=U, ro=torch.empty(len(ids), dtype=torch.int64, device=dev)))
+    L_max = max(b["L"] for b in batches)
+    find_ws = idm.workspace(L_max)
+    bwd_ws = rse.bwd_workspace(L_max, T, B, D, dev)
+    out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    n_u = torch.zeros(1, dtype=torch.int64, device=dev)
+    log(f"staged {len(batches)} batches, setup {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    step_no = [0]
+
+    def step(b, ev=None):
+        if ev:
+            ev[0].record(stream)
+        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws)
+        if ev:
+            ev[1].record(stream)
+        rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
+        if ev:
+            ev[2].record(stream)
+        g = b["grad"] if b["grad"] is not None else 2.0 * out
+        step_no[0] += 1
+        rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+                                     ws=bwd_ws)
+        if ev:
+            ev[3].record(stream)
+
+    for k in range(args.warmup):
+        step(batches[k % len(batches)])
+    torch.cuda.synchronize()
+    used, st = blk.status()
+    assert st == 0, st
+
+    # ----------------------------------------------------- timed region --
+    # The library brackets every launch of the segmented-update kernel (the
+    # step's largest) with HIP events on its stream while the trace is on.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rse.trace_start(rse.K_SEG_UPDATE)
+    w0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(batches[(args.warmup + k) % len(batches)], evs[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    n_seg, seg_ms = rse.trace_stop()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    t_find = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    t_seg = seg_ms / max(n_seg, 1)
+    idm_st, _ = idm.status()
+    used, st = blk.status()
+    assert idm_st == 0 and st == 0, (idm_st, st)
+
+    sel = [batches[(args.warmup + k) % len(batches)] for k in range(args.steps)]
+    L_avg = float(np.mean([b["L"] for b in sel]))
+    U_avg = float(np.mean([b["U"] for b in sel]))
+    rb = blk.row_bytes
+    comp = float(np.mean([compulsory_bytes(cfg, b["L"], b["U"], 0, rb) for b in sel]))
+    lookups_s = L_avg / (ms_step * 1e-3)
+    rows_s = U_avg / (ms_step * 1e-3)
+    step_gbs = comp / (ms_step * 1e-3) / 1e9
+
+    # roofline of the segmented-update kernel: algorithmic bytes per launch =
+    # sorted (row, gradient-row) pairs read (8 B per lookup) + one gradient row
+    # per lookup (dim * 4 B) + each touched row (weights + state) read and
+    # written once
+    seg_bytes = float(np.mean([b["L"] * 8 + b["L"] * D * 4 + b["U"] * rb * 2 for b in sel]))
+    seg_gbs = seg_bytes / (t_seg * 1e-3) / 1e9
+    TB = T * B
+    w_bytes = D * (2 if cfg.wdtype == synth.BF16 else 4)
+    fwd_bytes = float(np.mean([b["L"] * 8 + (TB + 1) * 8 + b["U"] * w_bytes + TB * D * 4 for b in sel]))
+    traffic = read_traffic("seg_update_clicklog.txt", KERNEL_REV)
+    roofline = {"bound": "hbm", "kernel": f"k_seg_update<{D},{'bf16' if cfg.wdtype else 'f32'}>",
+                "achieved": round(seg_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(seg_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": int(seg_bytes), "avg_launch_ms": round(t_seg, 4),
+                "launches_timed": n_seg}
+    fwd_roof = {"kernel": "embedding_bag_fwd", "achieved": round(fwd_bytes / (t_fwd * 1e-3) / 1e9, 1),
+                "unit": "GB/s", "algorithmic_bytes_per_launch": int(fwd_bytes),
+                "avg_launch_ms": round(float(t_fwd), 4)}
+
+    # --------------------------------------------------- CPU baseline -----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, wl, args.cpu_steps)
+
+    res = {
+        "metric": "embedding lookups/sec (fwd+bwd+update), 1 MI355X",
+        "value": round(lookups_s, 1),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 storage, f64 accumulate" if cfg.wdtype == synth.F32 else "bf16 storage, f64 accumulate",
+        "data": "synthetic (seeded Zipf lookups over random 63-bit keys, N(0,1) grads)",
+        "config": {"workload": f"{cfg.name}: {T} tables x batch {B}, dim {D}, "
+                               f"{total_keys} live rows", "tables": T, "batch": B, "dim": D,
+                   "lookups_per_step": L_avg, "unique_rows_per_step": U_avg, "live_rows": total_keys,
+                   "map_load": args.map_load},
+        "updated_rows_per_s": round(rows_s, 1),
+        "step_compulsory_bytes": int(comp),
+        "step_hbm_gbs": round(step_gbs, 1),
+        "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4),
+        "ms_find": round(float(t_find), 4), "ms_fwd": round(float(t_fwd), 4), "ms_bwd_update": round(float(t_bwd), 4),
+        "wall_s": round(wall, 4),
+        "roofline": roofline,
+        "fwd_roofline": fwd_roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+# identifies the kernel source the stored traffic counters were taken on
+KERNEL_REV = "seg-v3"
+
+
+def read_traffic(name, rev):
+    """HBM bytes per launch from a committed counter summary (profiles/),
+    or None if absent or taken on another kernel revision."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_rev") != rev or "hbm_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["hbm_bytes_per_launch"]))
+
+
+def cpu_baseline(cfg, wl, steps):
+    """The oracle, single-threaded, on the same workload: the full key
+    universe inserted, then `steps` whole steps (find + forward + backward
+    with update); lookups per second of the timed steps."""
+    import oracle
+
+    t0 = time.time()
+    orc = oracle.OracleTable(cfg.dim, cfg.wdtype, cfg.optim, cfg.n_tables, cfg.merged, seed=cfg.seed,
+                             lr=cfg.lr, eps=cfg.eps, beta1=cfg.beta1, beta2=cfg.beta2)
+    for ids, bounds in wl.prepopulation(chunk=1 << 24):
+        orc.find_or_insert(ids, bounds, 1)
+    log(f"oracle prepopulated in {time.time() - t0:.1f}s")
+    tot_L, tot_t = 0, 0.0
+    for k in range(steps):
+        ids, bo = wl.batch_inputs(k)
+        g = wl.grad(k)
+        s = time.perf_counter()
+        ro, _ = orc.find_or_insert(ids, bo, cfg.batch)
+        out = orc.fwd(ro, bo, cfg.batch, cfg.pooling)
+        if cfg.grad != "normal":
+            g = (2.0 * out).astype(np.float32)
+        orc.bwd_update(ro, bo, cfg.batch, g, cfg.pooling)
+        tot_t += time.perf_counter() - s
+        tot_L += len(ids)
+    return {"value": round(tot_L / tot_t, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full steps ({tot_L} lookups) after inserting all {int(wl.card.sum())} keys; "
+                      f"{tot_t:.1f}s timed"}
+
+
+if __name__ == "__main__":
+    main()

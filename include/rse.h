@@ -272,6 +272,28 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
                              int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes,
                              void* stream);
 
+/* ------------------------------------------------------- kernel trace -- */
+/*
+ * Per-kernel timing with HIP events, for measurement: while a trace is
+ * active the library records an event pair on the launch stream around every
+ * launch of the chosen kernel (process-wide, up to 4096 launches).  Host
+ * code only; recording adds two stream markers per traced launch.
+ */
+enum {
+    RSE_K_PROBE = 1,       /* IDMap probe / insert-claim kernel */
+    RSE_K_FWD = 2,         /* pooled forward kernel */
+    RSE_K_SORT_SCATTER = 3, /* radix-sort scatter (one per digit pass) */
+    RSE_K_SEG_UPDATE = 4,  /* segmented reduction + fused optimizer */
+    RSE_K_COMBINE = 5      /* long-segment combine */
+};
+
+/* Start tracing `kernel` (one RSE_K_* id); clears earlier records. */
+int rse_trace_start(int32_t kernel);
+
+/* Stop tracing; synchronises the recorded events and returns the number of
+ * traced launches and their summed duration in milliseconds. */
+int rse_trace_stop(int64_t* n_launches_out, double* total_ms_out);
+
 #ifdef __cplusplus
 }
 #endif

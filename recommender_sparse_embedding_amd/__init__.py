@@ -263,8 +263,25 @@ def embedding_bag_bwd_update(blocks: EmbeddingBlocks, row_off: torch.Tensor, bag
                                        _ptr(ws), ws.numel(), _stream(stream)), "embedding_bag_bwd_update")
 
 
+# ----------------------------------------------------------------- trace --
+K_PROBE, K_FWD, K_SORT_SCATTER, K_SEG_UPDATE, K_COMBINE = 1, 2, 3, 4, 5
+
+
+def trace_start(kernel: int):
+    """Record HIP events around every launch of `kernel` (a K_* id)."""
+    check(lib.rse_trace_start(kernel), "rse_trace_start")
+
+
+def trace_stop():
+    """(launches, total ms) of the traced kernel since trace_start."""
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    check(lib.rse_trace_stop(ctypes.byref(n), ctypes.byref(ms)), "rse_trace_stop")
+    return n.value, ms.value
+
+
 __all__ = [
     "F32", "BF16", "SGD", "ADAGRAD", "ADAM", "SUM", "MEAN", "Optim", "EmbeddingBlocks", "IdMap",
     "RseError", "blocks_grow", "idmap_find_or_insert", "embedding_bag_fwd", "embedding_bag_bwd_update",
-    "bwd_workspace", "row_bytes", "status_str", "lib",
+    "bwd_workspace", "row_bytes", "status_str", "lib", "trace_start", "trace_stop", "K_PROBE", "K_FWD",
+    "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE",
 ]

@@ -61,6 +61,8 @@ SIGNATURES = {
     "rse_bwd_workspace_size": ([_I64, _I32, _I64, _I32, _PSZ], ctypes.c_int),
     "embedding_bag_bwd_update": ([_P, _P, _I64, _P, _I32, _I64, _I32, _P, ctypes.POINTER(RseOptim), _P,
                                   _P, _SZ, _P], ctypes.c_int),
+    "rse_trace_start": ([_I32], ctypes.c_int),
+    "rse_trace_stop": ([_PI64, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
 }
 
 _lib = None

@@ -1,6 +1,8 @@
 """Build librse.so (the HIP library) in-tree with hipcc for gfx950.
 
-Usage: python -m recommender_sparse_embedding_amd.build
+Usage: python recommender_sparse_embedding_amd/build.py   (or __graft_entry__.build())
+This file must stay importable without the package (it builds what the
+package loads).
 """
 
 from __future__ import annotations

@@ -35,16 +35,16 @@ namespace {
 constexpr int P = 64;            // lookups per piece
 constexpr int LONG_T = 128;      // longest segment reduced by one group
 constexpr int HALO = LONG_T + 1;
+constexpr int MAX_SEG_BLOCKS = 65535;
 
 struct OptParams {
     double lr, eps, b1, b2, omb1, omb2, bc1, bc2;
 };
 
 struct Ctr {                     // device counters of one call
-    unsigned long long n_valid;
     unsigned long long n_owners;
     unsigned long long bad;
-    unsigned long long pad[5];
+    unsigned long long pad[6];
 };
 
 struct BwdArgs {
@@ -52,14 +52,18 @@ struct BwdArgs {
     const uint32_t* keys;        // sorted rows
     const uint32_t* vals;        // bag of each sorted lookup
     const int64_t* bag_off;
-    const float* grad;           // [batch, n_tables, dim]
+    const float* grad;           // [batch, n_tables, dim]; sorted values index its rows
     int64_t batch;
     int32_t n_tables;
     int32_t mean;
+    int64_t n;                   // lookups (sorted pairs)
+    uint32_t invalid;            // key of lookups without a row (sorted last)
+    int32_t n_seg_blocks;        // grid of the segmented-update kernel
     Ctr* ctr;
     double* carry;               // [n_pieces][2][dim]
     uint32_t* owners;            // head positions of long segments
-    unsigned long long* n_unique;
+    uint32_t* blk_unique;        // rows finished per segmented-update block
+    int64_t* n_unique;
     OptParams op;
 };
 
@@ -73,9 +77,8 @@ struct Geo {
 };
 
 // ------------------------------------------------------------- pairs -----
-__global__ void k_bwd_reset(Ctr* ctr, uint32_t* totals, int n_totals, unsigned long long* n_unique) {
+__global__ void k_bwd_reset(Ctr* ctr, uint32_t* totals, int n_totals, int64_t* n_unique) {
     if (threadIdx.x == 0) {
-        ctr->n_valid = 0;
         ctr->n_owners = 0;
         ctr->bad = 0;
         *n_unique = 0;
@@ -85,10 +88,11 @@ __global__ void k_bwd_reset(Ctr* ctr, uint32_t* totals, int n_totals, unsigned l
 
 // One thread per bag: key = row (or `invalid`), value = bag.  Malformed bag
 // offsets or rows beyond the capacity mark the call bad (nothing is updated).
+// The value is the lookup's gradient row b * n_tables + t (the layout of
+// grad), so the reduction reads gradients without any division.
 __global__ void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t n_bags, int64_t n_ids,
-                        int64_t capacity, uint32_t invalid, uint32_t* keys, uint32_t* vals, Ctr* ctr,
-                        int32_t* status) {
-    unsigned long long valid = 0;
+                        int64_t batch, int32_t n_tables, int64_t capacity, uint32_t invalid, uint32_t* keys,
+                        uint32_t* vals, Ctr* ctr, int32_t* status) {
     bool bad = false;
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_bags;
          j += (int64_t)gridDim.x * blockDim.x) {
@@ -97,26 +101,18 @@ __global__ void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t 
             bad = true;
             continue;
         }
+        const uint32_t t = (uint32_t)((uint64_t)j / (uint64_t)batch);
+        const uint32_t gr = (uint32_t)(j - (int64_t)t * batch) * (uint32_t)n_tables + t;
         for (int64_t i = s; i < e; ++i) {
             const int64_t r = row_off[i];
             uint32_t k = invalid;
             if (r >= 0) {
                 if (r >= capacity) bad = true;
-                else {
-                    k = (uint32_t)r;
-                    ++valid;
-                }
+                else k = (uint32_t)r;
             }
             keys[i] = k;
-            vals[i] = (uint32_t)j;
+            vals[i] = gr;
         }
-    }
-    // wave-aggregated counter update
-    const unsigned long long any = __ballot(valid != 0);
-    if (any) {
-        unsigned long long v = valid;
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-        if (lane_id() == 0) atomicAdd(&ctr->n_valid, v);
     }
     if (bad) {
         ctr->bad = 1;
@@ -126,11 +122,16 @@ __global__ void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t 
 
 // ------------------------------------------------------ grad gather ------
 template <int D, bool BF16>
-__device__ __forceinline__ const float* grad_row(const BwdArgs& a, uint32_t j, int li) {
-    using G = Geo<D, BF16>;
-    const int64_t t = (int64_t)j / a.batch;
-    const int64_t b = (int64_t)j - t * a.batch;
-    return a.grad + (b * a.n_tables + t) * D + li * G::VEC;
+__device__ __forceinline__ const float* grad_row(const BwdArgs& a, uint32_t gr, int li) {
+    return a.grad + (int64_t)gr * D + li * Geo<D, BF16>::VEC;
+}
+
+// Length of the bag whose gradient row is gr = b * n_tables + t (mean only).
+__device__ __forceinline__ double bag_len(const BwdArgs& a, uint32_t gr) {
+    const uint32_t b = gr / (uint32_t)a.n_tables;
+    const uint32_t t = gr - b * (uint32_t)a.n_tables;
+    const int64_t j = (int64_t)t * a.batch + b;
+    return (double)(a.bag_off[j + 1] - a.bag_off[j]);
 }
 
 template <int VEC>
@@ -145,54 +146,82 @@ __device__ __forceinline__ void load_grad(float* out, const float* src) {
     }
 }
 
-// acc += sum over sorted positions [x, y) (LDS window based at w0) in order.
+template <int VEC>
+__device__ __forceinline__ void add_grad(double* acc, const float* gv, bool mean, double len) {
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        double g = (double)gv[k];
+        if (mean) g = g / len;
+        acc[k] += g;
+    }
+}
+
+// acc += sum over window positions [x, y) of the LDS-staged bag ids, in
+// order.  U gradient rows are loaded together (all loads issued before any
+// is used); a tail shorter than U is loaded one row at a time.
 template <int D, bool BF16>
-__device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_vals, int64_t w0, int64_t x,
-                                          int64_t y, int li, double* acc) {
+__device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_vals, int x, int y, int li,
+                                          double* acc) {
     constexpr int VEC = Geo<D, BF16>::VEC;
-    constexpr int U = 4;
-    for (int64_t q = x; q < y; q += U) {
+    constexpr int U = 8;
+    int q = x;
+    for (; q + U <= y; q += U) {
         float gv[U][VEC];
-        double sc[U];
+        uint32_t j[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (q + u < y) {
-                const uint32_t j = s_vals[q + u - w0];
-                load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j, li));
-                sc[u] = a.mean ? (double)(a.bag_off[j + 1] - a.bag_off[j]) : 1.0;
-            }
-        }
+        for (int u = 0; u < U; ++u) j[u] = s_vals[q + u];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (q + u < y) {
+        for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
+        double len[U];
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    double g = (double)gv[u][k];
-                    if (a.mean) g = g / sc[u];
-                    acc[k] += g;
-                }
-            }
-        }
+        for (int u = 0; u < U; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+    }
+    for (; q < y; ++q) {
+        float gv[VEC];
+        const uint32_t j = s_vals[q];
+        load_grad<VEC>(gv, grad_row<D, BF16>(a, j, li));
+        const double len = a.mean ? bag_len(a, j) : 1.0;
+        add_grad<VEC>(acc, gv, a.mean, len);
     }
 }
 
 // ---------------------------------------------------------- epilogue -----
 // Row update in fp64, rounded once to the storage types.  Lane li owns
-// elements [li*VEC, li*VEC + VEC).
+// elements [li*VEC, li*VEC + VEC).  The row and its state are loaded before
+// the gradient gather so both are in flight together.
+template <int D, bool BF16>
+struct RowRegs {
+    static constexpr int VEC = Geo<D, BF16>::VEC;
+    uint4 w;
+    float st0[VEC];
+    float st1[VEC];
+};
+
 template <int D, bool BF16, int OPT>
-__device__ __forceinline__ void update_row(const BwdArgs& a, uint32_t row_idx, int li, const double* g) {
+__device__ __forceinline__ void load_row(const char* row, int li, RowRegs<D, BF16>& r) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     constexpr int64_t W_BYTES = (int64_t)D * (BF16 ? 2 : 4);
-    char* row = a.rv.row(row_idx);
-    uint4 wq = *reinterpret_cast<const uint4*>(row + li * 16);
+    r.w = *reinterpret_cast<const uint4*>(row + li * 16);
+    const float* st0 = reinterpret_cast<const float*>(row + W_BYTES) + li * VEC;
+    if (OPT != RSE_SGD) load_grad<VEC>(r.st0, st0);
+    if (OPT == RSE_ADAM) load_grad<VEC>(r.st1, st0 + D);
+}
+
+template <int D, bool BF16, int OPT>
+__device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, const RowRegs<D, BF16>& r,
+                                           const double* g) {
+    constexpr int VEC = Geo<D, BF16>::VEC;
+    constexpr int64_t W_BYTES = (int64_t)D * (BF16 ? 2 : 4);
     double w[VEC];
     if (!BF16) {
-        w[0] = __uint_as_float(wq.x);
-        w[1] = __uint_as_float(wq.y);
-        w[2] = __uint_as_float(wq.z);
-        w[3] = __uint_as_float(wq.w);
+        w[0] = __uint_as_float(r.w.x);
+        w[1] = __uint_as_float(r.w.y);
+        w[2] = __uint_as_float(r.w.z);
+        w[3] = __uint_as_float(r.w.w);
     } else {
-        const uint32_t q4[4] = {wq.x, wq.y, wq.z, wq.w};
+        const uint32_t q4[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             w[2 * k] = __uint_as_float(q4[k] << 16);
@@ -207,10 +236,9 @@ __device__ __forceinline__ void update_row(const BwdArgs& a, uint32_t row_idx, i
         for (int k = 0; k < VEC; ++k) wn[k] = w[k] - a.op.lr * g[k];
     } else if (OPT == RSE_ADAGRAD) {
         float acc[VEC];
-        load_grad<VEC>(acc, st0);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float an = (float)((double)acc[k] + g[k] * g[k]);
+            const float an = (float)((double)r.st0[k] + g[k] * g[k]);
             acc[k] = an;
             wn[k] = w[k] - a.op.lr * (g[k] / (sqrt((double)an) + a.op.eps));
         }
@@ -219,12 +247,10 @@ __device__ __forceinline__ void update_row(const BwdArgs& a, uint32_t row_idx, i
             *reinterpret_cast<float4*>(st0 + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
     } else {
         float m[VEC], v[VEC];
-        load_grad<VEC>(m, st0);
-        load_grad<VEC>(v, st1);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float mn = (float)(a.op.b1 * (double)m[k] + a.op.omb1 * g[k]);
-            const float vn = (float)(a.op.b2 * (double)v[k] + a.op.omb2 * g[k] * g[k]);
+            const float mn = (float)(a.op.b1 * (double)r.st0[k] + a.op.omb1 * g[k]);
+            const float vn = (float)(a.op.b2 * (double)r.st1[k] + a.op.omb2 * g[k] * g[k]);
             m[k] = mn;
             v[k] = vn;
             const double mh = (double)mn / a.op.bc1;
@@ -252,121 +278,233 @@ __device__ __forceinline__ void update_row(const BwdArgs& a, uint32_t row_idx, i
 }
 
 // ------------------------------------------------- segmented update ------
+// Head flags of the LDS window as one 64-bit mask per 64 positions (one
+// ballot per wave-sized chunk), so the bounds of a segment are found with a
+// few bit scans instead of walking the keys.
+template <int NMASK>
+struct HeadMasks {
+    unsigned long long m[NMASK];
+};
+
+// First head strictly after window position x (x in [0, wn)); wn if none.
+template <int NMASK>
+__device__ __forceinline__ int next_head(const unsigned long long* m, int x, int wn) {
+    if (x + 1 >= wn) return wn;
+    int c = (x + 1) >> 6;
+    unsigned long long bits = (x + 1) & 63 ? (m[c] & (~0ull << ((x + 1) & 63))) : m[c];
+    while (true) {
+        if (bits) return (c << 6) + __ffsll((long long)bits) - 1;
+        if (++c >= NMASK || (c << 6) >= wn) return wn;
+        bits = m[c];
+    }
+}
+
+// Last head at or before window position x (position 0 is always a head).
+__device__ __forceinline__ int prev_head(const unsigned long long* m, int x) {
+    int c = x >> 6;
+    unsigned long long bits = m[c] & (((x & 63) == 63) ? ~0ull : ((2ull << (x & 63)) - 1));
+    while (!bits) bits = m[--c];
+    return (c << 6) + 63 - __clzll((long long)bits);
+}
+
+// One piece's lookups.  A long segment's part in the piece (at the start,
+// continuing an earlier piece, or at the end, continuing past it) is summed
+// as a plain run, 8 gradient rows in flight, into a carry slot.  The short
+// segments in between are walked CH lookups at a time: the CH gradient rows
+// and the rows (weights + state) of every segment starting among them are
+// loaded together, then consumed in order, and a segment is finished
+// (optimizer applied) at its last lookup, which may lie past the piece end.
+template <int D, bool BF16, int OPT, int NMASK>
+__device__ __forceinline__ void walk_piece(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
+                                           const unsigned long long* s_head, const uint64_t* s_chunks, int wn,
+                                           int64_t w0, int64_t k, int x0, int xb, int li, uint32_t& finished) {
+    constexpr int VEC = Geo<D, BF16>::VEC;
+    constexpr int CH = 4;
+    auto is_head = [&](int q) -> bool { return (s_head[q >> 6] >> (q & 63)) & 1ull; };
+    auto carry = [&](int slot, const double* acc) {
+        double* dst = a.carry + ((int64_t)k * 2 + slot) * D + li * VEC;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) dst[c] = acc[c];
+    };
+    // lookups without a row sort last: stop at the head of that run
+    int lim = xb;
+    if (s_keys[xb - 1] == a.invalid) lim = prev_head(s_head, xb - 1);
+    if (lim <= x0) return;
+    int p = x0;
+    if (!is_head(p)) {
+        const int h = prev_head(s_head, p);
+        const int e = next_head<NMASK>(s_head, p, wn);
+        if (e - h > LONG_T) {
+            const int e2 = e < lim ? e : lim;
+            double acc[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+            sum_range<D, BF16>(a, s_vals, p, e2, li, acc);
+            carry(0, acc);
+            p = e2;
+        } else {
+            p = e;                   // short: finished by the piece holding its head
+        }
+    }
+    if (p >= lim) return;
+    // the last segment starting in the piece: long (summed into slot 1) or
+    // short (the walk runs to its end)
+    const int hl = prev_head(s_head, lim - 1);
+    const int el = next_head<NMASK>(s_head, hl, wn);
+    const bool tail_long = el - hl > LONG_T;
+    const int qend = tail_long ? hl : el;
+    double acc[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+    RowRegs<D, BF16> cur;
+    char* cur_row = nullptr;
+    int cur_end = p;
+    for (int q = p; q < qend; q += CH) {
+        float gv[CH][VEC];
+        uint32_t j[CH];
+        bool hd[CH];
+        RowRegs<D, BF16> rr[CH];
+        char* rp[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int qq = q + u < qend ? q + u : qend - 1;
+            j[u] = s_vals[qq];
+            hd[u] = q + u < qend && is_head(q + u);
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            rp[u] = nullptr;
+            if (hd[u]) {
+                rp[u] = a.rv.row(s_chunks, s_keys[q + u]);
+                load_row<D, BF16, OPT>(rp[u], li, rr[u]);
+            }
+        }
+        double len[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int x = q + u;
+            if (x < qend) {
+                if (hd[u]) {
+                    cur_end = next_head<NMASK>(s_head, x, wn);
+                    cur = rr[u];
+                    cur_row = rp[u];
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+                }
+                add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+                if (x + 1 == cur_end) {
+                    finish_row<D, BF16, OPT>(a, cur_row, li, cur, acc);
+                    ++finished;
+                }
+            }
+        }
+    }
+    if (tail_long) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+        sum_range<D, BF16>(a, s_vals, hl, xb, li, acc);
+        carry(1, acc);
+        if (li == 0) {
+            const unsigned long long pos = atomicAdd(&a.ctr->n_owners, 1ull);
+            a.owners[pos] = (uint32_t)(w0 + hl);
+        }
+    }
+}
+
 template <int D, bool BF16, int OPT>
 __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a) {
     using G = Geo<D, BF16>;
-    constexpr int VEC = G::VEC, LPR = G::LPR, GPB = G::GPB, WIN = G::WIN;
+    constexpr int LPR = G::LPR, GPB = G::GPB, WIN = G::WIN;
+    constexpr int NMASK = (WIN + 63) / 64;
     __shared__ uint32_t s_keys[WIN];
     __shared__ uint32_t s_vals[WIN];
+    __shared__ unsigned long long s_head[NMASK];
+    __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    __shared__ uint32_t s_done;
+    stage_chunks(s_chunks, a.rv);
+    if (threadIdx.x == 0) s_done = 0;
     if (a.ctr->bad) return;
-    const int64_t n_valid = (int64_t)a.ctr->n_valid;
-    const int64_t n_pieces = (n_valid + P - 1) / P;
+    const int64_t n = a.n;
+    const int64_t n_pieces = (n + P - 1) / P;
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
-    unsigned long long finished = 0;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / WAVE;
+    uint32_t finished = 0;
 
     for (int64_t pb = (int64_t)blockIdx.x * GPB; pb < n_pieces; pb += (int64_t)gridDim.x * GPB) {
         const int64_t blk_a = pb * P;
-        const int64_t blk_b = (pb + GPB) * P < n_valid ? (pb + GPB) * P : n_valid;
+        const int64_t blk_b = (pb + GPB) * P < n ? (pb + GPB) * P : n;
         const int64_t w0 = blk_a - HALO > 0 ? blk_a - HALO : 0;
-        const int64_t w1 = blk_b + HALO < n_valid ? blk_b + HALO : n_valid;
+        const int64_t w1 = blk_b + HALO < n ? blk_b + HALO : n;
+        const int wn = (int)(w1 - w0);
         __syncthreads();
-        for (int64_t q = w0 + threadIdx.x; q < w1; q += G::BLOCK) {
-            s_keys[q - w0] = a.keys[q];
-            s_vals[q - w0] = a.vals[q];
+        for (int q = threadIdx.x; q < wn; q += G::BLOCK) {
+            s_keys[q] = a.keys[w0 + q];
+            s_vals[q] = a.vals[w0 + q];
+        }
+        __syncthreads();
+        // window position 0 counts as a head: a segment reaching back to it
+        // is at least HALO long, i.e. long either way
+        for (int c = wave; c < NMASK; c += G::BLOCK / WAVE) {
+            const int q = c * 64 + lane;
+            const bool h = q < wn && (q == 0 || s_keys[q] != s_keys[q - 1]);
+            const unsigned long long m = __ballot(h);
+            if (lane == 0) s_head[c] = m;
         }
         __syncthreads();
         const int64_t k = pb + g;
         if (k >= n_pieces) continue;
-        const int64_t a0 = k * P;
-        const int64_t b0 = a0 + P < n_valid ? a0 + P : n_valid;
-        auto K = [&](int64_t q) -> uint32_t { return s_keys[q - w0]; };
-        // same-key run around q, counted up to HALO each way (within the window)
-        auto fwd_run = [&](int64_t q, uint32_t key) -> int64_t {
-            int64_t e = q;
-            const int64_t lim = (q + HALO < w1) ? q + HALO : w1;
-            while (e < lim && K(e) == key) ++e;
-            return e - q;              // >= HALO means "long" (or window end)
-        };
-        auto bwd_run = [&](int64_t q, uint32_t key) -> int64_t {
-            int64_t h = q;
-            const int64_t lim = (q - HALO > w0) ? q - HALO : w0;
-            while (h > lim && K(h - 1) == key) --h;
-            return q - h;
-        };
-        int64_t p = a0;
-        if (p > 0 && K(p) == K(p - 1)) {
-            // segment started in an earlier piece
-            const uint32_t key = K(p);
-            const int64_t nb = bwd_run(p, key);
-            const int64_t nf = fwd_run(p, key);
-            const bool at_end = p + nf == n_valid;   // window end is the data end
-            const bool is_long = nb + nf > LONG_T || (!at_end && p + nf == w1);
-            if (is_long) {
-                int64_t e = p;
-                while (e < b0 && K(e) == key) ++e;
-                double acc[VEC];
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-                sum_range<D, BF16>(a, s_vals, w0, p, e, li, acc);
-                double* dst = a.carry + ((int64_t)k * 2 + 0) * D + li * VEC;
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) dst[c] = acc[c];
-                p = e;
-            } else {
-                p += nf;
-            }
-        }
-        while (p < b0) {
-            const uint32_t key = K(p);
-            const int64_t nf = fwd_run(p, key);
-            const bool at_end = p + nf == n_valid;
-            const bool is_long = nf > LONG_T || (!at_end && p + nf == w1);
-            double acc[VEC];
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-            if (!is_long) {
-                sum_range<D, BF16>(a, s_vals, w0, p, p + nf, li, acc);
-                update_row<D, BF16, OPT>(a, key, li, acc);
-                ++finished;
-                p += nf;
-            } else {
-                sum_range<D, BF16>(a, s_vals, w0, p, b0, li, acc);
-                double* dst = a.carry + ((int64_t)k * 2 + 1) * D + li * VEC;
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) dst[c] = acc[c];
-                if (li == 0) {
-                    const unsigned long long pos = atomicAdd(&a.ctr->n_owners, 1ull);
-                    a.owners[pos] = (uint32_t)p;
-                }
-                p = b0;
-            }
-        }
+        const int x0 = (int)(k * P - w0);
+        const int xb = (int)((k * P + P < n ? k * P + P : n) - w0);
+        walk_piece<D, BF16, OPT, NMASK>(a, s_keys, s_vals, s_head, s_chunks, wn, w0, k, x0, xb, li, finished);
     }
-    if (li == 0 && finished) atomicAdd(a.n_unique, finished);
+    // rows finished by this block (one LDS add per group), no global atomics
+    if (li == 0 && finished) atomicAdd(&s_done, finished);
+    __syncthreads();
+    if (threadIdx.x == 0) a.blk_unique[blockIdx.x] = s_done;
 }
 
 // ------------------------------------------------- long segment combine --
 // One block per owner (grid-stride): partials of the pieces the segment
-// covers, added round-robin per group then in group order.
+// covers, added round-robin per group then in group order.  Block 0 also
+// totals the distinct rows.
 template <int D, bool BF16, int OPT>
 __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_combine(BwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GPB = G::GPB;
     __shared__ double s_part[GPB][D];
     __shared__ int64_t s_end;
+    __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    __shared__ unsigned long long s_sum[G::BLOCK / WAVE];
+    stage_chunks(s_chunks, a.rv);
     if (a.ctr->bad) return;
-    const int64_t n_valid = (int64_t)a.ctr->n_valid;
     const int64_t n_owners = (int64_t)a.ctr->n_owners;
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
+    if (blockIdx.x == 0) {
+        unsigned long long c = 0;
+        for (int b = threadIdx.x; b < a.n_seg_blocks; b += G::BLOCK) c += a.blk_unique[b];
+        for (int o = WAVE / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, WAVE);
+        if (lane_id() == 0) s_sum[threadIdx.x / WAVE] = c;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long t = (unsigned long long)n_owners;
+            for (int w = 0; w < G::BLOCK / WAVE; ++w) t += s_sum[w];
+            *a.n_unique = (int64_t)t;
+        }
+    }
     for (int64_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
         const int64_t h = a.owners[o];
         const uint32_t key = a.keys[h];
         __syncthreads();
         if (threadIdx.x == 0) {
             // end of the run: first position after h with a different key
-            int64_t lo = h, hi = n_valid;   // keys[lo] == key; keys[hi] != key (or end)
+            int64_t lo = h, hi = a.n;   // keys[lo] == key; keys[hi] != key (or end)
             while (hi - lo > 1) {
                 const int64_t mid = lo + (hi - lo) / 2;
                 if (a.keys[mid] == key) lo = mid;
@@ -393,11 +531,14 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_combine(BwdArgs a) {
             double tot[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; ++c) tot[c] = s_part[0][li * VEC + c];
+#pragma unroll 1
             for (int q = 1; q < GPB; ++q)
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) tot[c] += s_part[q][li * VEC + c];
-            update_row<D, BF16, OPT>(a, key, li, tot);
-            if (li == 0) atomicAdd(a.n_unique, 1ull);
+            char* row = a.rv.row(s_chunks, key);
+            RowRegs<D, BF16> rr;
+            load_row<D, BF16, OPT>(row, li, rr);
+            finish_row<D, BF16, OPT>(a, row, li, rr, tot);
         }
     }
 }
@@ -411,6 +552,7 @@ struct BwdWs {
     uint32_t* v1;
     double* carry;
     uint32_t* owners;
+    uint32_t* blk_unique;
     void* sort_ws;
 };
 
@@ -426,19 +568,27 @@ BwdWs carve(void* base, int64_t n_ids, int32_t dim, size_t* total) {
     w.v1 = c.take<uint32_t>(n);
     w.carry = c.take<double>(n_pieces * 2 * (size_t)dim);
     w.owners = c.take<uint32_t>(n_pieces);
+    w.blk_unique = c.take<uint32_t>(MAX_SEG_BLOCKS);
     w.sort_ws = c.take<char>(sort_workspace((int64_t)n, nullptr));
     if (total) *total = c.size();
     return w;
 }
 
 template <int D, bool BF16, int OPT>
-int launch_update(const BwdArgs& a, int64_t n_ids, hipStream_t s) {
+int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     using G = Geo<D, BF16>;
     const int64_t n_pieces = (n_ids + P - 1) / P;
-    const int blocks = fill_blocks(n_pieces, G::GPB, 65535);
-    hipLaunchKernelGGL((k_seg_update<D, BF16, OPT>), dim3(blocks), dim3(G::BLOCK), 0, s, a);
+    const int blocks = fill_blocks(n_pieces, G::GPB, MAX_SEG_BLOCKS);
+    a.n_seg_blocks = blocks;
+    {
+        TraceScope ts(RSE_K_SEG_UPDATE, s);
+        hipLaunchKernelGGL((k_seg_update<D, BF16, OPT>), dim3(blocks), dim3(G::BLOCK), 0, s, a);
+    }
     const int cblocks = fill_blocks(n_pieces, 1, 2048);
-    hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(G::BLOCK), 0, s, a);
+    {
+        TraceScope ts(RSE_K_COMBINE, s);
+        hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(G::BLOCK), 0, s, a);
+    }
     return launch_status();
 }
 
@@ -500,9 +650,8 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     BwdWs w = carve(d_ws, n_ids, blocks->dim, &need);
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
-    unsigned long long* n_unique = reinterpret_cast<unsigned long long*>(d_n_unique_out);
     uint32_t* totals = sort_totals(w.sort_ws, n_ids > 0 ? n_ids : 1);
-    hipLaunchKernelGGL(k_bwd_reset, dim3(1), dim3(256), 0, s, w.ctr, totals, SORT_MAX_PASSES * 256, n_unique);
+    hipLaunchKernelGGL(k_bwd_reset, dim3(1), dim3(256), 0, s, w.ctr, totals, SORT_MAX_PASSES * 256, d_n_unique_out);
     if (n_ids == 0 || n_bags == 0) return launch_status();
 
     const int64_t capacity = blocks->capacity();
@@ -510,7 +659,7 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     if (bits < 1) bits = 1;
     const uint32_t invalid = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
     hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, 256, 8192)), dim3(256), 0, s, d_row_off,
-                       d_bag_offsets, n_bags, n_ids, capacity, invalid, w.k0, w.v0, w.ctr,
+                       d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
                        &blocks->header()->status);
     bool alt = false;
     int rc = radix_sort_pairs(w.k0, w.v0, w.k1, w.v1, n_ids, bits, w.sort_ws, &alt, s);
@@ -525,10 +674,14 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     a.batch = batch;
     a.n_tables = n_tables;
     a.mean = pooling == RSE_MEAN;
+    a.n = n_ids;
+    a.invalid = invalid;
+    a.n_seg_blocks = 0;
     a.ctr = w.ctr;
     a.carry = w.carry;
     a.owners = w.owners;
-    a.n_unique = n_unique;
+    a.blk_unique = w.blk_unique;
+    a.n_unique = d_n_unique_out;
     a.op.lr = opt->lr;
     a.op.eps = opt->eps;
     a.op.b1 = opt->beta1;

@@ -54,18 +54,36 @@ struct BlocksHeader {
 };
 static_assert(sizeof(BlocksHeader) == 256, "BlocksHeader size");
 
-// Everything a kernel needs to address rows (passed by value).
+// Everything a kernel needs to address rows (passed by value).  Kernels on
+// the hot path stage the chunk-pointer table in LDS (stage_chunks) so that a
+// row address costs an LDS read instead of a dependent global load.
+constexpr int LDS_CHUNKS = 512;
+
 struct RowsView {
     const uint64_t* chunks;   // device chunk-pointer table
     int64_t row_bytes;
     int32_t shift;            // log2(rows per chunk)
-    int32_t pad;
+    int32_t n_chunks;
     uint64_t mask;            // rows per chunk - 1
     __device__ __forceinline__ char* row(int64_t r) const {
         const uint64_t base = chunks[(uint64_t)r >> shift];
         return reinterpret_cast<char*>(base + ((uint64_t)r & mask) * (uint64_t)row_bytes);
     }
+    __device__ __forceinline__ bool lds_ok() const { return n_chunks <= LDS_CHUNKS; }
+    // s: the LDS copy made by stage_chunks
+    __device__ __forceinline__ char* row(const uint64_t* s, int64_t r) const {
+        const uint64_t c = (uint64_t)r >> shift;
+        const uint64_t base = lds_ok() ? s[c] : chunks[c];
+        return reinterpret_cast<char*>(base + ((uint64_t)r & mask) * (uint64_t)row_bytes);
+    }
 };
+
+// All threads of the block must call this (it synchronises the block).
+__device__ __forceinline__ void stage_chunks(uint64_t* s, const RowsView& rv) {
+    const int n = rv.n_chunks < LDS_CHUNKS ? rv.n_chunks : LDS_CHUNKS;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) s[i] = rv.chunks[i];
+    __syncthreads();
+}
 
 // ------------------------------------------------------------ hashing ----
 // Bucket hash: MurmurHash3's 64-bit finaliser (Appleby), salted per table.

@@ -50,14 +50,20 @@ __device__ __forceinline__ void widen_add(double* acc, const uint4& q) {
     }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Pooled rows are written once and not read again by this kernel: stream
+// them past the caches so hot embedding rows stay resident.
 template <int VEC>
 __device__ __forceinline__ void store_out(float* dst, const double* acc, double scale, bool mean) {
     float f[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) f[k] = (float)(mean ? acc[k] / scale : acc[k]);
 #pragma unroll
-    for (int k = 0; k < VEC; k += 4)
-        *reinterpret_cast<float4*>(dst + k) = make_float4(f[k], f[k + 1], f[k + 2], f[k + 3]);
+    for (int k = 0; k < VEC; k += 4) {
+        const f32x4 v = {f[k], f[k + 1], f[k + 2], f[k + 3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + k));
+    }
 }
 
 struct FwdArgs {
@@ -81,18 +87,129 @@ __device__ __forceinline__ void flag_bad(const FwdArgs& a) {
     atomicCAS(a.status, 0, (int32_t)RSE_ERR_BAD_INPUT);
 }
 
-// ----------------------------------------------------- group per bags ----
-template <int D, bool BF16, int BPG, int UNROLL>
-__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
+// Row loads are issued unconditionally (a missing or rejected row reads a
+// dummy row and is masked out of the sum), so all UNROLL loads of a group
+// are in flight together instead of being serialised behind branches.
+__device__ __forceinline__ const char* dummy_row(const uint64_t* s_chunks, const RowsView& rv) {
+    return reinterpret_cast<const char*>(rv.lds_ok() ? s_chunks[0] : rv.chunks[0]);
+}
+
+// ---------------------------------------------------- one-hot bags ------
+// A group owns BPG consecutive bags; the first row of every bag is loaded
+// at once (BPG loads in flight), further rows of a bag (rare) in order.
+template <int D, bool BF16, int BPG>
+__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    stage_chunks(s_chunks, a.rv);
     const int lane = lane_id();
     const int g = lane / LPR;
     const int li = lane % LPR;
     const int64_t gid = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE * GROUPS + g;
     const int64_t n_groups = (int64_t)gridDim.x * (FWD_BLOCK / WAVE) * GROUPS;
-    const int64_t W_BYTES = (int64_t)D * (BF16 ? 2 : 4);
-    (void)W_BYTES;
+    const bool can_load = a.capacity > 0 && a.n_ids > 0;
+    const char* dummy = can_load ? dummy_row(s_chunks, a.rv) : nullptr;
+
+    for (int64_t jb = gid * BPG; jb < a.n_bags; jb += n_groups * BPG) {
+        const int nb = (int)(a.n_bags - jb < BPG ? a.n_bags - jb : BPG);
+        int64_t off[BPG + 1];
+        int64_t spec[BPG];
+#pragma unroll
+        for (int k = 0; k <= BPG; ++k) off[k] = a.bag_off[jb + (k < nb ? k : nb)];
+        // one-hot layouts have bag j's lookup at index j: load that row
+        // offset in parallel with the bag offsets (used if the guess holds)
+        if (can_load) {
+#pragma unroll
+            for (int k = 0; k < BPG; ++k) spec[k] = a.row_off[jb + k < a.n_ids ? jb + k : a.n_ids - 1];
+        }
+        bool ok = off[0] >= 0 && off[BPG] <= a.n_ids;   // off[BPG] == off[nb] (clamped loads)
+#pragma unroll
+        for (int k = 0; k < BPG; ++k) ok = ok && off[k + 1] >= off[k];
+        if (!ok) {
+            if (li == 0) flag_bad(a);
+            continue;
+        }
+        int64_t r[BPG];
+        bool v[BPG];
+        uint4 q[BPG];
+#pragma unroll
+        for (int k = 0; k < BPG; ++k) {
+            const bool has = k < nb && off[k + 1] > off[k];
+            r[k] = !can_load ? -1 : (off[k] == jb + k ? spec[k] : a.row_off[has ? off[k] : 0]);
+            v[k] = has && r[k] >= 0 && r[k] < a.capacity;
+            if (has && r[k] >= a.capacity && li == 0) flag_bad(a);
+        }
+        if (can_load) {
+#pragma unroll
+            for (int k = 0; k < BPG; ++k)
+                q[k] = *reinterpret_cast<const uint4*>((v[k] ? a.rv.row(s_chunks, r[k]) : dummy) + li * 16);
+        }
+        const uint32_t t0 = (uint32_t)((uint64_t)jb / (uint64_t)a.batch);
+        const uint32_t b0 = (uint32_t)(jb - (int64_t)t0 * a.batch);
+        // bags of at most one lookup are finished from the prefetched rows;
+        // longer bags (rare here) are summed afresh below, in order
+        bool multi = false;
+        uint32_t t = t0, b = b0;
+#pragma unroll
+        for (int k = 0; k < BPG; ++k) {
+            const int64_t len = off[k + 1] - off[k];
+            if (k < nb && len <= 1) {
+                double acc[VEC];
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+                if (v[k]) widen_add<BF16>(acc, q[k]);
+                store_out<VEC>(a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC, acc, 1.0, false);
+            }
+            multi = multi || (k < nb && len > 1);
+            if (++b == (uint32_t)a.batch) {
+                b = 0;
+                ++t;
+            }
+        }
+        if (multi) {
+            t = t0;
+            b = b0;
+            for (int k = 0; k < nb; ++k) {
+                const int64_t s0 = a.bag_off[jb + k], e0 = a.bag_off[jb + k + 1];
+                if (e0 - s0 > 1) {
+                    double acc[VEC];
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+                    for (int64_t i = s0; i < e0; ++i) {
+                        const int64_t rr = a.row_off[i];
+                        if (rr >= a.capacity) {
+                            if (li == 0) flag_bad(a);
+                        } else if (rr >= 0) {
+                            widen_add<BF16>(acc, *reinterpret_cast<const uint4*>(a.rv.row(s_chunks, rr) + li * 16));
+                        }
+                    }
+                    store_out<VEC>(a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC, acc, (double)(e0 - s0),
+                                   a.mean);
+                }
+                if (++b == (uint32_t)a.batch) {
+                    b = 0;
+                    ++t;
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------- group per bags ----
+template <int D, bool BF16, int BPG, int UNROLL>
+__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
+    using G = Geo<D, BF16>;
+    constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    stage_chunks(s_chunks, a.rv);
+    const int lane = lane_id();
+    const int g = lane / LPR;
+    const int li = lane % LPR;
+    const int64_t gid = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE * GROUPS + g;
+    const int64_t n_groups = (int64_t)gridDim.x * (FWD_BLOCK / WAVE) * GROUPS;
+    const bool can_load = a.capacity > 0;
+    const char* dummy = can_load ? dummy_row(s_chunks, a.rv) : nullptr;
 
     for (int64_t jb = gid * BPG; jb < a.n_bags; jb += n_groups * BPG) {
         const int64_t je = jb + BPG < a.n_bags ? jb + BPG : a.n_bags;
@@ -114,51 +231,54 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
         int64_t bag_start = a.bag_off[jb];
         int64_t bag_end = a.bag_off[jb + 1];
         const int64_t last = a.bag_off[je];
+        uint32_t t = (uint32_t)((uint64_t)jb / (uint64_t)a.batch);
+        uint32_t b = (uint32_t)(jb - (int64_t)t * a.batch);
         double acc[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
 
-        auto close_bag = [&](int64_t jj, int64_t len) {
-            const int64_t t = jj / a.batch;
-            const int64_t b = jj - t * a.batch;
-            float* dst = a.out + (b * a.n_tables + t) * D + li * VEC;
+        auto close_bag = [&](int64_t len) {
+            float* dst = a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC;
             store_out<VEC>(dst, acc, (double)len, a.mean && len > 0);
 #pragma unroll
             for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
+            if (++b == (uint32_t)a.batch) {
+                b = 0;
+                ++t;
+            }
         };
 
         for (int64_t i = bag_start; i < last; i += UNROLL) {
             int64_t r[UNROLL];
+            bool v[UNROLL];
             uint4 q[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                r[u] = (i + u < last) ? a.row_off[i + u] : -1;
-                if (r[u] >= a.capacity) {
-                    if (li == 0) flag_bad(a);
-                    r[u] = -1;
-                }
+                r[u] = a.row_off[i + u < last ? i + u : last - 1];
+                v[u] = i + u < last && r[u] >= 0 && r[u] < a.capacity;
+                if (i + u < last && r[u] >= a.capacity && li == 0) flag_bad(a);
             }
+            if (can_load) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                if (r[u] >= 0) q[u] = *reinterpret_cast<const uint4*>(a.rv.row(r[u]) + li * 16);
-                else q[u] = make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < UNROLL; ++u)
+                    q[u] = *reinterpret_cast<const uint4*>((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int64_t ii = i + u;
                 if (ii >= last) break;
                 while (ii >= bag_end) {      // close finished (possibly empty) bags
-                    close_bag(j, bag_end - bag_start);
+                    close_bag(bag_end - bag_start);
                     ++j;
                     bag_start = bag_end;
                     bag_end = a.bag_off[j + 1];
                 }
-                if (r[u] >= 0) widen_add<BF16>(acc, q[u]);
+                if (v[u]) widen_add<BF16>(acc, q[u]);
             }
         }
         // close the remaining bags of the run (including trailing empty ones)
         while (j < je) {
-            close_bag(j, bag_end - bag_start);
+            close_bag(bag_end - bag_start);
             ++j;
             if (j < je) {
                 bag_start = bag_end;
@@ -173,11 +293,15 @@ template <int D, bool BF16, int UNROLL>
 __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    stage_chunks(s_chunks, a.rv);
     const int lane = lane_id();
     const int g = lane / LPR;
     const int li = lane % LPR;
     const int64_t wid = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE;
     const int64_t n_waves = (int64_t)gridDim.x * (FWD_BLOCK / WAVE);
+    const bool can_load = a.capacity > 0;
+    const char* dummy = can_load ? dummy_row(s_chunks, a.rv) : nullptr;
     for (int64_t j = wid; j < a.n_bags; j += n_waves) {
         const int64_t s = a.bag_off[j];
         const int64_t e = a.bag_off[j + 1];
@@ -190,24 +314,23 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
         for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
         for (int64_t i = s + g; i < e; i += (int64_t)GROUPS * UNROLL) {
             int64_t r[UNROLL];
+            bool v[UNROLL];
             uint4 q[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int64_t ii = i + (int64_t)u * GROUPS;
-                r[u] = ii < e ? a.row_off[ii] : -1;
-                if (r[u] >= a.capacity) {
-                    if (li == 0) flag_bad(a);
-                    r[u] = -1;
-                }
+                r[u] = a.row_off[ii < e ? ii : e - 1];
+                v[u] = ii < e && r[u] >= 0 && r[u] < a.capacity;
+                if (ii < e && r[u] >= a.capacity && li == 0) flag_bad(a);
             }
+            if (can_load) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                if (r[u] >= 0) q[u] = *reinterpret_cast<const uint4*>(a.rv.row(r[u]) + li * 16);
-                else q[u] = make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < UNROLL; ++u)
+                    q[u] = *reinterpret_cast<const uint4*>((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (v[u]) widen_add<BF16>(acc, q[u]);
             }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                if (r[u] >= 0) widen_add<BF16>(acc, q[u]);
         }
         // fixed xor tree across the groups
 #pragma unroll
@@ -216,7 +339,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
             for (int k = 0; k < VEC; ++k) acc[k] += shfl_xor_f64(acc[k], m);
         }
         if (g == 0) {
-            const int64_t t = j / a.batch;
+            const int64_t t = (int64_t)((uint64_t)j / (uint64_t)a.batch);
             const int64_t b = j - t * a.batch;
             const int64_t len = e - s;
             store_out<VEC>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, (double)len,
@@ -225,17 +348,29 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
     }
 }
 
+#ifndef RSE_FWD_ONEHOT_BPG
+#define RSE_FWD_ONEHOT_BPG 8
+#endif
+
 template <int D, bool BF16>
 int launch_fwd(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
     using G = Geo<D, BF16>;
+    TraceScope ts(RSE_K_FWD, s);
     const double avg = a.n_bags > 0 ? (double)n_ids / (double)a.n_bags : 0.0;
+    constexpr int WAVES = FWD_BLOCK / WAVE;
     if (avg >= 2.0 * G::GROUPS && G::GROUPS > 1) {
-        const int blocks = fill_blocks(a.n_bags, FWD_BLOCK / WAVE, 256 * 32);
+        const int blocks = fill_blocks(a.n_bags, WAVES, 256 * 32);
         hipLaunchKernelGGL((k_fwd_wave<D, BF16, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
+    } else if (avg <= 1.5) {
+        // one-hot: a group owns BPG bags, their first rows all in flight
+        constexpr int BPG = RSE_FWD_ONEHOT_BPG;
+        const int64_t groups = (a.n_bags + BPG - 1) / BPG;
+        const int blocks = fill_blocks(groups, WAVES * G::GROUPS, 256 * 32);
+        hipLaunchKernelGGL((k_fwd_onehot<D, BF16, BPG>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
     } else {
         constexpr int BPG = 4;
         const int64_t groups = (a.n_bags + BPG - 1) / BPG;
-        const int blocks = fill_blocks(groups, (FWD_BLOCK / WAVE) * G::GROUPS, 256 * 32);
+        const int blocks = fill_blocks(groups, WAVES * G::GROUPS, 256 * 32);
         hipLaunchKernelGGL((k_fwd_groups<D, BF16, BPG, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
     }
     return launch_status();
@@ -252,6 +387,7 @@ extern "C" int embedding_bag_fwd(const rse_blocks* blocks, const int64_t* d_row_
     if (n_ids > 0 && !d_row_off) return RSE_ERR_INVALID_ARG;
     const int64_t n_bags = (int64_t)n_tables * batch;
     if (n_bags == 0) return RSE_OK;
+    if (n_bags > (int64_t)0xFFFFFFFFll) return RSE_ERR_INVALID_ARG;
     if (!d_out) return RSE_ERR_INVALID_ARG;
     FwdArgs a;
     a.rv = blocks->view();

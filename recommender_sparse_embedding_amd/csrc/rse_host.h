@@ -32,7 +32,7 @@ struct rse_blocks {
         v.chunks = chunk_table();
         v.row_bytes = row_bytes;
         v.shift = shift;
-        v.pad = 0;
+        v.n_chunks = n_chunks;
         v.mask = (1ull << shift) - 1;
         return v;
     }
@@ -73,6 +73,23 @@ inline bool dim_supported(int32_t dim, int32_t w_dtype) {
                                     dim == 256;
     return false;
 }
+
+// Kernel trace (rse_trace.hip): launch sites call trace_mark before and
+// after launching a traceable kernel; it is a no-op unless that kernel is
+// being traced.
+extern int g_trace_kernel;
+void trace_mark(int kernel, hipStream_t s, bool after);
+
+struct TraceScope {
+    int kernel;
+    hipStream_t s;
+    TraceScope(int k, hipStream_t st) : kernel(k), s(st) {
+        if (g_trace_kernel == kernel) trace_mark(kernel, s, false);
+    }
+    ~TraceScope() {
+        if (g_trace_kernel == kernel) trace_mark(kernel, s, true);
+    }
+};
 
 // Number of blocks that keeps every CU busy for a grid-stride kernel.
 inline int fill_blocks(int64_t work_items, int items_per_block, int max_blocks) {

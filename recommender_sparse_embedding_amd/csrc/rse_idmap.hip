@@ -300,9 +300,11 @@ struct MarkArgs {
 // names it.  First sights are counted per region for the load check.
 __global__ void k_mark(MarkArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    __shared__ uint32_t s_new[RSE_MAX_TABLES];   // per-region first sights of this block
     const unsigned long long n_miss = a.ws.ctr[0];
     if (n_miss == 0) return;
     for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) s_new[r] = 0;
     __syncthreads();
     for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
          q += (unsigned long long)gridDim.x * blockDim.x) {
@@ -319,9 +321,12 @@ __global__ void k_mark(MarkArgs a) {
         }
         if (v == PENDING_BASE + (uint64_t)i) {
             a.ws.flag[i] = 2;
-            atomicAdd((unsigned long long*)&a.dir[region].new_keys, 1ull);
+            atomicAdd(&s_new[region], 1u);
         }
     }
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x)
+        if (s_new[r]) atomicAdd((unsigned long long*)&a.dir[r].new_keys, (unsigned long long)s_new[r]);
 }
 
 // ---------------------------------------------------------------- scan ---
@@ -762,7 +767,10 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     pa.ws = ws;
     // 8 lookups per wave per iteration; enough waves to fill 256 CUs
     const int probe_blocks = fill_blocks((n_ids + 7) / 8, PROBE_BLOCK / 64, 256 * 16);
-    hipLaunchKernelGGL(k_probe, dim3(probe_blocks), dim3(PROBE_BLOCK), 0, s, pa);
+    {
+        TraceScope ts(RSE_K_PROBE, s);
+        hipLaunchKernelGGL(k_probe, dim3(probe_blocks), dim3(PROBE_BLOCK), 0, s, pa);
+    }
 
     const int miss_blocks = fill_blocks(n_ids, 256, 2048);
     MarkArgs ma;

@@ -175,8 +175,11 @@ int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int
             hipLaunchKernelGGL(k_count, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, n, shift, nbits,
                                hist, n_tiles, tot);
             hipLaunchKernelGGL(k_offsets, dim3(256), dim3(SB), 0, s, hist, n_tiles, tot);
-            hipLaunchKernelGGL(k_scatter, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, vi, ko, vo, n,
-                               shift, nbits, hist, n_tiles);
+            {
+                TraceScope ts(RSE_K_SORT_SCATTER, s);
+                hipLaunchKernelGGL(k_scatter, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, vi, ko, vo, n,
+                                   shift, nbits, hist, n_tiles);
+            }
             alt = !alt;
         }
     }
