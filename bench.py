@@ -235,7 +235,7 @@ def main():
 
 
 # identifies the kernel source the stored traffic counters were taken on
-KERNEL_REV = "seg-v3"
+KERNEL_REV = "seg-v4"
 
 
 def read_traffic(name, rev):

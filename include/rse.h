@@ -79,6 +79,7 @@ enum {
 #define RSE_MAX_TABLES 1024
 #define RSE_MAX_MERGED_TABLES 128           /* table id must fit in 7 bits */
 #define RSE_MAX_ROWS 4294967294LL            /* row offsets fit in 32 bits */
+#define RSE_MAX_BWD_IDS 1073741823LL         /* lookups per backward call (2^30 - 1) */
 
 enum { RSE_F32 = 0, RSE_BF16 = 1 };               /* weight storage type */
 enum { RSE_SGD = 0, RSE_ADAGRAD = 1, RSE_ADAM = 2 };
@@ -265,6 +266,10 @@ int rse_bwd_workspace_size(int64_t n_ids, int32_t n_tables, int64_t batch, int32
  * (Adam is the lazy form of Kingma & Ba 2015, Algorithm 1).  bf16 weights
  * round to nearest even.  Rows not in the batch are not read or written.
  * The number of distinct touched rows is written to *d_n_unique_out.
+ * n_ids may not exceed RSE_MAX_BWD_IDS.  The device sort waits on results of
+ * other workgroups with a bounded spin; should a wait time out, nothing is
+ * updated, *d_n_unique_out stays 0 and the blocks' sticky status becomes
+ * RSE_ERR_HIP.
  */
 int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
                              const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,

@@ -64,6 +64,8 @@ struct BwdArgs {
     uint32_t* owners;            // head positions of long segments
     uint32_t* blk_unique;        // rows finished per segmented-update block
     int64_t* n_unique;
+    const uint32_t* sort_err;    // set if a radix pass timed out: nothing is updated
+    int32_t* status;             // the blocks' sticky status
     OptParams op;
 };
 
@@ -77,22 +79,35 @@ struct Geo {
 };
 
 // ------------------------------------------------------------- pairs -----
-__global__ void k_bwd_reset(Ctr* ctr, uint32_t* totals, int n_totals, int64_t* n_unique) {
+__global__ void k_bwd_reset(Ctr* ctr, SortPrep sp, int64_t* n_unique) {
     if (threadIdx.x == 0) {
         ctr->n_owners = 0;
         ctr->bad = 0;
         *n_unique = 0;
+        *sp.error = 0;
     }
-    for (int k = threadIdx.x; k < n_totals; k += blockDim.x) totals[k] = 0;
+    if (threadIdx.x < SORT_MAX_PASSES) sp.tile_ctr[threadIdx.x] = 0;
+    for (int k = threadIdx.x; k < SORT_MAX_PASSES * SORT_MAX_BINS; k += blockDim.x) sp.totals[k] = 0;
 }
 
 // One thread per bag: key = row (or `invalid`), value = bag.  Malformed bag
 // offsets or rows beyond the capacity mark the call bad (nothing is updated).
 // The value is the lookup's gradient row b * n_tables + t (the layout of
-// grad), so the reduction reads gradients without any division.
-__global__ void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t n_bags, int64_t n_ids,
-                        int64_t batch, int32_t n_tables, int64_t capacity, uint32_t invalid, uint32_t* keys,
-                        uint32_t* vals, Ctr* ctr, int32_t* status) {
+// grad), so the reduction reads gradients without any division.  The kernel
+// also builds the radix sort's digit histograms of every pass (block-local in
+// LDS, then added to the totals) and clears the sort's look-back state; on bad
+// input it raises the sort's error flag so that no pass runs (unwritten keys
+// would not match the totals).
+__global__ __launch_bounds__(256) void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t n_bags,
+                                               int64_t n_ids, int64_t batch, int32_t n_tables, int64_t capacity,
+                                               uint32_t invalid, uint32_t* keys, uint32_t* vals, Ctr* ctr,
+                                               int32_t* status, SortPrep sp, int passes, int width) {
+    __shared__ uint32_t s_hist[SORT_MAX_PASSES * SORT_MAX_BINS];
+    for (int q = threadIdx.x; q < SORT_MAX_PASSES * SORT_MAX_BINS; q += blockDim.x) s_hist[q] = 0;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < sp.state_words;
+         q += (int64_t)gridDim.x * blockDim.x)
+        sp.state[q] = 0;
+    __syncthreads();
     bool bad = false;
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_bags;
          j += (int64_t)gridDim.x * blockDim.x) {
@@ -112,12 +127,17 @@ __global__ void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t 
             }
             keys[i] = k;
             vals[i] = gr;
+            sort_hist_add(s_hist, k, passes, width);
         }
     }
     if (bad) {
         ctr->bad = 1;
+        atomicExch(sp.error, 2u);
         atomicCAS(status, 0, (int32_t)RSE_ERR_BAD_INPUT);
     }
+    __syncthreads();
+    for (int q = threadIdx.x; q < passes * SORT_MAX_BINS; q += blockDim.x)
+        if (s_hist[q]) atomicAdd(&sp.totals[q], s_hist[q]);
 }
 
 // ------------------------------------------------------ grad gather ------
@@ -428,6 +448,10 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a)
     stage_chunks(s_chunks, a.rv);
     if (threadIdx.x == 0) s_done = 0;
     if (a.ctr->bad) return;
+    if (*a.sort_err) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicCAS(a.status, 0, (int32_t)RSE_ERR_HIP);
+        return;
+    }
     const int64_t n = a.n;
     const int64_t n_pieces = (n + P - 1) / P;
     const int g = threadIdx.x / LPR;
@@ -482,7 +506,7 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_combine(BwdArgs a) {
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
     __shared__ unsigned long long s_sum[G::BLOCK / WAVE];
     stage_chunks(s_chunks, a.rv);
-    if (a.ctr->bad) return;
+    if (a.ctr->bad || *a.sort_err) return;
     const int64_t n_owners = (int64_t)a.ctr->n_owners;
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
@@ -645,22 +669,25 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     if (opt->kind != blocks->optim) return RSE_ERR_INVALID_ARG;
     if (opt->kind == RSE_ADAM && opt->step < 1) return RSE_ERR_INVALID_ARG;
     const int64_t n_bags = (int64_t)n_tables * batch;
-    if (n_ids > (int64_t)0xFFFFFFFFll || n_bags > (int64_t)0xFFFFFFFFll) return RSE_ERR_INVALID_ARG;
+    if (n_ids > RSE_MAX_BWD_IDS || n_bags > (int64_t)0xFFFFFFFFll) return RSE_ERR_INVALID_ARG;
     size_t need = 0;
     BwdWs w = carve(d_ws, n_ids, blocks->dim, &need);
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
-    uint32_t* totals = sort_totals(w.sort_ws, n_ids > 0 ? n_ids : 1);
-    hipLaunchKernelGGL(k_bwd_reset, dim3(1), dim3(256), 0, s, w.ctr, totals, SORT_MAX_PASSES * 256, d_n_unique_out);
+    SortPrep sp = sort_prep(w.sort_ws, n_ids);
+    hipLaunchKernelGGL(k_bwd_reset, dim3(1), dim3(256), 0, s, w.ctr, sp, d_n_unique_out);
     if (n_ids == 0 || n_bags == 0) return launch_status();
 
     const int64_t capacity = blocks->capacity();
     int bits = bit_length((uint64_t)capacity);
     if (bits < 1) bits = 1;
     const uint32_t invalid = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
-    hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, 256, 8192)), dim3(256), 0, s, d_row_off,
-                       d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
-                       &blocks->header()->status);
+    const SortPlan plan = sort_plan(bits);
+    sp.state_words = sp.state_words / SORT_MAX_PASSES * plan.passes;   // only the passes that run
+    // grid bounded so the per-block histogram flush stays a few hundred atomics per bin
+    hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, 256, 512)), dim3(256), 0, s, d_row_off, d_bag_offsets,
+                       n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
+                       &blocks->header()->status, sp, plan.passes, plan.width);
     bool alt = false;
     int rc = radix_sort_pairs(w.k0, w.v0, w.k1, w.v1, n_ids, bits, w.sort_ws, &alt, s);
     if (rc) return rc;
@@ -682,6 +709,8 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     a.owners = w.owners;
     a.blk_unique = w.blk_unique;
     a.n_unique = d_n_unique_out;
+    a.sort_err = sp.error;
+    a.status = &blocks->header()->status;
     a.op.lr = opt->lr;
     a.op.eps = opt->eps;
     a.op.b1 = opt->beta1;

@@ -5,17 +5,46 @@
 
 namespace rse_host {
 
-constexpr int SORT_TILE = 4096;      // keys per sort block
+constexpr int SORT_TILE = 4096;      // keys per sort block (256 threads x 16)
 constexpr int SORT_MAX_PASSES = 4;   // 32-bit keys
+constexpr int SORT_MAX_BINS = 512;   // digits of up to 9 bits
 
-// Workspace bytes for sorting n pairs (hist + per-pass digit totals).
+// Digit plan for keys of `bits` bits: passes of at most 9 bits each.
+struct SortPlan {
+    int passes;
+    int width;                       // bits per digit (last pass may use fewer)
+};
+SortPlan sort_plan(int bits);
+
+// Workspace bytes for sorting n pairs.
 size_t sort_workspace(int64_t n, int64_t* n_tiles_out);
 
-// Pointer to the per-pass digit totals inside the workspace (256 * 4 per
-// pass); they must be zero before radix_sort_pairs runs.
-uint32_t* sort_totals(void* ws, int64_t n);
+// Device pointers inside the sort workspace that the pair-building kernel
+// fills before the passes: per-pass digit totals (SORT_MAX_PASSES x
+// SORT_MAX_BINS, must start at zero) and the look-back state (zeroed by the
+// pair kernel).  `error` is nonzero if a pass failed or was skipped.
+struct SortPrep {
+    uint32_t* totals;        // [SORT_MAX_PASSES][SORT_MAX_BINS]
+    uint32_t* state;         // [SORT_MAX_PASSES][n_tiles][SORT_MAX_BINS]
+    uint32_t* tile_ctr;      // [SORT_MAX_PASSES] dynamic tile counters
+    uint32_t* error;         // look-back timeout flag
+    int64_t state_words;     // words of `state` to zero
+};
+SortPrep sort_prep(void* ws, int64_t n);
 
+// Sorts (k0, v0) by the low `bits` bits, stably, ping-ponging through
+// (k1, v1); the result ends in (k1, v1) if *result_in_alt.  Requires the
+// digit totals of every pass to be in prep.totals and the rest of prep to be
+// zero (the caller's pair kernel does both).
 int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n, int bits,
                      void* ws, bool* result_in_alt, hipStream_t s);
+
+// Device helper for the pair kernel: adds key's digits of every pass to
+// block-local histograms (LDS, [SORT_MAX_PASSES][SORT_MAX_BINS]).
+__device__ __forceinline__ void sort_hist_add(uint32_t* lds_hist, uint32_t key, int passes, int width) {
+    const uint32_t mask = (1u << width) - 1u;
+    for (int p = 0; p < passes; ++p)
+        atomicAdd(&lds_hist[p * SORT_MAX_BINS + ((key >> (p * width)) & mask)], 1u);
+}
 
 }  // namespace rse_host

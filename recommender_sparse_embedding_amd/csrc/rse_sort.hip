@@ -3,17 +3,23 @@
 // duplicate gradients are merged without floating-point atomics; here by
 // sorting lookups by row and reducing each run).
 //
-// Per 8-bit digit pass, three kernels:
-//   count:   per tile (4096 keys) digit histogram -> hist[digit][tile], and the
-//            pass's global digit totals (integer atomics);
-//   offsets: one block per digit scans its row of hist and adds the digit's
-//            base (sum of the smaller digits' totals);
-//   scatter: each tile ranks its keys stably (row by row of 256 keys: a
-//            digit-match mask per wave from 8 ballots, per-wave counts in LDS,
-//            running per-digit counts), then writes every pair to
-//            offset[digit][tile] + rank.
-// Keys only use the low `bits` bits, so the number of passes is
-// ceil(bits / 8), set by the table's row capacity.
+// One kernel per digit pass (digits of up to 9 bits, so 26-bit row keys take
+// three passes); the digit histograms of every pass are computed beforehand
+// by the pair-building kernel.  Per pass, each block:
+//   1. takes the next tile (4096 pairs) from an atomic counter, so every tile
+//      it may wait on belongs to a block that is already running;
+//   2. ranks the tile's keys stably: each wave owns 1024 consecutive pairs
+//      and walks them 64 at a time, building a digit-match mask per lane from
+//      one ballot per digit bit and keeping wave-private running counts in
+//      LDS, so no block barrier is needed per row;
+//   3. publishes its per-digit counts, then looks back over the preceding
+//      tiles' published counts (decoupled look-back, Merrill & Garland 2016)
+//      to get its global offset per digit, and publishes the inclusive sums;
+//   4. reorders the tile in LDS by digit and writes it out, so consecutive
+//      lanes write consecutive addresses of each digit's run.
+// Look-back waits are bounded: on a timeout the pass raises an error flag
+// and writes nothing (the caller reports RSE_ERR_HIP) instead of hanging.  A
+// pass whose error flag is already raised when a block starts does nothing.
 #include "rse_sort.h"
 
 using namespace rse;
@@ -21,119 +27,168 @@ using namespace rse_host;
 
 namespace {
 
-constexpr int SB = 256;            // threads per sort block
-constexpr int ITEMS = SORT_TILE / SB;
+constexpr int SB = 256;                         // threads per sort block
+constexpr int ITEMS = SORT_TILE / SB;           // 16 pairs per thread
+constexpr int SWAVES = SB / WAVE;
+constexpr int PER_WAVE = SORT_TILE / SWAVES;    // 1024 consecutive pairs per wave
+constexpr uint32_t ST_AGG = 1u << 30;           // tile count published
+constexpr uint32_t ST_INC = 2u << 30;           // inclusive prefix published
+constexpr uint32_t ST_VAL = (1u << 30) - 1u;
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
-__global__ __launch_bounds__(SB) void k_count(const uint32_t* keys, int64_t n, int shift, int nbits,
-                                             uint32_t* hist, int64_t n_tiles, uint32_t* totals) {
-    __shared__ uint32_t h[256];
-    h[threadIdx.x] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
-    const uint32_t dmask = (1u << nbits) - 1;
-#pragma unroll 4
-    for (int k = 0; k < ITEMS; ++k) {
-        const int64_t i = base + k * SB + threadIdx.x;
-        if (i < n) atomicAdd(&h[(keys[i] >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    const uint32_t c = h[threadIdx.x];
-    hist[(int64_t)threadIdx.x * n_tiles + blockIdx.x] = c;
-    if (c) atomicAdd(&totals[threadIdx.x], c);
+__device__ __forceinline__ uint32_t load_state(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_state(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One block per digit: exclusive scan of hist[digit][0..n_tiles) plus base.
-__global__ __launch_bounds__(SB) void k_offsets(uint32_t* hist, int64_t n_tiles,
-                                               const uint32_t* totals) {
-    const int dg = blockIdx.x;
-    __shared__ uint32_t s_base;
-    __shared__ uint32_t wsum[SB / WAVE];
-    __shared__ uint32_t s_carry;
-    if (threadIdx.x == 0) {
-        uint32_t b = 0;
-        for (int k = 0; k < dg; ++k) b += totals[k];
-        s_base = b;
-        s_carry = 0;
+// Exclusive scan over `bins` (<= 512) values, two per thread; returns through
+// `out`; `tmp` holds SWAVES words.
+__device__ void block_scan_bins(const uint32_t* in, uint32_t* out, int bins, uint32_t* tmp) {
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
+    const int d0 = 2 * tid;
+    const uint32_t a = d0 < bins ? in[d0] : 0u;
+    const uint32_t b = d0 + 1 < bins ? in[d0 + 1] : 0u;
+    const uint32_t s = a + b;
+    uint32_t x = s;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
     }
+    if (lane == WAVE - 1) tmp[w] = x;
     __syncthreads();
-    uint32_t* row = hist + (int64_t)dg * n_tiles;
-    const int lane = lane_id();
-    const int w = threadIdx.x / WAVE;
-    for (int64_t c0 = 0; c0 < n_tiles; c0 += SB) {
-        const int64_t k = c0 + threadIdx.x;
-        const uint32_t v = k < n_tiles ? row[k] : 0;
-        uint32_t x = v;
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const uint32_t y = __shfl_up(x, o, WAVE);
-            if (lane >= o) x += y;
-        }
-        if (lane == WAVE - 1) wsum[w] = x;
-        __syncthreads();
-        uint32_t pre = 0, tot = 0;
-        for (int q = 0; q < SB / WAVE; ++q) {
-            if (q < w) pre += wsum[q];
-            tot += wsum[q];
-        }
-        const uint32_t carry = s_carry;
-        if (k < n_tiles) row[k] = s_base + carry + pre + x - v;
-        __syncthreads();
-        if (threadIdx.x == 0) s_carry = carry + tot;
-        __syncthreads();
-    }
+    uint32_t pre = 0;
+    for (int q = 0; q < w; ++q) pre += tmp[q];
+    const uint32_t ex = pre + x - s;
+    if (d0 < bins) out[d0] = ex;
+    if (d0 + 1 < bins) out[d0 + 1] = ex + a;
+    __syncthreads();
 }
 
-__global__ __launch_bounds__(SB) void k_scatter(const uint32_t* keys_in, const uint32_t* vals_in,
-                                               uint32_t* keys_out, uint32_t* vals_out, int64_t n,
-                                               int shift, int nbits, const uint32_t* offsets,
-                                               int64_t n_tiles) {
-    __shared__ uint32_t s_run[256];
-    __shared__ uint32_t s_cnt[SB / WAVE][256];
-    __shared__ uint32_t s_off[256];
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int w = tid / WAVE;
-    s_run[tid] = 0;
-    s_off[tid] = offsets[(int64_t)tid * n_tiles + blockIdx.x];
+__global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const uint32_t* vals_in,
+                                                uint32_t* keys_out, uint32_t* vals_out, int64_t n, int shift,
+                                                int width, const uint32_t* totals, uint32_t* state,
+                                                uint32_t* tile_ctr, uint32_t* error) {
+    __shared__ uint32_t s_wcnt[SWAVES][SORT_MAX_BINS];   // wave running counts -> wave prefixes
+    __shared__ uint32_t s_cnt[SORT_MAX_BINS];            // tile count per digit
+    __shared__ uint32_t s_pre[SORT_MAX_BINS];            // tile-local exclusive prefix per digit
+    __shared__ uint32_t s_base[SORT_MAX_BINS];           // global exclusive prefix of the digit
+    __shared__ uint32_t s_glob[SORT_MAX_BINS];           // output position of the digit's first pair here
+    __shared__ uint32_t s_k[SORT_TILE];
+    __shared__ uint32_t s_v[SORT_TILE];
+    __shared__ uint32_t s_tmp[SWAVES];
+    __shared__ uint32_t s_tile;
+    __shared__ uint32_t s_fail;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
+    const int bins = 1 << width;
+    const uint32_t dmask = (uint32_t)bins - 1u;
+    if (tid == 0) {
+        s_tile = atomicAdd(tile_ctr, 1u);
+        s_fail = load_state(error) != 0u;     // raised before the pass: skip it
+    }
+    for (int d = tid; d < SWAVES * SORT_MAX_BINS; d += SB) (&s_wcnt[0][0])[d] = 0;
+    __syncthreads();
+    if (s_fail) return;
+    const uint32_t tile = s_tile;
+    const int64_t base = (int64_t)tile * SORT_TILE;
+    const int64_t tile_n = n - base < SORT_TILE ? n - base : SORT_TILE;
+
+    // 1-2. stable rank within the wave's 1024 pairs
+    uint32_t key[ITEMS], val[ITEMS], wr[ITEMS];
+    const unsigned long long lt = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int q = 0; q < SB / WAVE; ++q) s_cnt[q][tid] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
-    const uint32_t dmask = (1u << nbits) - 1;
-    const unsigned long long lt_mask = (1ull << lane) - 1;
     for (int k = 0; k < ITEMS; ++k) {
-        const int64_t i = base + (int64_t)k * SB + tid;
-        const bool valid = i < n;
-        uint32_t key = 0, val = 0, dg = 0;
-        if (valid) {
-            key = keys_in[i];
-            val = vals_in[i];
-            dg = (key >> shift) & dmask;
-        }
-        unsigned long long peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (dg >> b) & 1u;
+        const int64_t i = base + (int64_t)w * PER_WAVE + k * WAVE + lane;
+        const bool v = i < n;
+        key[k] = v ? keys_in[i] : 0u;
+        val[k] = v ? vals_in[i] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int64_t i = base + (int64_t)w * PER_WAVE + k * WAVE + lane;
+        const bool v = i < n;
+        const uint32_t d = (key[k] >> shift) & dmask;
+        unsigned long long peers = __ballot(v);
+        for (int b = 0; b < width; ++b) {
+            const bool bit = (d >> b) & 1u;
             const unsigned long long m = __ballot(bit);
             peers &= bit ? m : ~m;
         }
-        const uint32_t wrank = (uint32_t)__popcll(peers & lt_mask);
-        if (valid && wrank == 0) s_cnt[w][dg] = (uint32_t)__popcll(peers);
-        __syncthreads();
-        if (valid) {
-            uint32_t r = s_run[dg] + wrank;
-            for (int q = 0; q < w; ++q) r += s_cnt[q][dg];
-            const uint32_t pos = s_off[dg] + r;
-            keys_out[pos] = key;
-            vals_out[pos] = val;
-        }
-        __syncthreads();
-        uint32_t add = 0;
+        const uint32_t r = (uint32_t)__popcll(peers & lt);
+        const uint32_t old = v ? s_wcnt[w][d] : 0u;      // every lane reads before the leader writes
+        wr[k] = old + r;
+        if (v && r == 0) s_wcnt[w][d] = old + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    // per digit: tile count, wave prefixes; publish the tile count
+    for (int d = tid; d < bins; d += SB) {
+        uint32_t c = 0;
 #pragma unroll
-        for (int q = 0; q < SB / WAVE; ++q) {
-            add += s_cnt[q][tid];
-            s_cnt[q][tid] = 0;
+        for (int q = 0; q < SWAVES; ++q) {
+            const uint32_t x = s_wcnt[q][d];
+            s_wcnt[q][d] = c;
+            c += x;
         }
-        s_run[tid] += add;
-        __syncthreads();
+        s_cnt[d] = c;
+        store_state(&state[(int64_t)tile * SORT_MAX_BINS + d], (tile == 0 ? ST_INC : ST_AGG) | c);
+    }
+    __syncthreads();
+    block_scan_bins(s_cnt, s_pre, bins, s_tmp);
+    block_scan_bins(totals, s_base, bins, s_tmp);
+    // 3. decoupled look-back per digit
+    for (int d = tid; d < bins; d += SB) {
+        uint32_t ex = 0;
+        if (tile > 0) {
+            int64_t t = (int64_t)tile - 1;
+            uint32_t spins = 0;
+            while (true) {
+                const uint32_t st = load_state(&state[t * SORT_MAX_BINS + d]);
+                if (st & ST_INC) {
+                    ex += st & ST_VAL;
+                    break;
+                }
+                if (st & ST_AGG) {
+                    ex += st & ST_VAL;
+                    --t;                        // tile 0 always publishes inclusive
+                    continue;
+                }
+                ++spins;
+                if (spins > SPIN_LIMIT || ((spins & 1023u) == 0 && load_state(error))) {
+                    s_fail = 1;
+                    atomicExch(error, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            store_state(&state[(int64_t)tile * SORT_MAX_BINS + d], ST_INC | (ex + s_cnt[d]));
+        }
+        s_glob[d] = s_base[d] + ex;
+    }
+    __syncthreads();
+    if (s_fail) return;
+    // 4. reorder in LDS by digit, then write runs out
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int64_t i = base + (int64_t)w * PER_WAVE + k * WAVE + lane;
+        if (i < n) {
+            const uint32_t d = (key[k] >> shift) & dmask;
+            const uint32_t pos = s_pre[d] + s_wcnt[w][d] + wr[k];
+            s_k[pos] = key[k];
+            s_v[pos] = val[k];
+        }
+    }
+    __syncthreads();
+    for (int x = tid; x < tile_n; x += SB) {
+        const uint32_t kk = s_k[x];
+        const uint32_t d = (kk >> shift) & dmask;
+        const uint32_t o = s_glob[d] + ((uint32_t)x - s_pre[d]);
+        if ((int64_t)o < n) {                 // always, when the totals match the keys
+            keys_out[o] = kk;
+            vals_out[o] = s_v[x];
+        } else {
+            atomicExch(error, 1u);
+        }
     }
 }
 
@@ -141,58 +196,60 @@ __global__ __launch_bounds__(SB) void k_scatter(const uint32_t* keys_in, const u
 
 namespace rse_host {
 
-size_t sort_workspace(int64_t n, int64_t* n_tiles_out) {
-    const int64_t n_tiles = (n + SORT_TILE - 1) / SORT_TILE;
-    if (n_tiles_out) *n_tiles_out = n_tiles;
-    // hist [256][n_tiles] + totals [MAX_PASSES][256]
-    return align_up((size_t)256 * (size_t)(n_tiles > 0 ? n_tiles : 1) * 4, 256) +
-           align_up((size_t)SORT_MAX_PASSES * 256 * 4, 256);
+SortPlan sort_plan(int bits) {
+    SortPlan p;
+    if (bits < 1) bits = 1;
+    p.passes = (bits + 8) / 9;
+    p.width = (bits + p.passes - 1) / p.passes;
+    return p;
 }
 
-// Sorts (k0, v0) by the low `bits` bits; ping-pongs through (k1, v1).  The
-// result ends in (k0, v0) if the number of passes is even, else in (k1, v1);
-// *result_in_alt reports which.  `totals` must be zeroed for all passes
-// beforehand (see sort_totals).
+static int64_t tiles_of(int64_t n) { return (n + SORT_TILE - 1) / SORT_TILE; }
+
+size_t sort_workspace(int64_t n, int64_t* n_tiles_out) {
+    const int64_t n_tiles = tiles_of(n > 0 ? n : 1);
+    if (n_tiles_out) *n_tiles_out = n_tiles;
+    return align_up((size_t)SORT_MAX_PASSES * SORT_MAX_BINS * 4, 256) +
+           align_up((size_t)SORT_MAX_PASSES * n_tiles * SORT_MAX_BINS * 4, 256) + 256 + 256;
+}
+
+SortPrep sort_prep(void* ws, int64_t n) {
+    const int64_t n_tiles = tiles_of(n > 0 ? n : 1);
+    Carver c(ws);
+    SortPrep p;
+    p.totals = c.take<uint32_t>((size_t)SORT_MAX_PASSES * SORT_MAX_BINS);
+    p.state = c.take<uint32_t>((size_t)SORT_MAX_PASSES * n_tiles * SORT_MAX_BINS);
+    p.tile_ctr = c.take<uint32_t>(SORT_MAX_PASSES);
+    p.error = c.take<uint32_t>(1);
+    p.state_words = (int64_t)SORT_MAX_PASSES * n_tiles * SORT_MAX_BINS;
+    return p;
+}
+
 int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n, int bits,
                      void* ws, bool* result_in_alt, hipStream_t s) {
-    int64_t n_tiles = 0;
-    sort_workspace(n, &n_tiles);
-    Carver c(ws);
-    uint32_t* hist = c.take<uint32_t>((size_t)256 * (size_t)(n_tiles > 0 ? n_tiles : 1));
-    uint32_t* totals = c.take<uint32_t>((size_t)SORT_MAX_PASSES * 256);
-    const int passes = (bits + 7) / 8;
-    if (passes > SORT_MAX_PASSES) return RSE_ERR_UNSUPPORTED;
+    const SortPlan plan = sort_plan(bits);
+    if (plan.passes > SORT_MAX_PASSES) return RSE_ERR_UNSUPPORTED;
+    if (n >= (int64_t)ST_VAL) return RSE_ERR_UNSUPPORTED;
+    const int64_t n_tiles = tiles_of(n);
+    SortPrep p = sort_prep(ws, n);
     bool alt = false;
     if (n > 0) {
-        for (int p = 0; p < passes; ++p) {
-            const int shift = 8 * p;
-            const int nbits = bits - shift < 8 ? bits - shift : 8;
+        for (int ps = 0; ps < plan.passes; ++ps) {
+            const int shift = plan.width * ps;
+            const int width = bits - shift < plan.width ? bits - shift : plan.width;
             uint32_t* ki = alt ? k1 : k0;
             uint32_t* vi = alt ? v1 : v0;
             uint32_t* ko = alt ? k0 : k1;
             uint32_t* vo = alt ? v0 : v1;
-            uint32_t* tot = totals + 256 * p;
-            hipLaunchKernelGGL(k_count, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, n, shift, nbits,
-                               hist, n_tiles, tot);
-            hipLaunchKernelGGL(k_offsets, dim3(256), dim3(SB), 0, s, hist, n_tiles, tot);
-            {
-                TraceScope ts(RSE_K_SORT_SCATTER, s);
-                hipLaunchKernelGGL(k_scatter, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, vi, ko, vo, n,
-                                   shift, nbits, hist, n_tiles);
-            }
+            TraceScope ts(RSE_K_SORT_SCATTER, s);
+            hipLaunchKernelGGL(k_onesweep, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, vi, ko, vo, n, shift, width,
+                               p.totals + ps * SORT_MAX_BINS, p.state + (int64_t)ps * n_tiles * SORT_MAX_BINS,
+                               p.tile_ctr + ps, p.error);
             alt = !alt;
         }
     }
     *result_in_alt = alt;
     return launch_status();
-}
-
-uint32_t* sort_totals(void* ws, int64_t n) {
-    int64_t n_tiles = 0;
-    sort_workspace(n, &n_tiles);
-    Carver c(ws);
-    c.take<uint32_t>((size_t)256 * (size_t)(n_tiles > 0 ? n_tiles : 1));
-    return c.take<uint32_t>((size_t)SORT_MAX_PASSES * 256);
 }
 
 }  // namespace rse_host
