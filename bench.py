@@ -45,7 +45,28 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=2)
     p.add_argument("--map-load", type=float, default=0.5)
+    p.add_argument("--serial-bwd", action="store_true",
+                   help="run the backward as one call after the forward instead of sorting on a second "
+                        "stream while the forward runs")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of COPY_BYTES (an elementwise kernel that reads and "
+                        "writes each byte once), to scale the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+COPY_BYTES = 872_415_232
+
+
+def copy_calibration():
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 10}))
 
 
 def compulsory_bytes(cfg, L, U, n_new, row_bytes):
@@ -63,6 +84,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -122,6 +146,10 @@ def main():
     log(f"staged {len(batches)} batches, setup {time.time() - t0:.1f}s")
 
     stream = torch.cuda.current_stream()
+    # the backward's sort needs only the row offsets: it runs on a second
+    # stream (default priority) while the forward runs on the first
+    side = torch.cuda.Stream(device=dev)
+    found_ev, sorted_ev = torch.cuda.Event(), torch.cuda.Event()
     step_no = [0]
 
     def step(b, ev=None):
@@ -130,13 +158,23 @@ def main():
         rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws)
         if ev:
             ev[1].record(stream)
+        plan = None
+        if not args.serial_bwd:
+            found_ev.record(stream)
+            side.wait_event(found_ev)
+            plan = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, bwd_ws, stream=side)
+            sorted_ev.record(side)
         rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
         if ev:
             ev[2].record(stream)
         g = b["grad"] if b["grad"] is not None else 2.0 * out
         step_no[0] += 1
-        rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
-                                     ws=bwd_ws)
+        if args.serial_bwd:
+            rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+                                         ws=bwd_ws)
+        else:
+            stream.wait_event(sorted_ev)
+            rse.embedding_bag_bwd_apply(blk, plan, b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u, bwd_ws)
         if ev:
             ev[3].record(stream)
 
@@ -225,6 +263,8 @@ def main():
         "step_compulsory_bytes": int(comp),
         "step_hbm_gbs": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4),
+        "schedule": ("find; bwd update after fwd (one stream)" if args.serial_bwd else
+                     "find; fwd on stream 1 || bwd prepare (pairs + sort) on stream 2; bwd apply on stream 1"),
         "ms_find": round(float(t_find), 4), "ms_fwd": round(float(t_fwd), 4), "ms_bwd_update": round(float(t_bwd), 4),
         "wall_s": round(wall, 4),
         "roofline": roofline,

@@ -277,6 +277,47 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
                              int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes,
                              void* stream);
 
+/*
+ * embedding_bag_bwd_update in two halves, so that the half that does not need
+ * the gradient can run while the forward does (same passages as above).
+ *
+ * embedding_bag_bwd_prepare validates the bag offsets and row offsets and
+ * sorts the lookups by row into d_ws; it reads only d_row_off and
+ * d_bag_offsets, so it may run on another stream concurrently with
+ * embedding_bag_fwd of the same batch (the caller orders it after the
+ * find-or-insert that wrote d_row_off).  *plan_out (host memory, caller
+ * owned) receives what the apply needs: the key width and the key used for
+ * lookups without a row, both fixed from the blocks' capacity at this call,
+ * so a blocks_grow between the halves is harmless.
+ *
+ * embedding_bag_bwd_apply reduces the gradient over the sorted lookups and
+ * updates the rows; it must be ordered after the prepare that wrote d_ws and
+ * plan (on one stream, or with an event), with the same d_ws, n_tables,
+ * batch and d_bag_offsets contents.  A plan may be applied more than once
+ * (each apply updates the rows again).  d_ws must not be reused by another
+ * prepare until the apply has run.  Bad input found by the prepare (sticky
+ * status RSE_ERR_BAD_INPUT) makes the apply update nothing and write 0 to
+ * *d_n_unique_out.  Returns RSE_ERR_INVALID_ARG if plan does not match the
+ * call (n_tables * batch, the blocks' dim).
+ */
+typedef struct rse_bwd_plan {
+    int64_t n_ids;         /* lookups sorted */
+    int64_t n_bags;        /* n_tables * batch */
+    uint32_t invalid;      /* sort key of lookups without a row: 2^key_bits - 1 */
+    int32_t key_bits;      /* bits of the row keys sorted on */
+    int32_t sorted_in_alt; /* which half of the workspace holds the sorted pairs */
+    int32_t dim;           /* the blocks' dim */
+} rse_bwd_plan;
+
+int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
+                              const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
+                              void* d_ws, size_t ws_bytes, rse_bwd_plan* plan_out, void* stream);
+
+int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan,
+                            const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
+                            int32_t pooling, const float* d_grad, const rse_optim* opt,
+                            int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- kernel trace -- */
 /*
  * Per-kernel timing with HIP events, for measurement: while a trace is

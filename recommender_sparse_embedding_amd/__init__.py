@@ -6,6 +6,9 @@ HIP stream.  The functions keep the C ABI's names:
 
     idmap_find_or_insert, embedding_bag_fwd, embedding_bag_bwd_update, blocks_grow
 
+and embedding_bag_bwd_update's two halves, embedding_bag_bwd_prepare (sort;
+may overlap the forward on another stream) and embedding_bag_bwd_apply.
+
 ``IdMap`` and ``EmbeddingBlocks`` own the caller-side device memory of the two
 library objects.  Importing this package loads librse.so and fails if it is
 missing (there is no CPU fallback).
@@ -19,7 +22,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import RseError, RseOptim, check
+from ._lib import RseBwdPlan, RseError, RseOptim, check
 
 F32, BF16 = 0, 1
 SGD, ADAGRAD, ADAM = 0, 1, 2
@@ -263,6 +266,39 @@ def embedding_bag_bwd_update(blocks: EmbeddingBlocks, row_off: torch.Tensor, bag
                                        _ptr(ws), ws.numel(), _stream(stream)), "embedding_bag_bwd_update")
 
 
+def embedding_bag_bwd_prepare(blocks: EmbeddingBlocks, row_off: torch.Tensor, bag_offsets: torch.Tensor,
+                              n_tables: int, batch: int, ws: torch.Tensor, stream=None):
+    """First half of embedding_bag_bwd_update: validates the offsets and sorts
+    the lookups by row into ws.  Needs no gradient, so it may run on another
+    stream while the forward runs.  Returns the plan for
+    embedding_bag_bwd_apply."""
+    _need(row_off, torch.int64, "row_off")
+    _need(bag_offsets, torch.int64, "bag_offsets")
+    if bag_offsets.numel() != n_tables * batch + 1:
+        raise ValueError("bag_offsets must hold n_tables * batch + 1 entries")
+    plan = RseBwdPlan()
+    check(lib.embedding_bag_bwd_prepare(blocks.handle, _ptr(row_off), row_off.numel(), _ptr(bag_offsets),
+                                        n_tables, batch, _ptr(ws), ws.numel(), ctypes.byref(plan),
+                                        _stream(stream)), "embedding_bag_bwd_prepare")
+    return plan
+
+
+def embedding_bag_bwd_apply(blocks: EmbeddingBlocks, plan, bag_offsets: torch.Tensor, n_tables: int,
+                            batch: int, pooling: int, grad: torch.Tensor, optim: Optim, step: int,
+                            n_unique: torch.Tensor, ws: torch.Tensor, stream=None):
+    """Second half of embedding_bag_bwd_update: reduces grad over the lookups
+    sorted by embedding_bag_bwd_prepare (same ws) and updates the rows."""
+    _need(bag_offsets, torch.int64, "bag_offsets")
+    _need(grad, torch.float32, "grad")
+    _need(n_unique, torch.int64, "n_unique")
+    if grad.numel() != batch * n_tables * blocks.dim:
+        raise ValueError("grad must hold batch * n_tables * dim floats")
+    o = optim.struct(step)
+    check(lib.embedding_bag_bwd_apply(blocks.handle, ctypes.byref(plan), _ptr(bag_offsets), n_tables, batch,
+                                      pooling, _ptr(grad), ctypes.byref(o), _ptr(n_unique), _ptr(ws),
+                                      ws.numel(), _stream(stream)), "embedding_bag_bwd_apply")
+
+
 # ----------------------------------------------------------------- trace --
 K_PROBE, K_FWD, K_SORT_SCATTER, K_SEG_UPDATE, K_COMBINE = 1, 2, 3, 4, 5
 
@@ -282,6 +318,7 @@ def trace_stop():
 __all__ = [
     "F32", "BF16", "SGD", "ADAGRAD", "ADAM", "SUM", "MEAN", "Optim", "EmbeddingBlocks", "IdMap",
     "RseError", "blocks_grow", "idmap_find_or_insert", "embedding_bag_fwd", "embedding_bag_bwd_update",
+    "embedding_bag_bwd_prepare", "embedding_bag_bwd_apply",
     "bwd_workspace", "row_bytes", "status_str", "lib", "trace_start", "trace_stop", "K_PROBE", "K_FWD",
     "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE",
 ]

@@ -23,6 +23,11 @@ class RseError(RuntimeError):
         self.code = code
 
 
+class RseBwdPlan(ctypes.Structure):
+    _fields_ = [("n_ids", ctypes.c_int64), ("n_bags", ctypes.c_int64), ("invalid", ctypes.c_uint32),
+                ("key_bits", ctypes.c_int32), ("sorted_in_alt", ctypes.c_int32), ("dim", ctypes.c_int32)]
+
+
 class RseOptim(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("eps", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
@@ -61,6 +66,10 @@ SIGNATURES = {
     "rse_bwd_workspace_size": ([_I64, _I32, _I64, _I32, _PSZ], ctypes.c_int),
     "embedding_bag_bwd_update": ([_P, _P, _I64, _P, _I32, _I64, _I32, _P, ctypes.POINTER(RseOptim), _P,
                                   _P, _SZ, _P], ctypes.c_int),
+    "embedding_bag_bwd_prepare": ([_P, _P, _I64, _P, _I32, _I64, _P, _SZ, ctypes.POINTER(RseBwdPlan), _P],
+                                  ctypes.c_int),
+    "embedding_bag_bwd_apply": ([_P, ctypes.POINTER(RseBwdPlan), _P, _I32, _I64, _I32, _P,
+                                 ctypes.POINTER(RseOptim), _P, _P, _SZ, _P], ctypes.c_int),
     "rse_trace_start": ([_I32], ctypes.c_int),
     "rse_trace_stop": ([_PI64, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
 }

@@ -6,10 +6,14 @@
 // "RecIS：阿里开源推荐系统统一训练框架", "代码架构" (fused sparse-gradient
 // update with fewer atomics).
 //
-// Pipeline (one stream):
-//   reset -> pairs: (row, bag) per lookup, row as a 32-bit key (-1 -> a key
-//   above every row, sorted last) -> stable radix sort by row -> segmented
-//   reduction with the optimizer fused in -> combine of long segments.
+// Pipeline, in two calls that may run on different streams:
+//   prepare (needs only the row offsets and bag offsets, so it can overlap
+//   the forward):  reset -> pairs: (row, bag) per lookup, row as a 32-bit
+//   key (-1 -> a key above every row, sorted last) -> stable radix sort by
+//   row;
+//   apply (needs the upstream gradient):  reset of its counters ->
+//   segmented reduction with the optimizer fused in -> combine of long
+//   segments.
 //
 // Segmented reduction.  The sorted lookups are cut into pieces of P = 64.
 // A segment (all lookups of one row) of length <= LONG_T = 128 is reduced
@@ -79,15 +83,22 @@ struct Geo {
 };
 
 // ------------------------------------------------------------- pairs -----
-__global__ void k_bwd_reset(Ctr* ctr, SortPrep sp, int64_t* n_unique) {
+__global__ void k_bwd_reset(Ctr* ctr, SortPrep sp) {
     if (threadIdx.x == 0) {
         ctr->n_owners = 0;
         ctr->bad = 0;
-        *n_unique = 0;
         *sp.error = 0;
     }
     if (threadIdx.x < SORT_MAX_PASSES) sp.tile_ctr[threadIdx.x] = 0;
     for (int k = threadIdx.x; k < SORT_MAX_PASSES * SORT_MAX_BINS; k += blockDim.x) sp.totals[k] = 0;
+}
+
+// Counters of one apply (so a prepared sort may be applied more than once).
+__global__ void k_apply_reset(Ctr* ctr, int64_t* n_unique) {
+    if (threadIdx.x == 0) {
+        ctr->n_owners = 0;
+        *n_unique = 0;
+    }
 }
 
 // One thread per bag: key = row (or `invalid`), value = bag.  Malformed bag
@@ -494,59 +505,82 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a)
 }
 
 // ------------------------------------------------- long segment combine --
-// One block per owner (grid-stride): partials of the pieces the segment
-// covers, added round-robin per group then in group order.  Block 0 also
-// totals the distinct rows.
+// One block per owner (grid-stride).  The pieces a long segment covers are
+// its head's piece k0 (partial in carry slot 1) and the following pieces
+// whose first key is still the segment's (slot 0); they form a prefix, so
+// one block-wide count per 2^8 pieces finds the last one.  Partials are added
+// round-robin per group (U loads in flight, added in piece order) then in
+// group order, so the sum is the same on every run.  Block 0 also totals the
+// distinct rows.  512 threads: the longest segment's partials are read in a
+// few rounds.
+constexpr int COMBINE_BLOCK = 512;
+
 template <int D, bool BF16, int OPT>
-__global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_combine(BwdArgs a) {
+__global__ __launch_bounds__(COMBINE_BLOCK) void k_combine(BwdArgs a) {
     using G = Geo<D, BF16>;
-    constexpr int VEC = G::VEC, LPR = G::LPR, GPB = G::GPB;
+    constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = COMBINE_BLOCK, GPB = BLOCK / LPR;
+    constexpr int U = 4;
     __shared__ double s_part[GPB][D];
-    __shared__ int64_t s_end;
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
-    __shared__ unsigned long long s_sum[G::BLOCK / WAVE];
+    __shared__ unsigned long long s_sum[BLOCK / WAVE];
     stage_chunks(s_chunks, a.rv);
     if (a.ctr->bad || *a.sort_err) return;
     const int64_t n_owners = (int64_t)a.ctr->n_owners;
+    const int64_t n_pieces = (a.n + P - 1) / P;
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
     if (blockIdx.x == 0) {
         unsigned long long c = 0;
-        for (int b = threadIdx.x; b < a.n_seg_blocks; b += G::BLOCK) c += a.blk_unique[b];
+        const int nb = a.n_seg_blocks;
+        for (int b0 = 0; b0 < nb; b0 += 8 * BLOCK) {
+            uint32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int b = b0 + u * BLOCK + (int)threadIdx.x;
+                v[u] = a.blk_unique[b < nb ? b : nb - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (b0 + u * BLOCK + (int)threadIdx.x < nb) c += v[u];
+        }
         for (int o = WAVE / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, WAVE);
         if (lane_id() == 0) s_sum[threadIdx.x / WAVE] = c;
         __syncthreads();
         if (threadIdx.x == 0) {
             unsigned long long t = (unsigned long long)n_owners;
-            for (int w = 0; w < G::BLOCK / WAVE; ++w) t += s_sum[w];
+            for (int w = 0; w < BLOCK / WAVE; ++w) t += s_sum[w];
             *a.n_unique = (int64_t)t;
         }
     }
     for (int64_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
         const int64_t h = a.owners[o];
         const uint32_t key = a.keys[h];
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            // end of the run: first position after h with a different key
-            int64_t lo = h, hi = a.n;   // keys[lo] == key; keys[hi] != key (or end)
-            while (hi - lo > 1) {
-                const int64_t mid = lo + (hi - lo) / 2;
-                if (a.keys[mid] == key) lo = mid;
-                else hi = mid;
-            }
-            s_end = hi;
-        }
-        __syncthreads();
-        const int64_t e = s_end;
         const int64_t k0 = h / P;
-        const int64_t k1 = (e - 1) / P;
+        int64_t k1 = k0;
+        for (int64_t kb = k0 + 1;; kb += BLOCK) {
+            const int64_t k = kb + threadIdx.x;
+            const bool in = k < n_pieces && a.keys[k * P] == key;
+            const int cnt = __syncthreads_count(in);
+            k1 += cnt;
+            if (cnt < BLOCK) break;
+        }
         double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-        for (int64_t k = k0 + g; k <= k1; k += GPB) {
-            const double* src = a.carry + (k * 2 + (k == k0 ? 1 : 0)) * D + li * VEC;
+        for (int64_t kq = k0 + g; kq <= k1; kq += U * GPB) {
+            double src[U][VEC];
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) acc[c] += src[c];
+            for (int u = 0; u < U; ++u) {
+                const int64_t k = kq + u * GPB <= k1 ? kq + u * GPB : k1;
+                const double* p = a.carry + (k * 2 + (k == k0 ? 1 : 0)) * D + li * VEC;
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) src[u][c] = p[c];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (kq + u * GPB <= k1)
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) acc[c] += src[u][c];
         }
 #pragma unroll
         for (int c = 0; c < VEC; ++c) s_part[g][li * VEC + c] = acc[c];
@@ -564,6 +598,7 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_combine(BwdArgs a) {
             load_row<D, BF16, OPT>(row, li, rr);
             finish_row<D, BF16, OPT>(a, row, li, rr, tot);
         }
+        __syncthreads();       // s_part is reused by the next owner
     }
 }
 
@@ -611,7 +646,7 @@ int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     const int cblocks = fill_blocks(n_pieces, 1, 2048);
     {
         TraceScope ts(RSE_K_COMBINE, s);
-        hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(G::BLOCK), 0, s, a);
+        hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(COMBINE_BLOCK), 0, s, a);
     }
     return launch_status();
 }
@@ -658,16 +693,12 @@ int rse_bwd_workspace_size(int64_t n_ids, int32_t n_tables, int64_t batch, int32
     return RSE_OK;
 }
 
-int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
-                             const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
-                             int32_t pooling, const float* d_grad, const rse_optim* opt,
-                             int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes, void* stream) {
-    if (!blocks || !d_bag_offsets || !opt || !d_n_unique_out || !d_ws) return RSE_ERR_INVALID_ARG;
+int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
+                              const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch, void* d_ws,
+                              size_t ws_bytes, rse_bwd_plan* plan_out, void* stream) {
+    if (!blocks || !d_bag_offsets || !d_ws || !plan_out) return RSE_ERR_INVALID_ARG;
     if (n_ids < 0 || n_tables <= 0 || batch < 0) return RSE_ERR_INVALID_ARG;
-    if (n_ids > 0 && (!d_row_off || !d_grad)) return RSE_ERR_INVALID_ARG;
-    if (pooling != RSE_SUM && pooling != RSE_MEAN) return RSE_ERR_INVALID_ARG;
-    if (opt->kind != blocks->optim) return RSE_ERR_INVALID_ARG;
-    if (opt->kind == RSE_ADAM && opt->step < 1) return RSE_ERR_INVALID_ARG;
+    if (n_ids > 0 && !d_row_off) return RSE_ERR_INVALID_ARG;
     const int64_t n_bags = (int64_t)n_tables * batch;
     if (n_ids > RSE_MAX_BWD_IDS || n_bags > (int64_t)0xFFFFFFFFll) return RSE_ERR_INVALID_ARG;
     size_t need = 0;
@@ -675,34 +706,69 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     SortPrep sp = sort_prep(w.sort_ws, n_ids);
-    hipLaunchKernelGGL(k_bwd_reset, dim3(1), dim3(256), 0, s, w.ctr, sp, d_n_unique_out);
-    if (n_ids == 0 || n_bags == 0) return launch_status();
-
     const int64_t capacity = blocks->capacity();
     int bits = bit_length((uint64_t)capacity);
     if (bits < 1) bits = 1;
     const uint32_t invalid = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
-    const SortPlan plan = sort_plan(bits);
-    sp.state_words = sp.state_words / SORT_MAX_PASSES * plan.passes;   // only the passes that run
-    // grid bounded so the per-block histogram flush stays a few hundred atomics per bin
-    hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, 256, 512)), dim3(256), 0, s, d_row_off, d_bag_offsets,
-                       n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
-                       &blocks->header()->status, sp, plan.passes, plan.width);
-    bool alt = false;
-    int rc = radix_sort_pairs(w.k0, w.v0, w.k1, w.v1, n_ids, bits, w.sort_ws, &alt, s);
-    if (rc) return rc;
+    rse_bwd_plan plan;
+    plan.n_ids = n_ids;
+    plan.n_bags = n_bags;
+    plan.invalid = invalid;
+    plan.key_bits = bits;
+    plan.sorted_in_alt = 0;
+    plan.dim = blocks->dim;
+    hipLaunchKernelGGL(k_bwd_reset, dim3(1), dim3(256), 0, s, w.ctr, sp);
+    if (n_ids > 0 && n_bags > 0) {
+        const SortPlan sp_plan = sort_plan(bits);
+        sp.state_words = sp.state_words / SORT_MAX_PASSES * sp_plan.passes;   // only the passes that run
+        // grid bounded so the per-block histogram flush stays a few hundred atomics per bin
+        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, 256, 512)), dim3(256), 0, s, d_row_off,
+                           d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
+                           &blocks->header()->status, sp, sp_plan.passes, sp_plan.width);
+        bool alt = false;
+        const int rc = radix_sort_pairs(w.k0, w.v0, w.k1, w.v1, n_ids, bits, w.sort_ws, &alt, s);
+        if (rc) return rc;
+        plan.sorted_in_alt = alt ? 1 : 0;
+    }
+    const int rc = launch_status();
+    if (rc == RSE_OK) *plan_out = plan;
+    return rc;
+}
+
+int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const int64_t* d_bag_offsets,
+                            int32_t n_tables, int64_t batch, int32_t pooling, const float* d_grad,
+                            const rse_optim* opt, int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes,
+                            void* stream) {
+    if (!blocks || !plan || !d_bag_offsets || !opt || !d_n_unique_out || !d_ws) return RSE_ERR_INVALID_ARG;
+    if (n_tables <= 0 || batch < 0 || plan->n_ids < 0 || plan->n_ids > RSE_MAX_BWD_IDS)
+        return RSE_ERR_INVALID_ARG;
+    const int64_t n_ids = plan->n_ids;
+    const int64_t n_bags = (int64_t)n_tables * batch;
+    if (plan->n_bags != n_bags || plan->dim != blocks->dim) return RSE_ERR_INVALID_ARG;
+    if (plan->key_bits < 1 || plan->key_bits > 32) return RSE_ERR_INVALID_ARG;
+    if (n_ids > 0 && !d_grad) return RSE_ERR_INVALID_ARG;
+    if (pooling != RSE_SUM && pooling != RSE_MEAN) return RSE_ERR_INVALID_ARG;
+    if (opt->kind != blocks->optim) return RSE_ERR_INVALID_ARG;
+    if (opt->kind == RSE_ADAM && opt->step < 1) return RSE_ERR_INVALID_ARG;
+    size_t need = 0;
+    BwdWs w = carve(d_ws, n_ids, blocks->dim, &need);
+    if (ws_bytes < need) return RSE_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    SortPrep sp = sort_prep(w.sort_ws, n_ids);
+    hipLaunchKernelGGL(k_apply_reset, dim3(1), dim3(64), 0, s, w.ctr, d_n_unique_out);
+    if (n_ids == 0 || n_bags == 0) return launch_status();
 
     BwdArgs a;
     a.rv = blocks->view();
-    a.keys = alt ? w.k1 : w.k0;
-    a.vals = alt ? w.v1 : w.v0;
+    a.keys = plan->sorted_in_alt ? w.k1 : w.k0;
+    a.vals = plan->sorted_in_alt ? w.v1 : w.v0;
     a.bag_off = d_bag_offsets;
     a.grad = d_grad;
     a.batch = batch;
     a.n_tables = n_tables;
     a.mean = pooling == RSE_MEAN;
     a.n = n_ids;
-    a.invalid = invalid;
+    a.invalid = plan->invalid;
     a.n_seg_blocks = 0;
     a.ctr = w.ctr;
     a.carry = w.carry;
@@ -720,6 +786,23 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
     a.op.bc1 = opt->kind == RSE_ADAM ? 1.0 - std::pow(opt->beta1, (double)opt->step) : 1.0;
     a.op.bc2 = opt->kind == RSE_ADAM ? 1.0 - std::pow(opt->beta2, (double)opt->step) : 1.0;
     return dispatch(a, blocks->dim, blocks->w_dtype == RSE_BF16, opt->kind, n_ids, s);
+}
+
+int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
+                             const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,
+                             int32_t pooling, const float* d_grad, const rse_optim* opt,
+                             int64_t* d_n_unique_out, void* d_ws, size_t ws_bytes, void* stream) {
+    if (!blocks || !d_bag_offsets || !opt || !d_n_unique_out || !d_ws) return RSE_ERR_INVALID_ARG;
+    if (n_ids > 0 && (!d_row_off || !d_grad)) return RSE_ERR_INVALID_ARG;
+    if (pooling != RSE_SUM && pooling != RSE_MEAN) return RSE_ERR_INVALID_ARG;
+    if (opt->kind != blocks->optim) return RSE_ERR_INVALID_ARG;
+    if (opt->kind == RSE_ADAM && opt->step < 1) return RSE_ERR_INVALID_ARG;
+    rse_bwd_plan plan;
+    int rc = embedding_bag_bwd_prepare(blocks, d_row_off, n_ids, d_bag_offsets, n_tables, batch, d_ws, ws_bytes,
+                                       &plan, stream);
+    if (rc) return rc;
+    return embedding_bag_bwd_apply(blocks, &plan, d_bag_offsets, n_tables, batch, pooling, d_grad, opt,
+                                   d_n_unique_out, d_ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ class GpuTables:
     """The library's objects for one table group, sized for `max_rows`."""
 
     def __init__(self, cfg: synth.Config, card, max_rows: int, rows_per_chunk_log2: int = 14,
-                 load: float = 0.7, device="cuda", extra_keys=0):
+                 load: float = 0.7, device="cuda", extra_keys=0, split: bool = False):
         import recommender_sparse_embedding_amd as rse
 
         self.rse = rse
@@ -40,6 +40,11 @@ class GpuTables:
         self.step = 0
         self.n_new = torch.zeros(1, dtype=torch.int64, device=self.dev)
         self.n_unique = torch.zeros(1, dtype=torch.int64, device=self.dev)
+        # split: the backward's sort (prepare) runs on a side stream while the
+        # forward runs; the apply waits for it on the main stream
+        self.split = split
+        self.side = torch.cuda.Stream(device=self.dev) if split else None
+        self.plan = None
 
     def find_or_insert(self, ids, bounds, stride, insert=True):
         t_ids = torch.from_numpy(np.ascontiguousarray(ids)).to(self.dev)
@@ -56,13 +61,37 @@ class GpuTables:
         self.rse.embedding_bag_fwd(self.blocks, ro, t_bo, cfg.n_tables, cfg.batch, cfg.pooling, out)
         return out
 
+    def prepare(self, ro, bo):
+        """Split mode: start the backward's sort on the side stream (after
+        the work queued so far on the main stream)."""
+        if not self.split:
+            return
+        cfg = self.cfg
+        main = torch.cuda.current_stream(self.dev)
+        t_bo = torch.from_numpy(bo).to(self.dev)
+        self.ws = self.rse.bwd_workspace(ro.numel(), cfg.n_tables, cfg.batch, cfg.dim, self.dev)
+        ev = torch.cuda.Event()
+        ev.record(main)
+        self.side.wait_event(ev)
+        for t in (ro, t_bo, self.ws):
+            t.record_stream(self.side)
+        self.plan = self.rse.embedding_bag_bwd_prepare(self.blocks, ro, t_bo, cfg.n_tables, cfg.batch, self.ws,
+                                                       stream=self.side)
+        self.prepared = torch.cuda.Event()
+        self.prepared.record(self.side)
+
     def bwd(self, ro, bo, grad):
         cfg = self.cfg
         self.step += 1
         t_bo = torch.from_numpy(bo).to(self.dev)
         g = grad if isinstance(grad, torch.Tensor) else torch.from_numpy(grad).to(self.dev)
-        self.rse.embedding_bag_bwd_update(self.blocks, ro, t_bo, cfg.n_tables, cfg.batch, cfg.pooling,
-                                          g.contiguous(), self.optim, self.step, self.n_unique)
+        if self.split:
+            torch.cuda.current_stream(self.dev).wait_event(self.prepared)
+            self.rse.embedding_bag_bwd_apply(self.blocks, self.plan, t_bo, cfg.n_tables, cfg.batch, cfg.pooling,
+                                             g.contiguous(), self.optim, self.step, self.n_unique, self.ws)
+        else:
+            self.rse.embedding_bag_bwd_update(self.blocks, ro, t_bo, cfg.n_tables, cfg.batch, cfg.pooling,
+                                              g.contiguous(), self.optim, self.step, self.n_unique)
         return int(self.n_unique.item())
 
     def rows(self, offs):

@@ -93,4 +93,18 @@ def test_null_handles_rejected_without_gpu_work(lib):
     assert lib.embedding_bag_fwd(None, None, 0, None, 1, 1, 0, None, None) == -1
     assert lib.idmap_find_or_insert(None, None, None, 0, None, 1, 1, 1, None, None, None, 0, None) == -1
     assert lib.embedding_bag_bwd_update(None, None, 0, None, 1, 1, 0, None, None, None, None, 0, None) == -1
+    assert lib.embedding_bag_bwd_prepare(None, None, 0, None, 1, 1, None, 0, None, None) == -1
+    assert lib.embedding_bag_bwd_apply(None, None, None, 1, 1, 0, None, None, None, None, 0, None) == -1
     assert lib.rse_version() == 100
+
+
+def test_bwd_plan_layout_matches_header():
+    # the Python mirror of rse_bwd_plan must match the C layout: two int64,
+    # one uint32, three int32 -> 32 bytes
+    from recommender_sparse_embedding_amd._lib import RseBwdPlan
+
+    assert ctypes.sizeof(RseBwdPlan) == 32
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct rse_bwd_plan \{(.*?)\} rse_bwd_plan;", text, flags=re.S).group(1)
+    fields = re.findall(r"^\s*(\w+)\s+(\w+);", body, flags=re.M)
+    assert [f for _, f in fields] == [n for n, _ in RseBwdPlan._fields_]

@@ -19,14 +19,14 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64):
+def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64, split=False):
     wl = synth.Workload(cfg)
     orc = make_oracle(cfg)
     L_est = cfg.n_bags * (cfg.bag[2] if cfg.bag[0] == "uniform" else
                           cfg.bag[1] * 2 if cfg.bag[0] == "poisson" else cfg.bag[1])
     max_rows = int(wl.card.sum() if cfg.prepopulate else 0) + (max_new or L_est * steps) + 1024
     extra = (max_new or L_est * steps) if (cfg.fresh_frac > 0 or not cfg.prepopulate) else 0
-    gpu = GpuTables(cfg, wl.card, max_rows, extra_keys=extra)
+    gpu = GpuTables(cfg, wl.card, max_rows, extra_keys=extra, split=split)
     rtol = rtol_for(cfg.wdtype)
     for ids, bounds in wl.prepopulation(prepop_chunk):
         ro_r, nn_r = orc.find_or_insert(ids, bounds, 1)
@@ -41,6 +41,7 @@ def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64):
         ro_g, nn_g = gpu.find_or_insert(ids, bo, cfg.batch)
         assert nn_g == nn_r, (nn_g, nn_r)
         assert np.array_equal(ro_g.cpu().numpy(), ro_r), "row offsets"
+        gpu.prepare(ro_g, bo)
         out_g = gpu.fwd(ro_g, bo)
         out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
         assert_close(out_g.cpu().numpy(), out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol, "pooled output")
@@ -194,6 +195,108 @@ def test_run_to_run_bit_identical():
         w, s = gpu.rows(np.arange(orc.n_rows))
         res.append((w.view(np.uint32).copy(), s.view(np.uint32).copy()))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+# ------------------------------------------- backward in two halves ----
+@pytest.mark.parametrize("which", ["click_log", "mean_adam_bf16"])
+def test_split_backward_overlapping_forward(which):
+    """embedding_bag_bwd_prepare on a side stream, concurrent with the
+    forward; embedding_bag_bwd_apply after an event wait: same bar as the
+    one-call update."""
+    if which == "click_log":
+        cfg = synth.config(2, batch=2048, cardinality=("loguniform", 10, 200_000))
+        run_steps(cfg, 3, prepop_chunk=100_000, split=True)
+    else:
+        cfg = synth.config(3, n_tables=2, batch=512, dim=32, wdtype=1, optim=2, lr=1e-3,
+                           cardinality=("fixed", 20000), bag=("uniform", 1, 40), fresh_frac=0.01, pooling=1)
+        run_steps(cfg, 3, split=True)
+
+
+def _small_split_setup(rows_per_chunk_log2=4, n_chunks=1):
+    import recommender_sparse_embedding_amd as rse
+
+    cfg = synth.config(1, n_tables=1, batch=12, dim=16, bag=("fixed", 1), prepopulate=False, optim=1,
+                       lr=0.05)
+    gpu = GpuTables(cfg, [1000], (1 << rows_per_chunk_log2) * n_chunks, rows_per_chunk_log2=rows_per_chunk_log2)
+    return rse, cfg, gpu, make_oracle(cfg)
+
+
+def test_plan_applied_twice_updates_twice():
+    rse, cfg, gpu, orc = _small_split_setup()
+    ids = np.array([3, 7, 3, 9, 11, 7, 3, 20, 21, 22, 3, 9], dtype=np.int64)
+    bo = np.arange(13, dtype=np.int64)
+    ro_r, _ = orc.find_or_insert(ids, bo, cfg.batch)
+    ro_g, _ = gpu.find_or_insert(ids, bo, cfg.batch)
+    assert np.array_equal(ro_g.cpu().numpy(), ro_r)
+    G = np.random.default_rng(3).standard_normal((cfg.batch, 1, cfg.dim)).astype(np.float32)
+    t_bo = torch.from_numpy(bo).cuda()
+    ws = rse.bwd_workspace(len(ids), 1, cfg.batch, cfg.dim)
+    plan = rse.embedding_bag_bwd_prepare(gpu.blocks, ro_g, t_bo, 1, cfg.batch, ws)
+    for step in (1, 2):
+        rse.embedding_bag_bwd_apply(gpu.blocks, plan, t_bo, 1, cfg.batch, cfg.pooling, torch.from_numpy(G).cuda(),
+                                    gpu.optim, step, gpu.n_unique, ws)
+        U = orc.bwd_update(ro_r, bo, cfg.batch, G, cfg.pooling)
+        assert int(gpu.n_unique.item()) == U == 7
+    offs = np.arange(orc.n_rows)
+    w_g, s_g = gpu.rows(offs)
+    w_r, s_r = orc.get_rows(offs)
+    assert np.allclose(w_g, w_r, rtol=1e-6, atol=1e-7) and np.allclose(s_g, s_r, rtol=1e-6, atol=1e-7)
+
+
+def test_blocks_grow_between_prepare_and_apply():
+    """Lookups without a row sort under a key fixed at prepare time (2^5 - 1
+    for 16 rows); after growing to 48 rows and inserting keys up to row 34,
+    row 31 is real and must stay untouched by the apply."""
+    rse, cfg, gpu, orc = _small_split_setup()
+    base = np.arange(100, 110, dtype=np.int64)                   # rows 0..9
+    orc.find_or_insert(base, np.array([0, 10]), 1)
+    gpu.find_or_insert(base, np.array([0, 10]), 1)
+    ids = np.array([100, 101, 555, 102, 100, 556, 103, 104, 557, 105, 100, 109], dtype=np.int64)
+    bo = np.arange(13, dtype=np.int64)
+    ro_r, _ = orc.find_or_insert(ids, bo, cfg.batch, insert_missing=False)
+    ro_g, _ = gpu.find_or_insert(ids, bo, cfg.batch, insert=False)
+    assert np.array_equal(ro_g.cpu().numpy(), ro_r) and (ro_r == -1).sum() == 3
+    t_bo = torch.from_numpy(bo).cuda()
+    ws = rse.bwd_workspace(len(ids), 1, cfg.batch, cfg.dim)
+    plan = rse.embedding_bag_bwd_prepare(gpu.blocks, ro_g, t_bo, 1, cfg.batch, ws)
+    assert plan.key_bits == 5 and plan.invalid == 31
+    gpu.blocks.grow(2)
+    more = np.arange(200, 225, dtype=np.int64)                   # rows 10..34
+    orc.find_or_insert(more, np.array([0, 25]), 1)
+    ro_m, n_m = gpu.find_or_insert(more, np.array([0, 25]), 1)
+    assert n_m == 25 and int(ro_m[-1].item()) == 34
+    G = np.random.default_rng(4).standard_normal((cfg.batch, 1, cfg.dim)).astype(np.float32)
+    rse.embedding_bag_bwd_apply(gpu.blocks, plan, t_bo, 1, cfg.batch, cfg.pooling, torch.from_numpy(G).cuda(),
+                                gpu.optim, 1, gpu.n_unique, ws)
+    U = orc.bwd_update(ro_r, bo, cfg.batch, G, cfg.pooling)
+    assert int(gpu.n_unique.item()) == U == 7
+    offs = np.arange(35)
+    w_g, s_g = gpu.rows(offs)
+    w_r, s_r = orc.get_rows(offs)
+    assert np.array_equal(w_g[10:].view(np.uint32), w_r[10:].view(np.uint32)), "rows inserted later changed"
+    assert np.array_equal(s_g[10:].view(np.uint32), s_r[10:].view(np.uint32))
+    assert np.allclose(w_g, w_r, rtol=1e-6, atol=1e-7) and np.allclose(s_g, s_r, rtol=1e-6, atol=1e-7)
+
+
+def test_plan_mismatch_rejected():
+    rse, cfg, gpu, orc = _small_split_setup()
+    ids = np.arange(12, dtype=np.int64)
+    bo = np.arange(13, dtype=np.int64)
+    ro_g, _ = gpu.find_or_insert(ids, bo, cfg.batch)
+    t_bo = torch.from_numpy(bo).cuda()
+    ws = rse.bwd_workspace(len(ids), 1, cfg.batch, cfg.dim)
+    plan = rse.embedding_bag_bwd_prepare(gpu.blocks, ro_g, t_bo, 1, cfg.batch, ws)
+    G6 = torch.zeros((6, 1, cfg.dim), dtype=torch.float32, device="cuda")
+    with pytest.raises(rse.RseError) as e:                     # 6 bags, the plan has 12
+        rse.embedding_bag_bwd_apply(gpu.blocks, plan, torch.arange(7, device="cuda"), 1, 6, 0, G6, gpu.optim, 1,
+                                    gpu.n_unique, ws)
+    assert e.value.code == -1
+    G = torch.zeros((cfg.batch, 1, cfg.dim), dtype=torch.float32, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(rse.RseError) as e:
+        rse.embedding_bag_bwd_apply(gpu.blocks, plan, t_bo, 1, cfg.batch, 0, G, gpu.optim, 1, gpu.n_unique, small)
+    assert e.value.code == -3
+    del orc
 
 
 # ----------------------------------------------------------- failures ----
