@@ -46,8 +46,8 @@ def parse():
     p.add_argument("--cpu-steps", type=int, default=2)
     p.add_argument("--map-load", type=float, default=0.5)
     p.add_argument("--serial-bwd", action="store_true",
-                   help="run the backward as one call after the forward instead of sorting on a second "
-                        "stream while the forward runs")
+                   help="report the serial schedule (find, fwd, bwd update on one stream) as the value instead "
+                        "of the pipelined one")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (an elementwise kernel that reads and "
                         "writes each byte once), to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -146,65 +146,124 @@ def main():
     log(f"staged {len(batches)} batches, setup {time.time() - t0:.1f}s")
 
     stream = torch.cuda.current_stream()
-    # the backward's sort needs only the row offsets: it runs on a second
-    # stream (default priority) while the forward runs on the first
+    # second stream (default priority) for the work that does not wait for
+    # the previous phase: the backward's sort, and the next batch's find
     side = torch.cuda.Stream(device=dev)
-    found_ev, sorted_ev = torch.cuda.Event(), torch.cuda.Event()
+    ws2 = [bwd_ws, rse.bwd_workspace(L_max, T, B, D, dev)]
     step_no = [0]
 
-    def step(b, ev=None):
+    def grad_of(b):
+        return b["grad"] if b["grad"] is not None else 2.0 * out
+
+    def step_serial(b):
+        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws)
+        rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
+        step_no[0] += 1
+        rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, grad_of(b), opt, step_no[0], n_u,
+                                     ws=bwd_ws)
+
+    def step_overlap(b, ev=None):
+        """find; then the forward (stream 1) and the backward's sort (stream
+        2) together; then the apply."""
         if ev:
             ev[0].record(stream)
         rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws)
         if ev:
             ev[1].record(stream)
-        plan = None
-        if not args.serial_bwd:
-            found_ev.record(stream)
-            side.wait_event(found_ev)
-            plan = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, bwd_ws, stream=side)
-            sorted_ev.record(side)
+        found = torch.cuda.Event()
+        found.record(stream)
+        side.wait_event(found)
+        plan = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, bwd_ws, stream=side)
+        srt = torch.cuda.Event()
+        srt.record(side)
         rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
         if ev:
             ev[2].record(stream)
-        g = b["grad"] if b["grad"] is not None else 2.0 * out
+        g = grad_of(b)
         step_no[0] += 1
-        if args.serial_bwd:
-            rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
-                                         ws=bwd_ws)
-        else:
-            stream.wait_event(sorted_ev)
-            rse.embedding_bag_bwd_apply(blk, plan, b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u, bwd_ws)
+        stream.wait_event(srt)
+        rse.embedding_bag_bwd_apply(blk, plan, b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u, bwd_ws)
         if ev:
             ev[3].record(stream)
 
-    for k in range(args.warmup):
-        step(batches[k % len(batches)])
-    torch.cuda.synchronize()
+    # Pipelined steps: the find and sort of batch i+1 (stream 2) run while
+    # batch i's forward and apply run (stream 1).  The find of batch i+1 only
+    # touches the map, rows it creates and its own outputs, none of which
+    # batch i's apply reads or writes; the forward of batch i+1 waits for
+    # both.  Sort workspaces alternate; a sort waits for the apply that last
+    # used its workspace.
+    applied = [torch.cuda.Event(), torch.cuda.Event()]
+    fronted = [torch.cuda.Event(), torch.cuda.Event()]
+    plans = [None, None]
+
+    def front(i, b):
+        side.wait_event(applied[i % 2])
+        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws, stream=side)
+        plans[i % 2] = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, ws2[i % 2], stream=side)
+        fronted[i % 2].record(side)
+
+    def back(i, b):
+        stream.wait_event(fronted[i % 2])
+        rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
+        g = grad_of(b)
+        step_no[0] += 1
+        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+                                    ws2[i % 2])
+        applied[i % 2].record(stream)
+
+    def batch_at(k):
+        return batches[k % len(batches)]
+
+    def timed(schedule, first, n, evs=None):
+        """n steps over batches first.., timed between events on stream 1
+        (every stream's work inside is waited for); returns ms."""
+        torch.cuda.synchronize()
+        if schedule == "pipelined":
+            front(first, batch_at(first))
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for k in range(n):
+            i = first + k
+            if schedule == "serial":
+                step_serial(batch_at(i))
+            elif schedule == "overlap":
+                step_overlap(batch_at(i), evs[k] if evs else None)
+            else:
+                front(i + 1, batch_at(i + 1))      # the next batch: one find + sort per step
+                back(i, batch_at(i))
+        if schedule == "pipelined":
+            stream.wait_event(fronted[(first + n) % 2])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    schedule = "serial" if args.serial_bwd else ("pipelined" if len(batches) >= 2 else "overlap")
+    for name in ("serial", "overlap", schedule):
+        timed(name, 0, args.warmup)
     used, st = blk.status()
     assert st == 0, st
 
     # ----------------------------------------------------- timed region --
     # The library brackets every launch of the segmented-update kernel (the
     # step's largest) with HIP events on its stream while the trace is on.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rse.trace_start(rse.K_SEG_UPDATE)
     w0 = time.perf_counter()
-    start.record(stream)
-    for k in range(args.steps):
-        step(batches[(args.warmup + k) % len(batches)], evs[k])
-    stop.record(stream)
-    torch.cuda.synchronize()
+    ms_total = timed(schedule, args.warmup, args.steps)
     wall = time.perf_counter() - w0
     n_seg, seg_ms = rse.trace_stop()
-    ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    t_seg = seg_ms / max(n_seg, 1)
+    # the other schedules, and the phase split of the overlapped one, for reference
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ms_overlap = timed("overlap", args.warmup, args.steps, evs) / args.steps
     t_find = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
-    t_seg = seg_ms / max(n_seg, 1)
+    rse.trace_start(rse.K_FWD)
+    ms_serial = timed("serial", args.warmup, args.steps) / args.steps
+    n_fwd, fwd_ms = rse.trace_stop()
+    t_fwd_kernel = fwd_ms / max(n_fwd, 1)
     idm_st, _ = idm.status()
     used, st = blk.status()
     assert idm_st == 0 and st == 0, (idm_st, st)
@@ -233,9 +292,9 @@ def main():
                 "frac": round(seg_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(seg_bytes), "avg_launch_ms": round(t_seg, 4),
                 "launches_timed": n_seg}
-    fwd_roof = {"kernel": "embedding_bag_fwd", "achieved": round(fwd_bytes / (t_fwd * 1e-3) / 1e9, 1),
+    fwd_roof = {"kernel": "embedding_bag_fwd", "achieved": round(fwd_bytes / (t_fwd_kernel * 1e-3) / 1e9, 1),
                 "unit": "GB/s", "algorithmic_bytes_per_launch": int(fwd_bytes),
-                "avg_launch_ms": round(float(t_fwd), 4)}
+                "avg_launch_ms": round(float(t_fwd_kernel), 4)}
 
     # --------------------------------------------------- CPU baseline -----
     cpu = None
@@ -263,9 +322,14 @@ def main():
         "step_compulsory_bytes": int(comp),
         "step_hbm_gbs": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4),
-        "schedule": ("find; bwd update after fwd (one stream)" if args.serial_bwd else
-                     "find; fwd on stream 1 || bwd prepare (pairs + sort) on stream 2; bwd apply on stream 1"),
-        "ms_find": round(float(t_find), 4), "ms_fwd": round(float(t_fwd), 4), "ms_bwd_update": round(float(t_bwd), 4),
+        "schedule": {"serial": "find; fwd; bwd update (one stream)",
+                     "overlap": "find; fwd (stream 1) || bwd prepare = pairs + sort (stream 2); bwd apply",
+                     "pipelined": "fwd + bwd apply of batch i (stream 1) || find + bwd prepare of batch i+1 "
+                                  "(stream 2)"}[schedule],
+        "ms_per_step_by_schedule": {"serial": round(ms_serial, 4), "overlap": round(ms_overlap, 4),
+                                    "pipelined": round(ms_step, 4) if schedule == "pipelined" else None},
+        "overlap_phase_ms": {"find": round(float(t_find), 4), "fwd": round(float(t_fwd), 4),
+                             "bwd_update": round(float(t_bwd), 4)},
         "wall_s": round(wall, 4),
         "roofline": roofline,
         "fwd_roofline": fwd_roof,

@@ -41,13 +41,13 @@ __global__ void k_read_rows(RowsView rv, const int64_t* offs, int64_t n, int dim
         const char* row = rv.row(offs[q]);
         if (c < dim) {
             float v;
-            if (BF16) v = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[c]);
-            else v = reinterpret_cast<const float*>(row)[c];
+            if (BF16) v = bf16_to_f32(((const RSE_GLOBAL uint16_t*)row)[c]);
+            else v = ((const RSE_GLOBAL float*)row)[c];
             w_out[q * dim + c] = v;
         } else if (st_out) {
             const int64_t w_bytes = (int64_t)dim * (BF16 ? 2 : 4);
             st_out[q * (per_row - dim) + (c - dim)] =
-                reinterpret_cast<const float*>(row + w_bytes)[c - dim];
+                ((const RSE_GLOBAL float*)(row + w_bytes))[c - dim];
         }
     }
 }

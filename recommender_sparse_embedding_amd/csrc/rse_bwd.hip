@@ -169,7 +169,7 @@ template <int VEC>
 __device__ __forceinline__ void load_grad(float* out, const float* src) {
 #pragma unroll
     for (int k = 0; k < VEC; k += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + k);
+        const f32x4 v = gload_f4(src + k);
         out[k] = v.x;
         out[k + 1] = v.y;
         out[k + 2] = v.z;
@@ -225,7 +225,7 @@ __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_va
 template <int D, bool BF16>
 struct RowRegs {
     static constexpr int VEC = Geo<D, BF16>::VEC;
-    uint4 w;
+    u32x4 w;
     float st0[VEC];
     float st1[VEC];
 };
@@ -234,7 +234,7 @@ template <int D, bool BF16, int OPT>
 __device__ __forceinline__ void load_row(const char* row, int li, RowRegs<D, BF16>& r) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     constexpr int64_t W_BYTES = (int64_t)D * (BF16 ? 2 : 4);
-    r.w = *reinterpret_cast<const uint4*>(row + li * 16);
+    r.w = gload_u4(row + li * 16);
     const float* st0 = reinterpret_cast<const float*>(row + W_BYTES) + li * VEC;
     if (OPT != RSE_SGD) load_grad<VEC>(r.st0, st0);
     if (OPT == RSE_ADAM) load_grad<VEC>(r.st1, st0 + D);
@@ -275,7 +275,7 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
         }
 #pragma unroll
         for (int k = 0; k < VEC; k += 4)
-            *reinterpret_cast<float4*>(st0 + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+            gstore_f4(st0 + k, f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]});
     } else {
         float m[VEC], v[VEC];
 #pragma unroll
@@ -290,22 +290,22 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
         }
 #pragma unroll
         for (int k = 0; k < VEC; k += 4) {
-            *reinterpret_cast<float4*>(st0 + k) = make_float4(m[k], m[k + 1], m[k + 2], m[k + 3]);
-            *reinterpret_cast<float4*>(st1 + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+            gstore_f4(st0 + k, f32x4{m[k], m[k + 1], m[k + 2], m[k + 3]});
+            gstore_f4(st1 + k, f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]});
         }
     }
-    uint4 out;
+    u32x4 out;
     if (!BF16) {
-        out = make_uint4(__float_as_uint((float)wn[0]), __float_as_uint((float)wn[1]),
-                         __float_as_uint((float)wn[2]), __float_as_uint((float)wn[3]));
+        out = u32x4{__float_as_uint((float)wn[0]), __float_as_uint((float)wn[1]), __float_as_uint((float)wn[2]),
+                    __float_as_uint((float)wn[3])};
     } else {
         uint32_t q4[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             q4[k] = (uint32_t)f64_to_bf16_rne(wn[2 * k]) | ((uint32_t)f64_to_bf16_rne(wn[2 * k + 1]) << 16);
-        out = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+        out = u32x4{q4[0], q4[1], q4[2], q4[3]};
     }
-    reinterpret_cast<uint4*>(row)[li] = out;
+    gstore_u4(row + li * 16, out);
 }
 
 // ------------------------------------------------- segmented update ------

@@ -54,6 +54,25 @@ struct BlocksHeader {
 };
 static_assert(sizeof(BlocksHeader) == 256, "BlocksHeader size");
 
+// ------------------------------------------------- global row access ----
+// Row addresses are computed from integers (chunk base + offset), so the
+// compiler cannot tell which memory they point to and would use FLAT
+// instructions.  FLAT accesses are tracked by both the vector-memory and the
+// LDS counters, so every wait for an LDS read (or for the chunk-table read of
+// the next row) would also wait for all row loads in flight.  Rows are
+// therefore read and written through explicit global-address-space pointers
+// with clang vector types (HIP's uint4/float4 are structs, whose copies lose
+// the address space).
+#define RSE_GLOBAL __attribute__((address_space(1)))
+#define RSE_LDS __attribute__((address_space(3)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 gload_u4(const void* p) { return *(const RSE_GLOBAL u32x4*)p; }
+__device__ __forceinline__ f32x4 gload_f4(const void* p) { return *(const RSE_GLOBAL f32x4*)p; }
+__device__ __forceinline__ void gstore_u4(void* p, u32x4 v) { *(RSE_GLOBAL u32x4*)p = v; }
+__device__ __forceinline__ void gstore_f4(void* p, f32x4 v) { *(RSE_GLOBAL f32x4*)p = v; }
+
 // Everything a kernel needs to address rows (passed by value).  Kernels on
 // the hot path stage the chunk-pointer table in LDS (stage_chunks) so that a
 // row address costs an LDS read instead of a dependent global load.
@@ -66,14 +85,16 @@ struct RowsView {
     int32_t n_chunks;
     uint64_t mask;            // rows per chunk - 1
     __device__ __forceinline__ char* row(int64_t r) const {
-        const uint64_t base = chunks[(uint64_t)r >> shift];
+        const uint64_t base = ((const RSE_GLOBAL uint64_t*)chunks)[(uint64_t)r >> shift];
         return reinterpret_cast<char*>(base + ((uint64_t)r & mask) * (uint64_t)row_bytes);
     }
     __device__ __forceinline__ bool lds_ok() const { return n_chunks <= LDS_CHUNKS; }
-    // s: the LDS copy made by stage_chunks
+    // s: the LDS copy made by stage_chunks.  The two table reads are typed
+    // by address space so that they stay an LDS read and a global read (one
+    // FLAT read through a selected pointer would tie the counters together).
     __device__ __forceinline__ char* row(const uint64_t* s, int64_t r) const {
         const uint64_t c = (uint64_t)r >> shift;
-        const uint64_t base = lds_ok() ? s[c] : chunks[c];
+        const uint64_t base = lds_ok() ? ((const RSE_LDS uint64_t*)s)[c] : ((const RSE_GLOBAL uint64_t*)chunks)[c];
         return reinterpret_cast<char*>(base + ((uint64_t)r & mask) * (uint64_t)row_bytes);
     }
 };

@@ -34,7 +34,7 @@ struct Geo {
 };
 
 template <bool BF16>
-__device__ __forceinline__ void widen_add(double* acc, const uint4& q) {
+__device__ __forceinline__ void widen_add(double* acc, const u32x4& q) {
     if (!BF16) {
         acc[0] += (double)__uint_as_float(q.x);
         acc[1] += (double)__uint_as_float(q.y);
@@ -50,7 +50,6 @@ __device__ __forceinline__ void widen_add(double* acc, const uint4& q) {
     }
 }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Pooled rows are written once and not read again by this kernel: stream
 // them past the caches so hot embedding rows stay resident.
@@ -62,7 +61,7 @@ __device__ __forceinline__ void store_out(float* dst, const double* acc, double 
 #pragma unroll
     for (int k = 0; k < VEC; k += 4) {
         const f32x4 v = {f[k], f[k + 1], f[k + 2], f[k + 3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + k));
+        __builtin_nontemporal_store(v, (RSE_GLOBAL f32x4*)(dst + k));
     }
 }
 
@@ -91,107 +90,115 @@ __device__ __forceinline__ void flag_bad(const FwdArgs& a) {
 // dummy row and is masked out of the sum), so all UNROLL loads of a group
 // are in flight together instead of being serialised behind branches.
 __device__ __forceinline__ const char* dummy_row(const uint64_t* s_chunks, const RowsView& rv) {
-    return reinterpret_cast<const char*>(rv.lds_ok() ? s_chunks[0] : rv.chunks[0]);
+    return reinterpret_cast<const char*>(rv.lds_ok() ? ((const RSE_LDS uint64_t*)s_chunks)[0]
+                                                     : ((const RSE_GLOBAL uint64_t*)rv.chunks)[0]);
 }
 
 // ---------------------------------------------------- one-hot bags ------
-// A group owns BPG consecutive bags; the first row of every bag is loaded
-// at once (BPG loads in flight), further rows of a bag (rare) in order.
-template <int D, bool BF16, int BPG>
-__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
-    using G = Geo<D, BF16>;
-    constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
-    __shared__ uint64_t s_chunks[LDS_CHUNKS];
-    stage_chunks(s_chunks, a.rv);
-    const int lane = lane_id();
-    const int g = lane / LPR;
-    const int li = lane % LPR;
-    const int64_t gid = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE * GROUPS + g;
-    const int64_t n_groups = (int64_t)gridDim.x * (FWD_BLOCK / WAVE) * GROUPS;
-    const bool can_load = a.capacity > 0 && a.n_ids > 0;
-    const char* dummy = can_load ? dummy_row(s_chunks, a.rv) : nullptr;
-
-    for (int64_t jb = gid * BPG; jb < a.n_bags; jb += n_groups * BPG) {
-        const int nb = (int)(a.n_bags - jb < BPG ? a.n_bags - jb : BPG);
-        int64_t off[BPG + 1];
-        int64_t spec[BPG];
-#pragma unroll
-        for (int k = 0; k <= BPG; ++k) off[k] = a.bag_off[jb + (k < nb ? k : nb)];
-        // one-hot layouts have bag j's lookup at index j: load that row
-        // offset in parallel with the bag offsets (used if the guess holds)
-        if (can_load) {
-#pragma unroll
-            for (int k = 0; k < BPG; ++k) spec[k] = a.row_off[jb + k < a.n_ids ? jb + k : a.n_ids - 1];
-        }
-        bool ok = off[0] >= 0 && off[BPG] <= a.n_ids;   // off[BPG] == off[nb] (clamped loads)
-#pragma unroll
-        for (int k = 0; k < BPG; ++k) ok = ok && off[k + 1] >= off[k];
-        if (!ok) {
+// One chunk of BPG consecutive bags per group of LPR lanes, straight-line
+// (no loop: every wait covers exactly the loads it needs, and the stores are
+// the group's last instructions).  In the one-hot layout bag j holds exactly
+// lookup j.  Lane k < BPG loads bag k's two offsets and its row offset and
+// builds its row address (chunk table in LDS, reads clamped so none is
+// conditional); a group ballot decides whether the whole chunk is one-hot
+// and in range; the addresses are shuffled to all lanes and the BPG rows
+// loaded together.  Any other chunk (longer or empty bags, malformed
+// offsets, rows past the capacity) is done bag by bag by chunk_general.
+template <int D, bool BF16>
+__device__ __forceinline__ void chunk_general(const FwdArgs& a, const uint64_t* s_chunks, int64_t jb,
+                                                        int nb, int li) {
+    constexpr int VEC = Geo<D, BF16>::VEC;
+    for (int k = 0; k < nb; ++k) {
+        const int64_t j = jb + k;
+        const int64_t s0 = a.bag_off[j], e0 = a.bag_off[j + 1];
+        if (s0 < 0 || e0 < s0 || e0 > a.n_ids) {     // malformed: the bag's output is not written
             if (li == 0) flag_bad(a);
             continue;
         }
-        int64_t r[BPG];
-        bool v[BPG];
-        uint4 q[BPG];
+        double acc[VEC];
 #pragma unroll
-        for (int k = 0; k < BPG; ++k) {
-            const bool has = k < nb && off[k + 1] > off[k];
-            r[k] = !can_load ? -1 : (off[k] == jb + k ? spec[k] : a.row_off[has ? off[k] : 0]);
-            v[k] = has && r[k] >= 0 && r[k] < a.capacity;
-            if (has && r[k] >= a.capacity && li == 0) flag_bad(a);
-        }
-        if (can_load) {
-#pragma unroll
-            for (int k = 0; k < BPG; ++k)
-                q[k] = *reinterpret_cast<const uint4*>((v[k] ? a.rv.row(s_chunks, r[k]) : dummy) + li * 16);
-        }
-        const uint32_t t0 = (uint32_t)((uint64_t)jb / (uint64_t)a.batch);
-        const uint32_t b0 = (uint32_t)(jb - (int64_t)t0 * a.batch);
-        // bags of at most one lookup are finished from the prefetched rows;
-        // longer bags (rare here) are summed afresh below, in order
-        bool multi = false;
-        uint32_t t = t0, b = b0;
-#pragma unroll
-        for (int k = 0; k < BPG; ++k) {
-            const int64_t len = off[k + 1] - off[k];
-            if (k < nb && len <= 1) {
-                double acc[VEC];
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-                if (v[k]) widen_add<BF16>(acc, q[k]);
-                store_out<VEC>(a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC, acc, 1.0, false);
-            }
-            multi = multi || (k < nb && len > 1);
-            if (++b == (uint32_t)a.batch) {
-                b = 0;
-                ++t;
+        for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+        for (int64_t i = s0; i < e0; ++i) {
+            const int64_t r = a.row_off[i];
+            if (r >= a.capacity) {
+                if (li == 0) flag_bad(a);
+            } else if (r >= 0) {
+                widen_add<BF16>(acc, gload_u4(a.rv.row(s_chunks, r) + li * 16));
             }
         }
-        if (multi) {
-            t = t0;
-            b = b0;
-            for (int k = 0; k < nb; ++k) {
-                const int64_t s0 = a.bag_off[jb + k], e0 = a.bag_off[jb + k + 1];
-                if (e0 - s0 > 1) {
-                    double acc[VEC];
+        const int64_t t = (int64_t)((uint64_t)j / (uint64_t)a.batch);
+        const int64_t b = j - t * a.batch;
+        store_out<VEC>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, (double)(e0 - s0), a.mean && e0 > s0);
+    }
+}
+
+template <int D, bool BF16, int BPG, bool LDS_TAB>
+__global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
+    using G = Geo<D, BF16>;
+    constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    static_assert(BPG <= LPR && BPG <= 32, "one lane per bag of a chunk");
+    __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    const int lane = lane_id();
+    const int g = lane / LPR;
+    const int li = lane % LPR;
+    const int gbase = g * LPR;
+    const int64_t c = ((int64_t)blockIdx.x * FWD_BLOCK + threadIdx.x) / WAVE * GROUPS + g;
+    const int64_t n_chunk = (a.n_bags + BPG - 1) / BPG;
+    const bool live = c < n_chunk;
+    const int64_t jb = (live ? c : n_chunk - 1) * BPG;
+    const int nb = (int)(a.n_bags - jb < BPG ? a.n_bags - jb : BPG);
+    // lane k's bag (lanes past the chunk repeat its last bag); the host
+    // launches this kernel only with n_ids >= 1 and capacity >= 1
+    const int64_t j = jb + (li < nb ? li : nb - 1);
+    const int64_t lo = a.bag_off[j];
+    const int64_t hi = a.bag_off[j + 1];
+    const int64_t r = a.row_off[j < a.n_ids ? j : a.n_ids - 1];
+    if (LDS_TAB) stage_chunks(s_chunks, a.rv);
+    if (!live) return;
+
+    const bool one = lo == j && hi == j + 1;
+    const bool in_range = r < a.capacity;
+    const bool valid = one && r >= 0 && in_range;
+    const uint64_t ci = valid ? ((uint64_t)r >> a.rv.shift) : 0;
+    const uint64_t base = LDS_TAB ? ((const RSE_LDS uint64_t*)s_chunks)[ci]
+                                  : ((const RSE_GLOBAL uint64_t*)a.rv.chunks)[ci];
+    const uint64_t p = base + (valid ? ((uint64_t)r & a.rv.mask) * (uint64_t)a.rv.row_bytes : 0);
+    const uint64_t gmask = LPR == 64 ? ~0ull : ((1ull << LPR) - 1);
+    const uint64_t not_simple = (__ballot(li < BPG && !(one && in_range)) >> gbase) & gmask;
+    const uint32_t vbits = (uint32_t)((__ballot(li < BPG && valid) >> gbase) & ((1ull << BPG) - 1));
+    if (not_simple != 0 || nb != BPG) {
+        chunk_general<D, BF16>(a, s_chunks, jb, nb, li);
+        return;
+    }
+    u32x4 q[BPG];
 #pragma unroll
-                    for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-                    for (int64_t i = s0; i < e0; ++i) {
-                        const int64_t rr = a.row_off[i];
-                        if (rr >= a.capacity) {
-                            if (li == 0) flag_bad(a);
-                        } else if (rr >= 0) {
-                            widen_add<BF16>(acc, *reinterpret_cast<const uint4*>(a.rv.row(s_chunks, rr) + li * 16));
-                        }
-                    }
-                    store_out<VEC>(a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC, acc, (double)(e0 - s0),
-                                   a.mean);
-                }
-                if (++b == (uint32_t)a.batch) {
-                    b = 0;
-                    ++t;
-                }
-            }
+    for (int k = 0; k < BPG; ++k) {
+        const uint64_t pk = __shfl(p, gbase + k, WAVE);
+        q[k] = gload_u4(reinterpret_cast<const char*>(pk) + li * 16);
+    }
+    uint64_t t = (uint64_t)jb / (uint64_t)a.batch;
+    uint64_t b = (uint64_t)jb - t * (uint64_t)a.batch;
+#pragma unroll
+    for (int k = 0; k < BPG; ++k) {
+        float* dst = a.out + ((int64_t)b * a.n_tables + (int64_t)t) * D + li * VEC;
+        const bool v = (vbits >> k) & 1u;
+        if (!BF16) {
+            const u32x4 w = v ? q[k] : u32x4{0u, 0u, 0u, 0u};
+            __builtin_nontemporal_store(f32x4{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                              __uint_as_float(w.w)},
+                                        (RSE_GLOBAL f32x4*)dst);
+        } else {
+            const u32x4 w = v ? q[k] : u32x4{0u, 0u, 0u, 0u};
+            __builtin_nontemporal_store(f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)},
+                                        (RSE_GLOBAL f32x4*)dst);
+            __builtin_nontemporal_store(f32x4{__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                                              __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u)},
+                                        (RSE_GLOBAL f32x4*)(dst + 4));
+        }
+        if (++b == (uint64_t)a.batch) {
+            b = 0;
+            ++t;
         }
     }
 }
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
         for (int64_t i = bag_start; i < last; i += UNROLL) {
             int64_t r[UNROLL];
             bool v[UNROLL];
-            uint4 q[UNROLL];
+            u32x4 q[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 r[u] = a.row_off[i + u < last ? i + u : last - 1];
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
             if (can_load) {
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
-                    q[u] = *reinterpret_cast<const uint4*>((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
+                    q[u] = gload_u4((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
         for (int64_t i = s + g; i < e; i += (int64_t)GROUPS * UNROLL) {
             int64_t r[UNROLL];
             bool v[UNROLL];
-            uint4 q[UNROLL];
+            u32x4 q[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int64_t ii = i + (int64_t)u * GROUPS;
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
             if (can_load) {
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
-                    q[u] = *reinterpret_cast<const uint4*>((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
+                    q[u] = gload_u4((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
                     if (v[u]) widen_add<BF16>(acc, q[u]);
@@ -361,12 +368,18 @@ int launch_fwd(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
     if (avg >= 2.0 * G::GROUPS && G::GROUPS > 1) {
         const int blocks = fill_blocks(a.n_bags, WAVES, 256 * 32);
         hipLaunchKernelGGL((k_fwd_wave<D, BF16, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
-    } else if (avg <= 1.5) {
-        // one-hot: a group owns BPG bags, their first rows all in flight
-        constexpr int BPG = RSE_FWD_ONEHOT_BPG;
-        const int64_t groups = (a.n_bags + BPG - 1) / BPG;
-        const int blocks = fill_blocks(groups, WAVES * G::GROUPS, 256 * 32);
-        hipLaunchKernelGGL((k_fwd_onehot<D, BF16, BPG>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
+    } else if (avg <= 1.5 && n_ids > 0 && a.capacity > 0) {
+        // one-hot: one chunk of BPG bags per group, all its rows in flight
+        constexpr int BPG = G::LPR < RSE_FWD_ONEHOT_BPG ? G::LPR : RSE_FWD_ONEHOT_BPG;
+        const int64_t chunks = (a.n_bags + BPG - 1) / BPG;
+        const int64_t per_block = WAVES * G::GROUPS;
+        const int64_t blocks = (chunks + per_block - 1) / per_block;
+        if (blocks > 0x7FFFFFFFll) return RSE_ERR_INVALID_ARG;
+        if (a.rv.n_chunks <= LDS_CHUNKS)
+            hipLaunchKernelGGL((k_fwd_onehot<D, BF16, BPG, true>), dim3((unsigned)blocks), dim3(FWD_BLOCK), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_fwd_onehot<D, BF16, BPG, false>), dim3((unsigned)blocks), dim3(FWD_BLOCK), 0, s,
+                               a);
     } else {
         constexpr int BPG = 4;
         const int64_t groups = (a.n_bags + BPG - 1) / BPG;

@@ -568,7 +568,7 @@ __global__ void k_init_rows(RowsView rv, int dim, int64_t row_bytes, uint64_t se
         const uint64_t r = e / (uint64_t)q_per_row;
         const int64_t qi = (int64_t)(e - r * (uint64_t)q_per_row);
         char* row = rv.row((int64_t)(used + r));
-        uint4 out = make_uint4(0, 0, 0, 0);
+        u32x4 out = u32x4{0u, 0u, 0u, 0u};
         if (qi < w_q) {
             const uint64_t key = ws.new_key[r];
             const uint32_t tab = ws.new_tab[r];
@@ -585,9 +585,9 @@ __global__ void k_init_rows(RowsView rv, int dim, int64_t row_bytes, uint64_t se
                     wv[k] = lo | (hi << 16);
                 }
             }
-            out = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            out = u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
-        reinterpret_cast<uint4*>(row)[qi] = out;
+        gstore_u4(row + (int64_t)qi * 16, out);
     }
 }
 

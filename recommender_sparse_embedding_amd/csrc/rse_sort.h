@@ -5,7 +5,7 @@
 
 namespace rse_host {
 
-constexpr int SORT_TILE = 4096;      // keys per sort block (256 threads x 16)
+constexpr int SORT_TILE = 4096;      // keys per sort block (512 threads x 8)
 constexpr int SORT_MAX_PASSES = 4;   // 32-bit keys
 constexpr int SORT_MAX_BINS = 512;   // digits of up to 9 bits
 

@@ -8,7 +8,7 @@
 // by the pair-building kernel.  Per pass, each block:
 //   1. takes the next tile (4096 pairs) from an atomic counter, so every tile
 //      it may wait on belongs to a block that is already running;
-//   2. ranks the tile's keys stably: each wave owns 1024 consecutive pairs
+//   2. ranks the tile's keys stably: each wave owns 512 consecutive pairs
 //      and walks them 64 at a time, building a digit-match mask per lane from
 //      one ballot per digit bit and keeping wave-private running counts in
 //      LDS, so no block barrier is needed per row;
@@ -27,14 +27,15 @@ using namespace rse_host;
 
 namespace {
 
-constexpr int SB = 256;                         // threads per sort block
-constexpr int ITEMS = SORT_TILE / SB;           // 16 pairs per thread
+constexpr int SB = 512;                         // threads per sort block
+constexpr int ITEMS = SORT_TILE / SB;           // 8 pairs per thread
 constexpr int SWAVES = SB / WAVE;
-constexpr int PER_WAVE = SORT_TILE / SWAVES;    // 1024 consecutive pairs per wave
+constexpr int PER_WAVE = SORT_TILE / SWAVES;    // 512 consecutive pairs per wave
 constexpr uint32_t ST_AGG = 1u << 30;           // tile count published
 constexpr uint32_t ST_INC = 2u << 30;           // inclusive prefix published
 constexpr uint32_t ST_VAL = (1u << 30) - 1u;
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
+constexpr int LOOK = 8;                         // predecessors read per look-back step
 
 __device__ __forceinline__ uint32_t load_state(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -43,7 +44,7 @@ __device__ __forceinline__ void store_state(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exclusive scan over `bins` (<= 512) values, two per thread; returns through
+// Exclusive scan over `bins` (<= 512) values, up to two per thread; returns through
 // `out`; `tmp` holds SWAVES words.
 __device__ void block_scan_bins(const uint32_t* in, uint32_t* out, int bins, uint32_t* tmp) {
     const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
@@ -136,32 +137,52 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
     __syncthreads();
     block_scan_bins(s_cnt, s_pre, bins, s_tmp);
     block_scan_bins(totals, s_base, bins, s_tmp);
-    // 3. decoupled look-back per digit
+    // 3. decoupled look-back per digit, LOOK predecessors read at once: their
+    // counts are added newest first until an inclusive prefix is found
+    // (tile 0 always publishes one, so the walk ends); a predecessor that
+    // has published nothing yet is polled again.
     for (int d = tid; d < bins; d += SB) {
         uint32_t ex = 0;
         if (tile > 0) {
-            int64_t t = (int64_t)tile - 1;
+            int64_t t = (int64_t)tile - 1;      // newest predecessor not yet added
             uint32_t spins = 0;
+            bool timed_out = false;
             while (true) {
-                const uint32_t st = load_state(&state[t * SORT_MAX_BINS + d]);
-                if (st & ST_INC) {
-                    ex += st & ST_VAL;
-                    break;
+                uint32_t st[LOOK];
+#pragma unroll
+                for (int u = 0; u < LOOK; ++u) {
+                    const int64_t tt = t - u >= 0 ? t - u : 0;
+                    st[u] = load_state(&state[tt * SORT_MAX_BINS + d]);
                 }
-                if (st & ST_AGG) {
-                    ex += st & ST_VAL;
-                    --t;                        // tile 0 always publishes inclusive
-                    continue;
+                bool done = false, stall = false;
+                int used = 0;
+#pragma unroll
+                for (int u = 0; u < LOOK; ++u) {
+                    if (done || stall) continue;
+                    if (st[u] & ST_INC) {
+                        ex += st[u] & ST_VAL;
+                        done = true;
+                    } else if (st[u] & ST_AGG) {
+                        ex += st[u] & ST_VAL;
+                        ++used;
+                    } else {
+                        stall = true;
+                    }
                 }
-                ++spins;
-                if (spins > SPIN_LIMIT || ((spins & 1023u) == 0 && load_state(error))) {
-                    s_fail = 1;
-                    atomicExch(error, 1u);
-                    break;
+                if (done) break;
+                t -= used;
+                if (stall) {
+                    ++spins;
+                    if (spins > SPIN_LIMIT || ((spins & 1023u) == 0 && load_state(error))) {
+                        s_fail = 1;
+                        atomicExch(error, 1u);
+                        timed_out = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
                 }
-                __builtin_amdgcn_s_sleep(1);
             }
-            store_state(&state[(int64_t)tile * SORT_MAX_BINS + d], ST_INC | (ex + s_cnt[d]));
+            if (!timed_out) store_state(&state[(int64_t)tile * SORT_MAX_BINS + d], ST_INC | (ex + s_cnt[d]));
         }
         s_glob[d] = s_base[d] + ex;
     }

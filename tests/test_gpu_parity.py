@@ -22,8 +22,8 @@ def _say(*a):
 def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64, split=False):
     wl = synth.Workload(cfg)
     orc = make_oracle(cfg)
-    L_est = cfg.n_bags * (cfg.bag[2] if cfg.bag[0] == "uniform" else
-                          cfg.bag[1] * 2 if cfg.bag[0] == "poisson" else cfg.bag[1])
+    L_est = int(cfg.n_bags * (cfg.bag[2] if cfg.bag[0] == "uniform" else
+                              cfg.bag[1] * 3 if cfg.bag[0] == "poisson" else cfg.bag[1]))
     max_rows = int(wl.card.sum() if cfg.prepopulate else 0) + (max_new or L_est * steps) + 1024
     extra = (max_new or L_est * steps) if (cfg.fresh_frac > 0 or not cfg.prepopulate) else 0
     gpu = GpuTables(cfg, wl.card, max_rows, extra_keys=extra, split=split)
@@ -152,6 +152,45 @@ def test_forward_variants(dim, wdtype, pooling):
         run_steps(cfg, 1)
 
 
+@pytest.mark.parametrize("dim,wdtype", [(4, 0), (16, 0), (32, 1), (64, 0), (128, 0), (128, 1), (256, 0)])
+def test_forward_one_hot_chunks(dim, wdtype):
+    """One-hot batches take the chunked kernel: chunks that are wholly
+    one-hot (fast path), chunks holding an empty bag and a two-lookup bag,
+    the ragged last chunk (per-bag path), and ids not in the map (offset -1,
+    a zero row)."""
+    cfg = synth.config(2, n_tables=3, batch=301, dim=dim, wdtype=wdtype, cardinality=("fixed", 400))
+    wl = synth.Workload(cfg)
+    orc = make_oracle(cfg)
+    gpu = GpuTables(cfg, wl.card, int(wl.card.sum()) + 64)
+    for ids, bounds in wl.prepopulation():
+        orc.find_or_insert(ids, bounds, 1)
+        gpu.find_or_insert(ids, bounds, 1)
+    ids, bo = wl.batch_inputs(0)
+    assert np.array_equal(bo, np.arange(cfg.n_bags + 1))
+    bo = bo.copy()
+    for j in (17, 100, 640):            # bag j empty, bag j + 1 takes its lookup
+        bo[j + 1] = bo[j]
+    ids = ids.copy()
+    ids[[5, 200, 433]] = (1 << 62) + np.arange(3)          # never inserted
+    ro_r, _ = orc.find_or_insert(ids, bo, cfg.batch, insert_missing=False)
+    ro_g, _ = gpu.find_or_insert(ids, bo, cfg.batch, insert=False)
+    assert np.array_equal(ro_g.cpu().numpy(), ro_r) and (ro_r == -1).sum() >= 3
+    out_g = gpu.fwd(ro_g, bo).cpu().numpy()
+    out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
+    assert_close(out_g, out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol_for(wdtype), "one-hot pooled output")
+    for j in (17, 100, 640):
+        t, b = divmod(j, cfg.batch)
+        assert not out_g[b, t].any(), "empty bag"
+
+
+def test_forward_poisson_bags_per_bag_path():
+    """Bag lengths Poisson(1): the one-hot kernel is chosen (mean <= 1.5) and
+    most chunks fall back to the per-bag path."""
+    cfg = synth.config(1, n_tables=4, batch=500, dim=64, bag=("poisson", 1.0), cardinality=("fixed", 2000),
+                       prepopulate=True)
+    run_steps(cfg, 2)
+
+
 @pytest.mark.parametrize("optim", [0, 1, 2])
 @pytest.mark.parametrize("wdtype", [0, 1])
 def test_update_variants(optim, wdtype):
@@ -210,6 +249,83 @@ def test_split_backward_overlapping_forward(which):
         cfg = synth.config(3, n_tables=2, batch=512, dim=32, wdtype=1, optim=2, lr=1e-3,
                            cardinality=("fixed", 20000), bag=("uniform", 1, 40), fresh_frac=0.01, pooling=1)
         run_steps(cfg, 3, split=True)
+
+
+@pytest.mark.parametrize("which", ["click_log", "fresh_keys_adam"])
+def test_pipelined_next_find_overlaps_apply(which):
+    """The find and sort of batch s+1 on a second stream run while batch s's
+    forward and apply run on the first (the forward of s+1 waits for both):
+    every step matches the oracle run in plain order, including new keys
+    inserted while the previous batch's rows are being updated."""
+    if which == "click_log":
+        cfg = synth.config(2, batch=2048, cardinality=("loguniform", 10, 200_000))
+    else:
+        cfg = synth.config(3, n_tables=2, batch=512, dim=32, cardinality=("fixed", 20000), bag=("uniform", 1, 40),
+                           fresh_frac=0.05)
+    steps = 4
+    wl = synth.Workload(cfg)
+    orc = make_oracle(cfg)
+    L_max = max(len(wl.batch_inputs(s)[0]) for s in range(steps))
+    gpu = GpuTables(cfg, wl.card, int(wl.card.sum()) + L_max * steps + 1024, extra_keys=L_max * steps)
+    for ids, bounds in wl.prepopulation(100_000):
+        orc.find_or_insert(ids, bounds, 1)
+        gpu.find_or_insert(ids, bounds, 1)
+    rse = gpu.rse
+    dev = gpu.dev
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)
+    inputs = []
+    for s in range(steps):
+        ids, bo = wl.batch_inputs(s)
+        inputs.append(dict(ids=torch.from_numpy(ids).to(dev), bo=torch.from_numpy(bo).to(dev),
+                           ro=torch.empty(len(ids), dtype=torch.int64, device=dev),
+                           out=torch.empty((cfg.batch, cfg.n_tables, cfg.dim), dtype=torch.float32, device=dev),
+                           g=torch.from_numpy(wl.grad(s)).to(dev), nu=torch.zeros(1, dtype=torch.int64, device=dev)))
+    torch.cuda.synchronize()
+    ws = [rse.bwd_workspace(L_max, cfg.n_tables, cfg.batch, cfg.dim, dev) for _ in range(2)]
+    fws = gpu.map.workspace(L_max)
+    applied = [torch.cuda.Event(), torch.cuda.Event()]
+    fronted = [torch.cuda.Event(), torch.cuda.Event()]
+    plans = [None, None]
+    n_new = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def front(s):
+        x = inputs[s]
+        side.wait_event(applied[s % 2])
+        rse.idmap_find_or_insert(gpu.map, gpu.blocks, x["ids"], x["bo"], cfg.batch, cfg.n_tables, x["ro"], n_new,
+                                 ws=fws, stream=side)
+        plans[s % 2] = rse.embedding_bag_bwd_prepare(gpu.blocks, x["ro"], x["bo"], cfg.n_tables, cfg.batch,
+                                                     ws[s % 2], stream=side)
+        fronted[s % 2].record(side)
+
+    front(0)
+    for s in range(steps):
+        if s + 1 < steps:
+            front(s + 1)
+        x = inputs[s]
+        main.wait_event(fronted[s % 2])
+        rse.embedding_bag_fwd(gpu.blocks, x["ro"], x["bo"], cfg.n_tables, cfg.batch, cfg.pooling, x["out"])
+        rse.embedding_bag_bwd_apply(gpu.blocks, plans[s % 2], x["bo"], cfg.n_tables, cfg.batch, cfg.pooling,
+                                    x["g"], gpu.optim, s + 1, x["nu"], ws[s % 2])
+        applied[s % 2].record(main)
+    torch.cuda.synchronize()
+    touched = set()
+    for s in range(steps):
+        ids, bo = wl.batch_inputs(s)
+        ro_r, _ = orc.find_or_insert(ids, bo, cfg.batch)
+        assert np.array_equal(inputs[s]["ro"].cpu().numpy(), ro_r), f"row offsets, step {s}"
+        out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
+        assert_close(inputs[s]["out"].cpu().numpy(), out_r, pooled_magnitude(orc, ro_r, bo, cfg),
+                     rtol_for(cfg.wdtype), f"pooled output, step {s}")
+        U = orc.bwd_update(ro_r, bo, cfg.batch, wl.grad(s), cfg.pooling)
+        assert int(inputs[s]["nu"].item()) == U
+        touched |= set(np.unique(ro_r[ro_r >= 0]).tolist())
+    offs = np.array(sorted(touched), dtype=np.int64)
+    w_g, s_g = gpu.rows(offs)
+    w_r, s_r = orc.get_rows(offs)
+    assert_close(w_g, w_r, np.abs(w_r.astype(np.float64)) + 1e-3, rtol_for(cfg.wdtype), "rows after the steps")
+    if s_r.size:
+        assert_close(s_g, s_r, np.abs(s_r.astype(np.float64)) + 1e-30, 1e-5, "state after the steps")
 
 
 def _small_split_setup(rows_per_chunk_log2=4, n_chunks=1):
