@@ -202,12 +202,24 @@ class Workload:
 
     def batch_inputs(self, step: int):
         """ids int64[L], bag_offsets int64[T*B+1] for one step (step >= 0)."""
+        ids, _, bo = self._batch(step, as_counters=False)
+        return ids, bo
+
+    def batch_counters(self, step: int):
+        """The same step as generation counters: (counters uint64[L], table
+        int32[L], bag_offsets).  Lookup i's id is keys(table[i], counters[i]);
+        a prepopulated key's counter is its insertion index within its table."""
+        counters, table, bo = self._batch(step, as_counters=True)
+        return counters, table, bo
+
+    def _batch(self, step: int, as_counters: bool):
         cfg = self.cfg
         r = _rng(cfg.seed, 3, step)
         lens = self.bag_lengths(r)
         bo = np.zeros(cfg.n_bags + 1, np.int64)
         np.cumsum(lens, out=bo[1:])
-        ids = np.empty(int(bo[-1]), np.int64)
+        ids = np.empty(int(bo[-1]), np.uint64 if as_counters else np.int64)
+        table = np.empty(int(bo[-1]), np.int32) if as_counters else None
         for t in range(cfg.n_tables):
             a, b = int(bo[t * cfg.batch]), int(bo[(t + 1) * cfg.batch])
             n = b - a
@@ -224,8 +236,12 @@ class Workload:
                 pos = r.choice(n, n_fresh, replace=False)
                 start = int(self.card[t]) + step * FRESH_STRIDE
                 counters[pos] = np.arange(start, start + n_fresh, dtype=np.uint64)
-            ids[a:b] = self.keys(t, counters)
-        return ids, bo
+            if as_counters:
+                ids[a:b] = counters
+                table[a:b] = t
+            else:
+                ids[a:b] = self.keys(t, counters)
+        return ids, table, bo
 
     def grad(self, step: int, dtype=np.float32) -> np.ndarray:
         """Upstream gradient N(0,1), layout [batch, n_tables, dim]."""

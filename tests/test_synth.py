@@ -71,3 +71,23 @@ def test_prepopulation_pieces_cover_universe():
     assert np.array_equal(ids, whole[0][0])
     for pid, b in pieces:
         assert b[0] == 0 and b[-1] == len(pid)
+
+
+def test_batch_counters_describe_the_same_batch():
+    """batch_counters gives each lookup's table and generation counter: the
+    keys they map to are batch_inputs' ids, and prepopulated counters index
+    the universe (the insertion order)."""
+    for n, kw in ((2, dict(batch=64, cardinality=("fixed", 1000))), (3, dict(batch=32)),
+                  (5, dict(batch=16, n_tables=5, cardinality=("fixed", 1000)))):
+        cfg = synth.config(n, **kw)
+        wl = synth.Workload(cfg)
+        ids, bo = wl.batch_inputs(2)
+        counters, table, bo2 = wl.batch_counters(2)
+        assert np.array_equal(bo, bo2)
+        assert np.all(np.diff(table) >= 0)                      # table-major
+        keys = np.concatenate([wl.keys(t, counters[table == t]) for t in range(cfg.n_tables)])
+        assert np.array_equal(keys, ids)
+        old = counters < wl.card[table]
+        for t in range(cfg.n_tables):
+            m = old & (table == t)
+            assert np.array_equal(wl.universe(t)[counters[m].astype(np.int64)], ids[m])
