@@ -339,7 +339,7 @@ def main():
 
 
 # identifies the kernel source the stored traffic counters were taken on
-KERNEL_REV = "seg-v4"
+KERNEL_REV = "seg-v5"
 
 
 def read_traffic(name, rev):

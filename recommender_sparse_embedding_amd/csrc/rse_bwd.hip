@@ -15,18 +15,23 @@
 //   segmented reduction with the optimizer fused in -> combine of long
 //   segments.
 //
-// Segmented reduction.  The sorted lookups are cut into pieces of P = 64.
-// A segment (all lookups of one row) of length <= LONG_T = 128 is reduced
-// entirely by the group of lanes whose piece holds its first lookup, in
-// lookup order, in fp64, and the row is updated right there: the gradient
-// row never goes to memory.  A longer segment is reduced piecewise: every
-// piece it covers writes its fp64 partial to a carry slot, and the piece
-// holding its first lookup is listed as owner; the combine kernel adds the
-// partials in a fixed order (round-robin over a block's groups, then group
-// order) and updates the row.  Each block stages the keys and bag ids of its
-// pieces (plus LONG_T + 1 on either side) in LDS, so segment bounds are found
-// without global binary searches.  Only integer atomics (counters) are used;
-// results do not depend on timing.
+// Segmented reduction.  A segment is all lookups of one row (a run of the
+// sorted keys).  An index kernel classifies every segment once: one lookup,
+// 2..LONG_T lookups ("short"), or longer ("long", whose head is listed as
+// owner); the first two kinds go to lists.  The work kernel then runs three
+// kinds of blocks side by side:
+//   - long: the sorted lookups are cut into pieces of P = 64; each piece
+//     sums the part of a long segment it holds (at its start, continuing an
+//     earlier piece, and/or at its end, continuing past it) into a carry
+//     slot, 8 gradient rows in flight, in lookup order, in fp64;
+//   - singles: each group of lanes takes a few one-lookup segments and loads
+//     all their rows (weights + state) and gradient rows at once;
+//   - short: each group takes one short segment, loads its row, sums its
+//     gradient rows 8 at a time in lookup order, and updates the row.
+// The combine kernel adds each long segment's carries in a fixed order
+// (round-robin over a block's groups, then group order) and updates its row.
+// The lists' order depends on timing, but every segment is reduced and
+// updated independently, so results do not.  Only integer atomics are used.
 #include <cmath>
 
 #include "rse_sort.h"
@@ -45,10 +50,31 @@ struct OptParams {
     double lr, eps, b1, b2, omb1, omb2, bc1, bc2;
 };
 
-struct Ctr {                     // device counters of one call
-    unsigned long long n_owners;
+// Device counters of one call.  The three list lengths sit on separate
+// 128-byte lines: each index block adds to them once, and atomics on one
+// line serialise.
+struct Ctr {
     unsigned long long bad;
-    unsigned long long pad[6];
+    unsigned long long pad0[15];
+    unsigned long long n_single;  // one-lookup segments
+    unsigned long long pad1[15];
+    unsigned long long n_multi;   // segments of 2..LONG_T lookups
+    unsigned long long pad2[15];
+    unsigned long long n_owners;  // longer segments (their heads are listed in owners)
+    unsigned long long pad3[15];
+};
+
+constexpr int IX_BLOCK = 512;                      // index kernel: positions per block and thread
+constexpr int IX_TILE = 4096;
+constexpr int IX_PER = IX_TILE / IX_BLOCK;
+constexpr int IX_WIN = IX_TILE + HALO + 1;
+constexpr int IX_MASKS = (IX_WIN + 63) / 64;
+
+struct Multi {                   // a segment of 2..LONG_T lookups
+    uint32_t start;              // position of its first lookup in the sorted order
+    uint32_t len;
+    uint32_t key;                // its row
+    uint32_t pad;
 };
 
 struct BwdArgs {
@@ -62,11 +88,13 @@ struct BwdArgs {
     int32_t mean;
     int64_t n;                   // lookups (sorted pairs)
     uint32_t invalid;            // key of lookups without a row (sorted last)
-    int32_t n_seg_blocks;        // grid of the segmented-update kernel
+    int32_t l_blocks;            // work kernel: blocks [0, l_blocks) take long pieces,
+    int32_t s_blocks;            // the next s_blocks one-lookup segments, the rest short ones
     Ctr* ctr;
     double* carry;               // [n_pieces][2][dim]
     uint32_t* owners;            // head positions of long segments
-    uint32_t* blk_unique;        // rows finished per segmented-update block
+    uint2* singles;              // (row, gradient row) of one-lookup segments
+    Multi* multis;
     int64_t* n_unique;
     const uint32_t* sort_err;    // set if a radix pass timed out: nothing is updated
     int32_t* status;             // the blocks' sticky status
@@ -96,6 +124,8 @@ __global__ void k_bwd_reset(Ctr* ctr, SortPrep sp) {
 // Counters of one apply (so a prepared sort may be applied more than once).
 __global__ void k_apply_reset(Ctr* ctr, int64_t* n_unique) {
     if (threadIdx.x == 0) {
+        ctr->n_single = 0;
+        ctr->n_multi = 0;
         ctr->n_owners = 0;
         *n_unique = 0;
     }
@@ -338,19 +368,114 @@ __device__ __forceinline__ int prev_head(const unsigned long long* m, int x) {
     return (c << 6) + 63 - __clzll((long long)bits);
 }
 
-// One piece's lookups.  A long segment's part in the piece (at the start,
-// continuing an earlier piece, or at the end, continuing past it) is summed
-// as a plain run, 8 gradient rows in flight, into a carry slot.  The short
-// segments in between are walked CH lookups at a time: the CH gradient rows
-// and the rows (weights + state) of every segment starting among them are
-// loaded together, then consumed in order, and a segment is finished
-// (optimizer applied) at its last lookup, which may lie past the piece end.
-template <int D, bool BF16, int OPT, int NMASK>
-__device__ __forceinline__ void walk_piece(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
-                                           const unsigned long long* s_head, const uint64_t* s_chunks, int wn,
-                                           int64_t w0, int64_t k, int x0, int xb, int li, uint32_t& finished) {
+// ----------------------------------------------------------- index -------
+// Each block classifies the segments whose first lookup lies in its tile of
+// IX_TILE sorted positions.  It stages the tile's keys plus one position
+// before and HALO after (a segment of <= LONG_T lookups ends inside that
+// window; one reaching past it is long) and marks heads with one ballot per
+// 64 positions.  Each thread classifies IX_PER consecutive positions; a
+// block-wide exclusive scan of the per-thread counts (three 16-bit fields of
+// one 64-bit word) places the block's entries, and one atomic add per
+// non-empty list reserves them (the order of blocks in a list is not
+// fixed; nothing depends on it).
+__device__ __forceinline__ uint64_t block_scan_u64(uint64_t v, uint64_t* s_wsum, uint64_t* total) {
+    const int lane = lane_id(), w = threadIdx.x / WAVE;
+    uint64_t x = v;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint64_t y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) s_wsum[w] = x;
+    __syncthreads();
+    uint64_t pre = 0, all = 0;
+    for (int q = 0; q < IX_BLOCK / WAVE; ++q) {
+        if (q < w) pre += s_wsum[q];
+        all += s_wsum[q];
+    }
+    *total = all;
+    return pre + x - v;
+}
+
+__global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
+    __shared__ uint32_t s_keys[IX_WIN];
+    __shared__ unsigned long long s_head[IX_MASKS];
+    __shared__ uint64_t s_wsum[IX_BLOCK / WAVE];
+    __shared__ unsigned long long s_base[3];
+    if (a.ctr->bad || *a.sort_err) return;
+    const int64_t n = a.n;
+    const int64_t tile = blockIdx.x;
+    const int64_t t0 = tile * IX_TILE;
+    const int64_t t1 = t0 + IX_TILE < n ? t0 + IX_TILE : n;
+    const int64_t w0 = t0 > 0 ? t0 - 1 : 0;
+    const int64_t w1 = t1 + HALO < n ? t1 + HALO : n;
+    const int wn = (int)(w1 - w0);
+    const int lane = lane_id();
+    for (int q = threadIdx.x; q < wn; q += IX_BLOCK) s_keys[q] = a.keys[w0 + q];
+    __syncthreads();
+    for (int c = threadIdx.x / WAVE; c < IX_MASKS; c += IX_BLOCK / WAVE) {
+        const int q = c * 64 + lane;
+        const bool h = q < wn && (q == 0 ? w0 == 0 : s_keys[q] != s_keys[q - 1]);
+        const unsigned long long m = __ballot(h);
+        if (lane == 0) s_head[c] = m;
+    }
+    __syncthreads();
+    const int x_first = (int)(t0 - w0) + (int)threadIdx.x * IX_PER;
+    const int x_end = (int)(t1 - w0);
+    int cls[IX_PER];          // 0 one lookup, 1 short, 2 long, 3 none
+    int len[IX_PER];
+    uint64_t cnt = 0;         // per-class counts in 16-bit fields
+#pragma unroll
+    for (int u = 0; u < IX_PER; ++u) {
+        const int x = x_first + u;
+        cls[u] = 3;
+        len[u] = 0;
+        if (x < x_end && ((s_head[x >> 6] >> (x & 63)) & 1ull) && s_keys[x] != a.invalid) {
+            const int e = next_head<IX_MASKS>(s_head, x, wn);
+            const bool ends_here = e < wn || w1 == n;
+            const int l = e - x;
+            cls[u] = (!ends_here || l > LONG_T) ? 2 : (l == 1 ? 0 : 1);
+            len[u] = l;
+            cnt += 1ull << (16 * cls[u]);
+        }
+    }
+    uint64_t total = 0;
+    const uint64_t at = block_scan_u64(cnt, s_wsum, &total);
+    if (threadIdx.x == 0) {
+        const unsigned long long c0 = total & 0xFFFF, c1 = (total >> 16) & 0xFFFF, c2 = (total >> 32) & 0xFFFF;
+        s_base[0] = c0 ? atomicAdd(&a.ctr->n_single, c0) : 0;
+        s_base[1] = c1 ? atomicAdd(&a.ctr->n_multi, c1) : 0;
+        s_base[2] = c2 ? atomicAdd(&a.ctr->n_owners, c2) : 0;
+    }
+    __syncthreads();
+    uint64_t pos[3] = {s_base[0] + (at & 0xFFFF), s_base[1] + ((at >> 16) & 0xFFFF), s_base[2] + ((at >> 32) & 0xFFFF)};
+#pragma unroll
+    for (int u = 0; u < IX_PER; ++u) {
+        const int x = x_first + u;
+        const uint32_t p = (uint32_t)(w0 + x);
+        if (cls[u] == 0) {
+            a.singles[pos[0]++] = make_uint2(s_keys[x], a.vals[p]);
+        } else if (cls[u] == 1) {
+            Multi m;
+            m.start = p;
+            m.len = (uint32_t)len[u];
+            m.key = s_keys[x];
+            m.pad = 0;
+            a.multis[pos[1]++] = m;
+        } else if (cls[u] == 2) {
+            a.owners[pos[2]++] = p;
+        }
+    }
+}
+
+// ------------------------------------------------------------ work -------
+// Long role, one piece per group: the part of a long segment at the
+// piece's start (continuing an earlier piece) goes to carry slot 0, the part
+// of a long segment starting in the piece (continuing past it) to slot 1.
+template <int D, bool BF16, int NMASK>
+__device__ __forceinline__ void walk_long(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
+                                          const unsigned long long* s_head, int wn, int64_t k, int x0, int xb,
+                                          int li) {
     constexpr int VEC = Geo<D, BF16>::VEC;
-    constexpr int CH = 4;
     auto is_head = [&](int q) -> bool { return (s_head[q >> 6] >> (q & 63)) & 1ull; };
     auto carry = [&](int slot, const double* acc) {
         double* dst = a.carry + ((int64_t)k * 2 + slot) * D + li * VEC;
@@ -361,93 +486,105 @@ __device__ __forceinline__ void walk_piece(const BwdArgs& a, const uint32_t* s_k
     int lim = xb;
     if (s_keys[xb - 1] == a.invalid) lim = prev_head(s_head, xb - 1);
     if (lim <= x0) return;
-    int p = x0;
-    if (!is_head(p)) {
-        const int h = prev_head(s_head, p);
-        const int e = next_head<NMASK>(s_head, p, wn);
+    if (!is_head(x0)) {
+        const int h = prev_head(s_head, x0);
+        const int e = next_head<NMASK>(s_head, x0, wn);
         if (e - h > LONG_T) {
-            const int e2 = e < lim ? e : lim;
             double acc[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-            sum_range<D, BF16>(a, s_vals, p, e2, li, acc);
+            sum_range<D, BF16>(a, s_vals, x0, e < lim ? e : lim, li, acc);
             carry(0, acc);
-            p = e2;
-        } else {
-            p = e;                   // short: finished by the piece holding its head
         }
     }
-    if (p >= lim) return;
-    // the last segment starting in the piece: long (summed into slot 1) or
-    // short (the walk runs to its end)
     const int hl = prev_head(s_head, lim - 1);
-    const int el = next_head<NMASK>(s_head, hl, wn);
-    const bool tail_long = el - hl > LONG_T;
-    const int qend = tail_long ? hl : el;
-    double acc[VEC];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-    RowRegs<D, BF16> cur;
-    char* cur_row = nullptr;
-    int cur_end = p;
-    for (int q = p; q < qend; q += CH) {
-        float gv[CH][VEC];
-        uint32_t j[CH];
-        bool hd[CH];
-        RowRegs<D, BF16> rr[CH];
-        char* rp[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int qq = q + u < qend ? q + u : qend - 1;
-            j[u] = s_vals[qq];
-            hd[u] = q + u < qend && is_head(q + u);
-        }
-#pragma unroll
-        for (int u = 0; u < CH; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            rp[u] = nullptr;
-            if (hd[u]) {
-                rp[u] = a.rv.row(s_chunks, s_keys[q + u]);
-                load_row<D, BF16, OPT>(rp[u], li, rr[u]);
-            }
-        }
-        double len[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int x = q + u;
-            if (x < qend) {
-                if (hd[u]) {
-                    cur_end = next_head<NMASK>(s_head, x, wn);
-                    cur = rr[u];
-                    cur_row = rp[u];
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-                }
-                add_grad<VEC>(acc, gv[u], a.mean, len[u]);
-                if (x + 1 == cur_end) {
-                    finish_row<D, BF16, OPT>(a, cur_row, li, cur, acc);
-                    ++finished;
-                }
-            }
-        }
-    }
-    if (tail_long) {
+    if (hl >= x0 && next_head<NMASK>(s_head, hl, wn) - hl > LONG_T) {
+        double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
         sum_range<D, BF16>(a, s_vals, hl, xb, li, acc);
         carry(1, acc);
-        if (li == 0) {
-            const unsigned long long pos = atomicAdd(&a.ctr->n_owners, 1ull);
-            a.owners[pos] = (uint32_t)(w0 + hl);
+    }
+}
+
+// Singles role: SPG one-lookup segments per group, their rows and gradient
+// rows all requested before any is used.
+template <int D, bool BF16, int OPT, int SPG>
+__device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
+                                             int64_t n_groups, int li) {
+    constexpr int VEC = Geo<D, BF16>::VEC;
+    const int64_t ns = (int64_t)a.ctr->n_single;
+    for (int64_t i0 = gid * SPG; i0 < ns; i0 += n_groups * SPG) {
+        uint2 e[SPG];
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) e[u] = a.singles[i0 + u < ns ? i0 + u : ns - 1];
+        char* rp[SPG];
+        RowRegs<D, BF16> rr[SPG];
+        float gv[SPG][VEC];
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) {
+            rp[u] = a.rv.row(s_chunks, e[u].x);
+            load_row<D, BF16, OPT>(rp[u], li, rr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, e[u].y, li));
+        double len[SPG];
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) len[u] = a.mean ? bag_len(a, e[u].y) : 1.0;
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) {
+            if (i0 + u < ns) {
+                double acc[VEC];
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+                add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+                finish_row<D, BF16, OPT>(a, rp[u], li, rr[u], acc);
+            }
         }
     }
 }
 
+// Short role: one segment of 2..LONG_T lookups per group; its row is
+// requested with its first gradient rows, which are summed U at a time.
 template <int D, bool BF16, int OPT>
-__global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a) {
+__device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
+                                            int64_t n_groups, int li) {
+    constexpr int VEC = Geo<D, BF16>::VEC;
+    constexpr int U = 8;
+    const int64_t nm = (int64_t)a.ctr->n_multi;
+    for (int64_t i = gid; i < nm; i += n_groups) {
+        const Multi m = a.multis[i];
+        char* rp = a.rv.row(s_chunks, m.key);
+        RowRegs<D, BF16> rr;
+        load_row<D, BF16, OPT>(rp, li, rr);
+        double acc[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+        for (uint32_t c0 = 0; c0 < m.len; c0 += U) {
+            uint32_t j[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) j[u] = a.vals[m.start + (c0 + u < m.len ? c0 + u : m.len - 1)];
+            float gv[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
+            double len[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u < m.len) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+        }
+        finish_row<D, BF16, OPT>(a, rp, li, rr, acc);
+    }
+}
+
+template <int D, bool BF16>
+constexpr int singles_per_group() {
+    return 4;
+}
+
+template <int D, bool BF16, int OPT>
+__global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int LPR = G::LPR, GPB = G::GPB, WIN = G::WIN;
     constexpr int NMASK = (WIN + 63) / 64;
@@ -455,23 +592,32 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a)
     __shared__ uint32_t s_vals[WIN];
     __shared__ unsigned long long s_head[NMASK];
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
-    __shared__ uint32_t s_done;
     stage_chunks(s_chunks, a.rv);
-    if (threadIdx.x == 0) s_done = 0;
     if (a.ctr->bad) return;
     if (*a.sort_err) {
         if (blockIdx.x == 0 && threadIdx.x == 0) atomicCAS(a.status, 0, (int32_t)RSE_ERR_HIP);
         return;
     }
-    const int64_t n = a.n;
-    const int64_t n_pieces = (n + P - 1) / P;
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
+    const int blk = (int)blockIdx.x;
+    if (blk >= a.l_blocks) {
+        const int sb = blk - a.l_blocks;
+        if (sb < a.s_blocks) {
+            role_singles<D, BF16, OPT, singles_per_group<D, BF16>()>(
+                a, s_chunks, (int64_t)sb * GPB + g, (int64_t)a.s_blocks * GPB, li);
+        } else {
+            const int mb = sb - a.s_blocks;
+            const int m_blocks = (int)gridDim.x - a.l_blocks - a.s_blocks;
+            role_multis<D, BF16, OPT>(a, s_chunks, (int64_t)mb * GPB + g, (int64_t)m_blocks * GPB, li);
+        }
+        return;
+    }
+    const int64_t n = a.n;
+    const int64_t n_pieces = (n + P - 1) / P;
     const int lane = lane_id();
     const int wave = threadIdx.x / WAVE;
-    uint32_t finished = 0;
-
-    for (int64_t pb = (int64_t)blockIdx.x * GPB; pb < n_pieces; pb += (int64_t)gridDim.x * GPB) {
+    for (int64_t pb = (int64_t)blk * GPB; pb < n_pieces; pb += (int64_t)a.l_blocks * GPB) {
         const int64_t blk_a = pb * P;
         const int64_t blk_b = (pb + GPB) * P < n ? (pb + GPB) * P : n;
         const int64_t w0 = blk_a - HALO > 0 ? blk_a - HALO : 0;
@@ -496,12 +642,8 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a)
         if (k >= n_pieces) continue;
         const int x0 = (int)(k * P - w0);
         const int xb = (int)((k * P + P < n ? k * P + P : n) - w0);
-        walk_piece<D, BF16, OPT, NMASK>(a, s_keys, s_vals, s_head, s_chunks, wn, w0, k, x0, xb, li, finished);
+        walk_long<D, BF16, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
     }
-    // rows finished by this block (one LDS add per group), no global atomics
-    if (li == 0 && finished) atomicAdd(&s_done, finished);
-    __syncthreads();
-    if (threadIdx.x == 0) a.blk_unique[blockIdx.x] = s_done;
 }
 
 // ------------------------------------------------- long segment combine --
@@ -510,8 +652,10 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_update(BwdArgs a)
 // whose first key is still the segment's (slot 0); they form a prefix, so
 // one block-wide count per 2^8 pieces finds the last one.  Partials are added
 // round-robin per group (U loads in flight, added in piece order) then in
-// group order, so the sum is the same on every run.  Block 0 also totals the
-// distinct rows.  512 threads: the longest segment's partials are read in a
+// group order, so the sum is the same on every run.  Block 0 also writes the
+// number of distinct rows (one-lookup + short + long segments).  The row
+// address is read from the global chunk table (one row per block, nothing
+// staged in LDS).  512 threads: the longest segment's partials are read in a
 // few rounds.
 constexpr int COMBINE_BLOCK = 512;
 
@@ -521,38 +665,15 @@ __global__ __launch_bounds__(COMBINE_BLOCK) void k_combine(BwdArgs a) {
     constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = COMBINE_BLOCK, GPB = BLOCK / LPR;
     constexpr int U = 4;
     __shared__ double s_part[GPB][D];
-    __shared__ uint64_t s_chunks[LDS_CHUNKS];
-    __shared__ unsigned long long s_sum[BLOCK / WAVE];
-    stage_chunks(s_chunks, a.rv);
     if (a.ctr->bad || *a.sort_err) return;
-    const int64_t n_owners = (int64_t)a.ctr->n_owners;
     const int64_t n_pieces = (a.n + P - 1) / P;
+    const int64_t n_owners = (int64_t)a.ctr->n_owners;
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
-    if (blockIdx.x == 0) {
-        unsigned long long c = 0;
-        const int nb = a.n_seg_blocks;
-        for (int b0 = 0; b0 < nb; b0 += 8 * BLOCK) {
-            uint32_t v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int b = b0 + u * BLOCK + (int)threadIdx.x;
-                v[u] = a.blk_unique[b < nb ? b : nb - 1];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (b0 + u * BLOCK + (int)threadIdx.x < nb) c += v[u];
-        }
-        for (int o = WAVE / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, WAVE);
-        if (lane_id() == 0) s_sum[threadIdx.x / WAVE] = c;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            unsigned long long t = (unsigned long long)n_owners;
-            for (int w = 0; w < BLOCK / WAVE; ++w) t += s_sum[w];
-            *a.n_unique = (int64_t)t;
-        }
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *a.n_unique = (int64_t)(a.ctr->n_single + a.ctr->n_multi + (unsigned long long)n_owners);
     for (int64_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
+        __syncthreads();       // s_part of the previous owner has been read
         const int64_t h = a.owners[o];
         const uint32_t key = a.keys[h];
         const int64_t k0 = h / P;
@@ -593,12 +714,11 @@ __global__ __launch_bounds__(COMBINE_BLOCK) void k_combine(BwdArgs a) {
             for (int q = 1; q < GPB; ++q)
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) tot[c] += s_part[q][li * VEC + c];
-            char* row = a.rv.row(s_chunks, key);
+            char* row = a.rv.row(key);
             RowRegs<D, BF16> rr;
             load_row<D, BF16, OPT>(row, li, rr);
             finish_row<D, BF16, OPT>(a, row, li, rr, tot);
         }
-        __syncthreads();       // s_part is reused by the next owner
     }
 }
 
@@ -611,7 +731,8 @@ struct BwdWs {
     uint32_t* v1;
     double* carry;
     uint32_t* owners;
-    uint32_t* blk_unique;
+    uint2* singles;
+    Multi* multis;
     void* sort_ws;
 };
 
@@ -626,8 +747,9 @@ BwdWs carve(void* base, int64_t n_ids, int32_t dim, size_t* total) {
     w.k1 = c.take<uint32_t>(n);
     w.v1 = c.take<uint32_t>(n);
     w.carry = c.take<double>(n_pieces * 2 * (size_t)dim);
-    w.owners = c.take<uint32_t>(n_pieces);
-    w.blk_unique = c.take<uint32_t>(MAX_SEG_BLOCKS);
+    w.owners = c.take<uint32_t>(n / (LONG_T + 1) + 1);
+    w.singles = c.take<uint2>(n);
+    w.multis = c.take<Multi>(n / 2 + 1);
     w.sort_ws = c.take<char>(sort_workspace((int64_t)n, nullptr));
     if (total) *total = c.size();
     return w;
@@ -637,13 +759,20 @@ template <int D, bool BF16, int OPT>
 int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     using G = Geo<D, BF16>;
     const int64_t n_pieces = (n_ids + P - 1) / P;
-    const int blocks = fill_blocks(n_pieces, G::GPB, MAX_SEG_BLOCKS);
-    a.n_seg_blocks = blocks;
+    const int64_t ix_blocks = (n_ids + IX_TILE - 1) / IX_TILE;
+    hipLaunchKernelGGL(k_seg_index, dim3((unsigned)ix_blocks), dim3(IX_BLOCK), 0, s, a);
+    // long pieces: one block per GPB pieces; one-lookup and short segments:
+    // grid-stride pools (their counts are only known on the device), sized
+    // for a few passes when one lookup in ~16 starts a segment
+    a.l_blocks = fill_blocks(n_pieces, G::GPB, MAX_SEG_BLOCKS);
+    a.s_blocks = fill_blocks(n_ids, G::GPB * singles_per_group<D, BF16>() * 8, 2048);
+    const int m_blocks = fill_blocks(n_ids, G::GPB * 16, 2048);
+    const int64_t work_blocks = (int64_t)a.l_blocks + a.s_blocks + m_blocks;
+    const int cblocks = fill_blocks(n_pieces, 1, 2048);
     {
         TraceScope ts(RSE_K_SEG_UPDATE, s);
-        hipLaunchKernelGGL((k_seg_update<D, BF16, OPT>), dim3(blocks), dim3(G::BLOCK), 0, s, a);
+        hipLaunchKernelGGL((k_seg_work<D, BF16, OPT>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s, a);
     }
-    const int cblocks = fill_blocks(n_pieces, 1, 2048);
     {
         TraceScope ts(RSE_K_COMBINE, s);
         hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(COMBINE_BLOCK), 0, s, a);
@@ -769,11 +898,13 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
     a.mean = pooling == RSE_MEAN;
     a.n = n_ids;
     a.invalid = plan->invalid;
-    a.n_seg_blocks = 0;
+    a.l_blocks = 0;
+    a.s_blocks = 0;
     a.ctr = w.ctr;
     a.carry = w.carry;
     a.owners = w.owners;
-    a.blk_unique = w.blk_unique;
+    a.singles = w.singles;
+    a.multis = w.multis;
     a.n_unique = d_n_unique_out;
     a.sort_err = sp.error;
     a.status = &blocks->header()->status;
