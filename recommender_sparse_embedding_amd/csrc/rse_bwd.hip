@@ -580,7 +580,7 @@ __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_
 
 template <int D, bool BF16>
 constexpr int singles_per_group() {
-    return 4;
+    return 2;
 }
 
 template <int D, bool BF16, int OPT>
@@ -600,16 +600,25 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     }
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
-    const int blk = (int)blockIdx.x;
-    if (blk >= a.l_blocks) {
-        const int sb = blk - a.l_blocks;
-        if (sb < a.s_blocks) {
+    // roles are spread evenly over the block index (blocks start roughly in
+    // index order), so gathers of long pieces and row updates of short
+    // segments run side by side: block b is the floor(b*l/total)-th long
+    // block if that count steps at b, else a one-lookup or short block,
+    // spread the same way among the rest
+    const int64_t total = gridDim.x;
+    const int64_t b = blockIdx.x;
+    const int64_t lb = b * a.l_blocks / total, lb1 = (b + 1) * a.l_blocks / total;
+    const int blk = (int)lb;
+    if (lb1 == lb) {
+        const int64_t rest = total - a.l_blocks;
+        const int64_t r = b - lb1;
+        const int64_t sb = r * a.s_blocks / rest, sb1 = (r + 1) * a.s_blocks / rest;
+        if (sb1 > sb) {
             role_singles<D, BF16, OPT, singles_per_group<D, BF16>()>(
-                a, s_chunks, (int64_t)sb * GPB + g, (int64_t)a.s_blocks * GPB, li);
+                a, s_chunks, sb * GPB + g, (int64_t)a.s_blocks * GPB, li);
         } else {
-            const int mb = sb - a.s_blocks;
-            const int m_blocks = (int)gridDim.x - a.l_blocks - a.s_blocks;
-            role_multis<D, BF16, OPT>(a, s_chunks, (int64_t)mb * GPB + g, (int64_t)m_blocks * GPB, li);
+            const int64_t m_blocks = rest - a.s_blocks;
+            role_multis<D, BF16, OPT>(a, s_chunks, (r - sb1) * GPB + g, m_blocks * GPB, li);
         }
         return;
     }
