@@ -214,6 +214,8 @@ def main():
     def batch_at(k):
         return batches[k % len(batches)]
 
+    host_ms = {}      # host time to enqueue one step, per schedule
+
     def timed(schedule, first, n, evs=None):
         """n steps over batches first.., timed between events on stream 1
         (every stream's work inside is waited for); returns ms."""
@@ -223,6 +225,7 @@ def main():
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
+        h0 = time.perf_counter()
         for k in range(n):
             i = first + k
             if schedule == "serial":
@@ -235,6 +238,7 @@ def main():
         if schedule == "pipelined":
             stream.wait_event(fronted[(first + n) % 2])
         t1.record(stream)
+        host_ms[schedule] = (time.perf_counter() - h0) * 1e3 / max(n, 1)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
 
@@ -328,6 +332,7 @@ def main():
                                   "(stream 2)"}[schedule],
         "ms_per_step_by_schedule": {"serial": round(ms_serial, 4), "overlap": round(ms_overlap, 4),
                                     "pipelined": round(ms_step, 4) if schedule == "pipelined" else None},
+        "host_enqueue_ms_per_step": {k: round(v, 4) for k, v in host_ms.items()},
         "overlap_phase_ms": {"find": round(float(t_find), 4), "fwd": round(float(t_fwd), 4),
                              "bwd_update": round(float(t_bwd), 4)},
         "wall_s": round(wall, 4),

@@ -281,8 +281,9 @@ int embedding_bag_bwd_update(rse_blocks* blocks, const int64_t* d_row_off, int64
  * embedding_bag_bwd_update in two halves, so that the half that does not need
  * the gradient can run while the forward does (same passages as above).
  *
- * embedding_bag_bwd_prepare validates the bag offsets and row offsets and
- * sorts the lookups by row into d_ws; it reads only d_row_off and
+ * embedding_bag_bwd_prepare validates the bag offsets and row offsets,
+ * sorts the lookups by row into d_ws and indexes the runs of equal rows
+ * (one-lookup, short and long segments); it reads only d_row_off and
  * d_bag_offsets, so it may run on another stream concurrently with
  * embedding_bag_fwd of the same batch (the caller orders it after the
  * find-or-insert that wrote d_row_off).  *plan_out (host memory, caller

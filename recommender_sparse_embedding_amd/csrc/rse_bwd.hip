@@ -10,10 +10,9 @@
 //   prepare (needs only the row offsets and bag offsets, so it can overlap
 //   the forward):  reset -> pairs: (row, bag) per lookup, row as a 32-bit
 //   key (-1 -> a key above every row, sorted last) -> stable radix sort by
-//   row;
-//   apply (needs the upstream gradient):  reset of its counters ->
-//   segmented reduction with the optimizer fused in -> combine of long
-//   segments.
+//   row -> index of the segments (runs of equal rows);
+//   apply (needs the upstream gradient):  segmented reduction with the
+//   optimizer fused in -> combine of long segments.
 //
 // Segmented reduction.  A segment is all lookups of one row (a run of the
 // sorted keys).  An index kernel classifies every segment once: one lookup,
@@ -113,22 +112,19 @@ struct Geo {
 // ------------------------------------------------------------- pairs -----
 __global__ void k_bwd_reset(Ctr* ctr, SortPrep sp) {
     if (threadIdx.x == 0) {
-        ctr->n_owners = 0;
         ctr->bad = 0;
+        ctr->n_single = 0;
+        ctr->n_multi = 0;
+        ctr->n_owners = 0;
         *sp.error = 0;
     }
     if (threadIdx.x < SORT_MAX_PASSES) sp.tile_ctr[threadIdx.x] = 0;
     for (int k = threadIdx.x; k < SORT_MAX_PASSES * SORT_MAX_BINS; k += blockDim.x) sp.totals[k] = 0;
 }
 
-// Counters of one apply (so a prepared sort may be applied more than once).
-__global__ void k_apply_reset(Ctr* ctr, int64_t* n_unique) {
-    if (threadIdx.x == 0) {
-        ctr->n_single = 0;
-        ctr->n_multi = 0;
-        ctr->n_owners = 0;
-        *n_unique = 0;
-    }
+// An apply with no lookups still reports its distinct-row count (0).
+__global__ void k_zero_count(int64_t* n_unique) {
+    if (threadIdx.x == 0) *n_unique = 0;
 }
 
 // One thread per bag: key = row (or `invalid`), value = bag.  Malformed bag
@@ -674,7 +670,10 @@ __global__ __launch_bounds__(COMBINE_BLOCK) void k_combine(BwdArgs a) {
     constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = COMBINE_BLOCK, GPB = BLOCK / LPR;
     constexpr int U = 4;
     __shared__ double s_part[GPB][D];
-    if (a.ctr->bad || *a.sort_err) return;
+    if (a.ctr->bad || *a.sort_err) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_unique = 0;    // nothing was updated
+        return;
+    }
     const int64_t n_pieces = (a.n + P - 1) / P;
     const int64_t n_owners = (int64_t)a.ctr->n_owners;
     const int g = threadIdx.x / LPR;
@@ -768,8 +767,6 @@ template <int D, bool BF16, int OPT>
 int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     using G = Geo<D, BF16>;
     const int64_t n_pieces = (n_ids + P - 1) / P;
-    const int64_t ix_blocks = (n_ids + IX_TILE - 1) / IX_TILE;
-    hipLaunchKernelGGL(k_seg_index, dim3((unsigned)ix_blocks), dim3(IX_BLOCK), 0, s, a);
     // long pieces: one block per GPB pieces; one-lookup and short segments:
     // grid-stride pools (their counts are only known on the device), sized
     // for a few passes when one lookup in ~16 starts a segment
@@ -867,6 +864,19 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
         const int rc = radix_sort_pairs(w.k0, w.v0, w.k1, w.v1, n_ids, bits, w.sort_ws, &alt, s);
         if (rc) return rc;
         plan.sorted_in_alt = alt ? 1 : 0;
+        // the segment index needs only the sorted pairs
+        BwdArgs ia = {};
+        ia.keys = alt ? w.k1 : w.k0;
+        ia.vals = alt ? w.v1 : w.v0;
+        ia.n = n_ids;
+        ia.invalid = invalid;
+        ia.ctr = w.ctr;
+        ia.sort_err = sp.error;
+        ia.owners = w.owners;
+        ia.singles = w.singles;
+        ia.multis = w.multis;
+        const int64_t ix_blocks = (n_ids + IX_TILE - 1) / IX_TILE;
+        hipLaunchKernelGGL(k_seg_index, dim3((unsigned)ix_blocks), dim3(IX_BLOCK), 0, s, ia);
     }
     const int rc = launch_status();
     if (rc == RSE_OK) *plan_out = plan;
@@ -893,8 +903,10 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     SortPrep sp = sort_prep(w.sort_ws, n_ids);
-    hipLaunchKernelGGL(k_apply_reset, dim3(1), dim3(64), 0, s, w.ctr, d_n_unique_out);
-    if (n_ids == 0 || n_bags == 0) return launch_status();
+    if (n_ids == 0 || n_bags == 0) {
+        hipLaunchKernelGGL(k_zero_count, dim3(1), dim3(64), 0, s, d_n_unique_out);
+        return launch_status();
+    }
 
     BwdArgs a;
     a.rv = blocks->view();
