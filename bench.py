@@ -211,6 +211,31 @@ def main():
                                     ws2[i % 2])
         applied[i % 2].record(stream)
 
+    # "staggered": stream 2 sorts batch i while stream 1 runs its forward,
+    # then finds batch i+1 while stream 1 runs batch i's apply (the radix
+    # passes slow the segmented update down when they share the GPU with it,
+    # less so the forward).  Same per-step work and dependencies as above.
+    found = [torch.cuda.Event(), torch.cuda.Event()]
+    sorted_ = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def find_ahead(i, b):
+        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws, stream=side)
+        found[i % 2].record(side)
+
+    def staggered_step(i, b, b_next):
+        side.wait_event(applied[(i + 1) % 2])         # apply(i-1) is done: stream 1 starts forward(i)
+        plans[i % 2] = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, ws2[i % 2], stream=side)
+        sorted_[i % 2].record(side)
+        find_ahead(i + 1, b_next)
+        stream.wait_event(found[i % 2])
+        rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
+        g = grad_of(b)
+        step_no[0] += 1
+        stream.wait_event(sorted_[i % 2])
+        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+                                    ws2[i % 2])
+        applied[i % 2].record(stream)
+
     def batch_at(k):
         return batches[k % len(batches)]
 
@@ -222,6 +247,8 @@ def main():
         torch.cuda.synchronize()
         if schedule == "pipelined":
             front(first, batch_at(first))
+        if schedule == "staggered":
+            find_ahead(first, batch_at(first))
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
@@ -232,18 +259,22 @@ def main():
                 step_serial(batch_at(i))
             elif schedule == "overlap":
                 step_overlap(batch_at(i), evs[k] if evs else None)
+            elif schedule == "staggered":
+                staggered_step(i, batch_at(i), batch_at(i + 1))
             else:
                 front(i + 1, batch_at(i + 1))      # the next batch: one find + sort per step
                 back(i, batch_at(i))
         if schedule == "pipelined":
             stream.wait_event(fronted[(first + n) % 2])
+        if schedule == "staggered":
+            stream.wait_event(found[(first + n) % 2])
         t1.record(stream)
         host_ms[schedule] = (time.perf_counter() - h0) * 1e3 / max(n, 1)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
 
     schedule = "serial" if args.serial_bwd else ("pipelined" if len(batches) >= 2 else "overlap")
-    for name in ("serial", "overlap", schedule):
+    for name in ("serial", "overlap", "staggered", schedule):
         timed(name, 0, args.warmup)
     used, st = blk.status()
     assert st == 0, st
@@ -266,6 +297,7 @@ def main():
     t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     rse.trace_start(rse.K_FWD)
     ms_serial = timed("serial", args.warmup, args.steps) / args.steps
+    ms_stag = timed("staggered", args.warmup, args.steps) / args.steps if len(batches) >= 2 else None
     n_fwd, fwd_ms = rse.trace_stop()
     t_fwd_kernel = fwd_ms / max(n_fwd, 1)
     idm_st, _ = idm.status()
@@ -331,6 +363,7 @@ def main():
                      "pipelined": "fwd + bwd apply of batch i (stream 1) || find + bwd prepare of batch i+1 "
                                   "(stream 2)"}[schedule],
         "ms_per_step_by_schedule": {"serial": round(ms_serial, 4), "overlap": round(ms_overlap, 4),
+                                    "staggered": round(ms_stag, 4) if ms_stag else None,
                                     "pipelined": round(ms_step, 4) if schedule == "pipelined" else None},
         "host_enqueue_ms_per_step": {k: round(v, 4) for k, v in host_ms.items()},
         "overlap_phase_ms": {"find": round(float(t_find), 4), "fwd": round(float(t_fwd), 4),

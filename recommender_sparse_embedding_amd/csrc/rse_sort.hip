@@ -5,7 +5,8 @@
 //
 // One kernel per digit pass (digits of up to 9 bits, so 26-bit row keys take
 // three passes); the digit histograms of every pass are computed beforehand
-// by the pair-building kernel.  Per pass, each block:
+// by the pair-building kernel.  A pass runs a bounded number of blocks; each
+// repeatedly:
 //   1. takes the next tile (4096 pairs) from an atomic counter, so every tile
 //      it may wait on belongs to a block that is already running;
 //   2. ranks the tile's keys stably: each wave owns 512 consecutive pairs
@@ -36,6 +37,12 @@ constexpr uint32_t ST_INC = 2u << 30;           // inclusive prefix published
 constexpr uint32_t ST_VAL = (1u << 30) - 1u;
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 constexpr int LOOK = 8;                         // predecessors read per look-back step
+// Blocks per pass, each looping over tiles.  Measured beside the step's
+// large kernels: capping a pass at 64-128 blocks made the step slower (the
+// pass takes longer and the apply waits for it); at 256 and above the step
+// time no longer changes, so the cap only saves launching one block per
+// tile for very large batches.
+constexpr int64_t SORT_BLOCKS = 1024;
 
 __device__ __forceinline__ uint32_t load_state(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -70,7 +77,7 @@ __device__ void block_scan_bins(const uint32_t* in, uint32_t* out, int bins, uin
 __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const uint32_t* vals_in,
                                                 uint32_t* keys_out, uint32_t* vals_out, int64_t n, int shift,
                                                 int width, const uint32_t* totals, uint32_t* state,
-                                                uint32_t* tile_ctr, uint32_t* error) {
+                                                uint32_t* tile_ctr, uint32_t* error, uint32_t n_tiles) {
     __shared__ uint32_t s_wcnt[SWAVES][SORT_MAX_BINS];   // wave running counts -> wave prefixes
     __shared__ uint32_t s_cnt[SORT_MAX_BINS];            // tile count per digit
     __shared__ uint32_t s_pre[SORT_MAX_BINS];            // tile-local exclusive prefix per digit
@@ -84,14 +91,16 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
     const int bins = 1 << width;
     const uint32_t dmask = (uint32_t)bins - 1u;
+    // persistent: take tiles until none is left (or the pass has failed)
+    for (;;) {
     if (tid == 0) {
         s_tile = atomicAdd(tile_ctr, 1u);
-        s_fail = load_state(error) != 0u;     // raised before the pass: skip it
+        s_fail = load_state(error) != 0u;     // raised before or during the pass: stop
     }
     for (int d = tid; d < SWAVES * SORT_MAX_BINS; d += SB) (&s_wcnt[0][0])[d] = 0;
     __syncthreads();
-    if (s_fail) return;
     const uint32_t tile = s_tile;
+    if (s_fail || tile >= n_tiles) break;
     const int64_t base = (int64_t)tile * SORT_TILE;
     const int64_t tile_n = n - base < SORT_TILE ? n - base : SORT_TILE;
 
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
         s_glob[d] = s_base[d] + ex;
     }
     __syncthreads();
-    if (s_fail) return;
+    if (s_fail) break;
     // 4. reorder in LDS by digit, then write runs out
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
@@ -210,6 +219,8 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
         } else {
             atomicExch(error, 1u);
         }
+    }
+    __syncthreads();                          // LDS is reused by the next tile
     }
 }
 
@@ -263,9 +274,10 @@ int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int
             uint32_t* ko = alt ? k0 : k1;
             uint32_t* vo = alt ? v0 : v1;
             TraceScope ts(RSE_K_SORT_SCATTER, s);
-            hipLaunchKernelGGL(k_onesweep, dim3((unsigned)n_tiles), dim3(SB), 0, s, ki, vi, ko, vo, n, shift, width,
+            const int64_t grid = n_tiles < SORT_BLOCKS ? n_tiles : SORT_BLOCKS;
+            hipLaunchKernelGGL(k_onesweep, dim3((unsigned)grid), dim3(SB), 0, s, ki, vi, ko, vo, n, shift, width,
                                p.totals + ps * SORT_MAX_BINS, p.state + (int64_t)ps * n_tiles * SORT_MAX_BINS,
-                               p.tile_ctr + ps, p.error);
+                               p.tile_ctr + ps, p.error, (uint32_t)n_tiles);
             alt = !alt;
         }
     }
