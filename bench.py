@@ -110,12 +110,17 @@ def main():
     chunk_log2 = 20
     blk = rse.EmbeddingBlocks(D, cfg.wdtype, cfg.optim, chunk_log2, max_chunks=4096, seed=cfg.seed,
                               device=dev)
-    # rows the timed steps can add: never-seen keys (fresh fraction, or every
-    # key when tables start empty), bounded by the lookups of all steps
+    # rows the run can add: the whole universe when tables start empty (the
+    # lookups draw from it), else the never-seen keys of every find the run
+    # makes (warmup and timed steps of each schedule, plus look-ahead finds)
     max_bag = {"fixed": cfg.bag[1], "uniform": cfg.bag[-1], "poisson": 3 * cfg.bag[1]}[cfg.bag[0]]
-    new_frac = 1.0 if not cfg.prepopulate else cfg.fresh_frac
-    headroom = int(new_frac * cfg.n_bags * max_bag * (args.steps + args.warmup)) + (1 << chunk_log2)
-    blk.grow(-(-(total_keys + headroom) // (1 << chunk_log2)))
+    n_finds = 4 * args.warmup + 3 * args.steps + 8
+    if not cfg.prepopulate:
+        headroom = total_keys
+    else:
+        headroom = int(cfg.fresh_frac * cfg.n_bags * max_bag * n_finds)
+    headroom += 1 << chunk_log2
+    blk.grow(-(-((total_keys if cfg.prepopulate else 0) + headroom) // (1 << chunk_log2)))
     opt = rse.Optim(cfg.optim, cfg.lr, cfg.eps, cfg.beta1, cfg.beta2)
     n_new = torch.zeros(1, dtype=torch.int64, device=dev)
     pre_ws = idm.workspace(1 << 24)
@@ -126,7 +131,7 @@ def main():
                                  ws=pre_ws)
     torch.cuda.synchronize()
     used, st = blk.status()
-    assert st == 0 and used == total_keys, (used, st)
+    assert st == 0 and used == (total_keys if cfg.prepopulate else 0), (used, st)
     log(f"prepopulated {total_keys} keys in {time.time() - t0:.1f}s")
 
     batches = []
@@ -303,6 +308,7 @@ def main():
     idm_st, _ = idm.status()
     used, st = blk.status()
     assert idm_st == 0 and st == 0, (idm_st, st)
+    live_rows = used
 
     sel = [batches[(args.warmup + k) % len(batches)] for k in range(args.steps)]
     L_avg = float(np.mean([b["L"] for b in sel]))
@@ -351,8 +357,8 @@ def main():
         "dtype": "f32 storage, f64 accumulate" if cfg.wdtype == synth.F32 else "bf16 storage, f64 accumulate",
         "data": "synthetic (seeded Zipf lookups over random 63-bit keys, N(0,1) grads)",
         "config": {"workload": f"{cfg.name}: {T} tables x batch {B}, dim {D}, "
-                               f"{total_keys} live rows", "tables": T, "batch": B, "dim": D,
-                   "lookups_per_step": L_avg, "unique_rows_per_step": U_avg, "live_rows": total_keys,
+                               f"{live_rows} live rows", "tables": T, "batch": B, "dim": D,
+                   "lookups_per_step": L_avg, "unique_rows_per_step": U_avg, "live_rows": live_rows,
                    "map_load": args.map_load},
         "updated_rows_per_s": round(rows_s, 1),
         "step_compulsory_bytes": int(comp),
