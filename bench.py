@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--map-load", type=float, default=0.5)
     p.add_argument("--serial-bwd", action="store_true",
                    help="report the serial schedule (find, fwd, bwd update on one stream) as the value instead "
-                        "of the pipelined one")
+                        "of the lookahead one")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (an elementwise kernel that reads and "
                         "writes each byte once), to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -241,6 +241,41 @@ def main():
                                     ws2[i % 2])
         applied[i % 2].record(stream)
 
+    # "lookahead": stream 2 runs one more batch ahead.  While stream 1 runs
+    # batch i's forward and apply, stream 2 sorts batch i+1 (found during the
+    # previous step) and then finds batch i+2.  The sort shares the GPU with
+    # the forward and the find with the segmented update, and stream 1 never
+    # waits for the tail of a sort.  The find of i+2 writes only the map, rows
+    # it creates and batch i+2's offsets (a buffer last read by the forward
+    # of batch i-2 when at least three batches cycle); finds still run in
+    # batch order, so every result is that of the plain order.
+    ready = [torch.cuda.Event() for _ in range(3)]        # find of batch k done: ready[k % 3]
+    prepared = [torch.cuda.Event(), torch.cuda.Event()]   # prepare of batch k done: prepared[k % 2]
+
+    def la_find(k):
+        b = batch_at(k)
+        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws, stream=side)
+        ready[k % 3].record(side)
+
+    def la_prepare(k):
+        side.wait_event(applied[k % 2])               # the apply that last used this workspace
+        b = batch_at(k)
+        plans[k % 2] = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, ws2[k % 2], stream=side)
+        prepared[k % 2].record(side)
+
+    def la_step(i):
+        la_prepare(i + 1)
+        la_find(i + 2)
+        b = batch_at(i)
+        stream.wait_event(ready[i % 3])
+        rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
+        g = grad_of(b)
+        step_no[0] += 1
+        stream.wait_event(prepared[i % 2])
+        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+                                    ws2[i % 2])
+        applied[i % 2].record(stream)
+
     def batch_at(k):
         return batches[k % len(batches)]
 
@@ -254,6 +289,10 @@ def main():
             front(first, batch_at(first))
         if schedule == "staggered":
             find_ahead(first, batch_at(first))
+        if schedule == "lookahead":
+            la_find(first)
+            la_prepare(first)
+            la_find(first + 1)
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
@@ -266,6 +305,8 @@ def main():
                 step_overlap(batch_at(i), evs[k] if evs else None)
             elif schedule == "staggered":
                 staggered_step(i, batch_at(i), batch_at(i + 1))
+            elif schedule == "lookahead":
+                la_step(i)
             else:
                 front(i + 1, batch_at(i + 1))      # the next batch: one find + sort per step
                 back(i, batch_at(i))
@@ -273,13 +314,16 @@ def main():
             stream.wait_event(fronted[(first + n) % 2])
         if schedule == "staggered":
             stream.wait_event(found[(first + n) % 2])
+        if schedule == "lookahead":
+            stream.wait_event(prepared[(first + n) % 2])
+            stream.wait_event(ready[(first + n + 1) % 3])
         t1.record(stream)
         host_ms[schedule] = (time.perf_counter() - h0) * 1e3 / max(n, 1)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
 
-    schedule = "serial" if args.serial_bwd else ("pipelined" if len(batches) >= 2 else "overlap")
-    for name in ("serial", "overlap", "staggered", schedule):
+    schedule = "serial" if args.serial_bwd else ("lookahead" if len(batches) >= 3 else "overlap")
+    for name in ("serial", "overlap", "staggered", "pipelined", schedule):
         timed(name, 0, args.warmup)
     used, st = blk.status()
     assert st == 0, st
@@ -303,6 +347,7 @@ def main():
     rse.trace_start(rse.K_FWD)
     ms_serial = timed("serial", args.warmup, args.steps) / args.steps
     ms_stag = timed("staggered", args.warmup, args.steps) / args.steps if len(batches) >= 2 else None
+    ms_pipe = timed("pipelined", args.warmup, args.steps) / args.steps if len(batches) >= 2 else None
     n_fwd, fwd_ms = rse.trace_stop()
     t_fwd_kernel = fwd_ms / max(n_fwd, 1)
     idm_st, _ = idm.status()
@@ -366,11 +411,12 @@ def main():
         "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4),
         "schedule": {"serial": "find; fwd; bwd update (one stream)",
                      "overlap": "find; fwd (stream 1) || bwd prepare = pairs + sort (stream 2); bwd apply",
-                     "pipelined": "fwd + bwd apply of batch i (stream 1) || find + bwd prepare of batch i+1 "
-                                  "(stream 2)"}[schedule],
+                     "lookahead": "fwd + bwd apply of batch i (stream 1) || bwd prepare of batch i+1, then "
+                                  "find of batch i+2 (stream 2)"}[schedule],
         "ms_per_step_by_schedule": {"serial": round(ms_serial, 4), "overlap": round(ms_overlap, 4),
                                     "staggered": round(ms_stag, 4) if ms_stag else None,
-                                    "pipelined": round(ms_step, 4) if schedule == "pipelined" else None},
+                                    "pipelined": round(ms_pipe, 4) if ms_pipe else None,
+                                    "lookahead": round(ms_step, 4) if schedule == "lookahead" else None},
         "host_enqueue_ms_per_step": {k: round(v, 4) for k, v in host_ms.items()},
         "overlap_phase_ms": {"find": round(float(t_find), 4), "fwd": round(float(t_fwd), 4),
                              "bwd_update": round(float(t_bwd), 4)},

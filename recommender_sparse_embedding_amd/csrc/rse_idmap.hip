@@ -4,10 +4,11 @@
 // a map, not a dense or modulo-indexed table).
 //
 // Layout: per table a region of 16-byte slots {key, value} in buckets of 8
-// slots (128 bytes, one cache line).  A lookup is served by 8 lanes of a
-// wavefront that read one bucket with one 16-byte load each and compare by
-// ballot; a 64-lane wave therefore probes 8 lookups at once.  Buckets are
-// probed linearly from the bucket chosen by a salted 64-bit mix.
+// slots (128 bytes, one cache line).  A bucket is read by 8 lanes of a
+// wavefront with one 16-byte load each and compared by ballot; a 64-lane
+// wave takes 64 lookups at a time and has the first buckets of all of them
+// in flight together.  Buckets are probed linearly from the bucket chosen by
+// a salted 64-bit mix.
 //
 // find_or_insert runs as a fixed chain of kernels on one stream:
 //   reset -> probe (hits resolved; misses CAS-claim a slot and record their
@@ -121,7 +122,105 @@ __device__ bool load_bounds(int64_t* sb, const int64_t* bounds, int64_t stride, 
 }
 
 // -------------------------------------------------------------- probe ----
-// 8 lanes per lookup; each wave handles 8 lookups per iteration.
+// Results of the first-bucket pass, one per lookup: a value below
+// PENDING_BASE is the row offset found, the codes below are the rest.
+constexpr uint64_t RES_SLOW = ~0ull;          // needs the full probe
+constexpr uint64_t RES_ABSENT = ~0ull - 1;    // not in the map, nothing inserted
+constexpr uint64_t RES_BAD = ~0ull - 2;       // id out of range (merged mode)
+constexpr uint64_t RES_NONE = ~0ull - 3;      // lane past the end of the batch
+
+// Full probe of one lookup by the 8 lanes of a group: kind 0 hit, 1 pending
+// (a miss, inserted), 2 absent, 3 overflow.  `side`: the key is the empty
+// marker itself, kept in a per-table side slot.
+__device__ __forceinline__ void probe_full(const ProbeArgs& a, int64_t i, uint64_t key, int region, bool side,
+                                           int sub, int gshift, int& kind, uint64_t& val, uint32_t& slot_idx) {
+    kind = 2;
+    val = 0;
+    slot_idx = 0;
+    if (side) {
+        const uint64_t v = a.dir[region].side_val;
+        if (v < PENDING_BASE) {
+            kind = 0;
+            val = v;
+        } else if (a.insert) {
+            if (sub == 0) atomicMin((unsigned long long*)&a.dir[region].side_val,
+                                    (unsigned long long)(PENDING_BASE + (uint64_t)i));
+            kind = 1;
+            slot_idx = SIDE_MARK;
+        }
+        return;
+    }
+    const TableDir d = a.dir[region];
+    int64_t b = reduce_range(fmix64(key ^ d.salt), d.n_buckets);
+    int64_t probes = 0;
+    while (true) {
+        const int64_t sidx = d.slot_base + b * BUCKET;
+        const Slot s = a.slots[sidx + sub];
+        const uint32_t m = (uint32_t)(__ballot(s.key == key) >> gshift) & 0xFFu;
+        if (m) {
+            const int src = __ffs(m) - 1;
+            const uint64_t v = shfl_idx(s.val, gshift + src);
+            if (v < PENDING_BASE) {
+                kind = 0;
+                val = v;
+            } else {
+                // inserted by another lookup of this batch: join it
+                if (sub == 0)
+                    atomicMin((unsigned long long*)&a.slots[sidx + src].val,
+                              (unsigned long long)(PENDING_BASE + (uint64_t)i));
+                kind = 1;
+                slot_idx = (uint32_t)(sidx + src);
+            }
+            return;
+        }
+        const uint32_t e = (uint32_t)(__ballot(s.key == EMPTY_KEY) >> gshift) & 0xFFu;
+        if (e) {
+            if (!a.insert) return;
+            // Claim the first truly empty slot of the bucket, in slot order.
+            // A slot never returns to empty within the call, so slots seen as
+            // non-empty are skipped safely; a CAS that returns our key means
+            // another lookup got there first.
+            int claimed = -1;
+            if (sub == 0) {
+                uint32_t rem = e;
+                while (rem) {
+                    const int q = __ffs(rem) - 1;
+                    rem &= rem - 1;
+                    const unsigned long long old = atomicCAS((unsigned long long*)&a.slots[sidx + q].key,
+                                                             (unsigned long long)EMPTY_KEY, (unsigned long long)key);
+                    if (old == EMPTY_KEY || old == key) {
+                        atomicMin((unsigned long long*)&a.slots[sidx + q].val,
+                                  (unsigned long long)(PENDING_BASE + (uint64_t)i));
+                        claimed = q;
+                        break;
+                    }
+                }
+            }
+            claimed = shfl_idx(claimed, gshift);
+            if (claimed >= 0) {
+                kind = 1;
+                slot_idx = (uint32_t)(sidx + claimed);
+                return;
+            }
+            // bucket filled up meanwhile: continue with the next one
+        }
+        if (++probes >= d.n_buckets) {
+            kind = 3;
+            return;
+        }
+        b = (b + 1 == d.n_buckets) ? 0 : b + 1;
+    }
+}
+
+// 64 lookups per wave per iteration.  (1) One lane per lookup: id, table,
+// key and first bucket.  (2) Eight lanes per lookup: the first buckets of all
+// 64 lookups are loaded together (eight rounds, one 16-byte slot per lane per
+// round, all in flight at once) and matched; a committed key found there, or
+// a key found absent when nothing is inserted, is settled and written one
+// lane per lookup.  (3) The rest (keys being inserted or joined, keys further
+// along their chain, the empty-marker key) take the full probe, eight at a
+// time.  Most lookups of a steady-state batch are settled by (2), which costs
+// three dependent memory round trips per 64 lookups.
 __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
     const bool ok_bounds = load_bounds(sb, a.bounds, a.stride, a.n_tables, a.n_ids);
@@ -141,132 +240,101 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
     const int64_t wave_global = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
 
-    for (int64_t base = wave_global * 8; base < a.n_ids; base += n_waves * 8) {
-        const int64_t i = base + g;
+    for (int64_t base = wave_global * WAVE; base < a.n_ids; base += n_waves * WAVE) {
+        // (1) lanes past the end repeat the last lookup's reads, so that every
+        // load is issued unconditionally
+        const int64_t i = base + lane;
         const bool active = i < a.n_ids;
-        // result of this lookup: 0 hit, 1 pending (miss, inserted), 2 absent,
-        // 3 overflow, 4 bad id
-        int kind = 2;
-        uint64_t val = 0;
-        uint32_t slot_idx = 0;
-        if (active) {
-            const int t = table_of(sb, a.n_tables, i);
-            uint64_t key = (uint64_t)a.ids[i];
-            int region = t;
-            bool bad = false;
-            if (a.merged) {
-                if (key >= (1ull << 56)) bad = true;   // also rejects negative ids
-                key = ((uint64_t)t << 56) | key;
-                region = 0;
+        const int64_t ic = active ? i : a.n_ids - 1;
+        const int t = table_of(sb, a.n_tables, ic);
+        uint64_t key = (uint64_t)a.ids[ic];
+        int region = t;
+        uint64_t res = RES_SLOW;
+        if (a.merged) {
+            if (key >= (1ull << 56)) res = RES_BAD;   // also rejects negative ids
+            key = ((uint64_t)t << 56) | key;
+            region = 0;
+        }
+        const RSE_GLOBAL TableDir* dp = (const RSE_GLOBAL TableDir*)(a.dir + region);
+        const int64_t slot_base = dp->slot_base;
+        const int64_t n_buckets = dp->n_buckets;
+        const uint64_t salt = dp->salt;
+        const bool first = active && res == RES_SLOW && key != EMPTY_KEY;
+        const int64_t sidx0 = first ? slot_base + reduce_range(fmix64(key ^ salt), n_buckets) * BUCKET : 0;
+        if (!active) res = RES_NONE;
+
+        // (2) round r: group g reads the first bucket of lookup 8r + g
+        u32x4 pre[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int64_t sidx = shfl_idx(sidx0, r * 8 + g);
+            pre[r] = gload_u4(a.slots + sidx + sub);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int src = r * 8 + g;
+            const uint64_t key_r = shfl_idx(key, src);
+            const uint64_t sk = ((uint64_t)pre[r].y << 32) | pre[r].x;
+            const uint64_t sv = ((uint64_t)pre[r].w << 32) | pre[r].z;
+            const uint32_t m = (uint32_t)(__ballot(sk == key_r) >> gshift) & 0xFFu;
+            const uint32_t e = (uint32_t)(__ballot(sk == EMPTY_KEY) >> gshift) & 0xFFu;
+            const uint64_t v = shfl_idx(sv, gshift + (m ? __ffs(m) - 1 : 0));
+            uint64_t rg = RES_SLOW;
+            if (m) {
+                if (v < PENDING_BASE) rg = v;
+            } else if (e && !a.insert) {
+                rg = RES_ABSENT;
             }
-            if (bad) {
-                kind = 4;
-            } else if (key == EMPTY_KEY) {
-                // the empty marker itself: a per-table side slot
-                uint64_t v = a.dir[region].side_val;
-                if (v < PENDING_BASE) {
-                    kind = 0;
-                    val = v;
-                } else if (a.insert) {
-                    if (sub == 0) atomicMin((unsigned long long*)&a.dir[region].side_val,
-                                            (unsigned long long)(PENDING_BASE + (uint64_t)i));
-                    kind = 1;
-                    slot_idx = SIDE_MARK;
+            // back to one lane per lookup: lane 8r + g' takes group g''s result
+            const uint64_t mine = shfl_idx(rg, (lane & 7) * 8);
+            if ((lane >> 3) == r && first) res = mine;
+        }
+        if (res != RES_SLOW && res != RES_NONE) {
+            a.row_off[i] = res < PENDING_BASE ? (int64_t)res : -1;
+            a.ws.flag[i] = 0;
+            if (res == RES_BAD) a.ws.ctr[2] = 1;
+        }
+
+        // (3) the full probe for the rest: group g takes the g-th lowest
+        uint64_t slow = __ballot(res == RES_SLOW);
+        while (slow) {
+            uint64_t mg = slow;
+            for (int k = 0; k < g; ++k) mg &= mg - 1;
+            const bool has = mg != 0;
+            const int src = has ? __ffsll((long long)mg) - 1 : 0;
+            for (int k = 0; k < 8; ++k) slow &= slow - 1;
+            const uint64_t key_r = shfl_idx(key, src);
+            const int region_r = shfl_idx(region, src);
+            const int64_t ir = base + src;
+            int kind = 2;
+            uint64_t val = 0;
+            uint32_t slot_idx = 0;
+            if (has) probe_full(a, ir, key_r, region_r, key_r == EMPTY_KEY, sub, gshift, kind, val, slot_idx);
+            // write results (one lane per group) and append misses to the list
+            const bool leader = has && sub == 0;
+            const bool is_miss = leader && kind == 1;
+            const unsigned long long mm = __ballot(is_miss);
+            unsigned long long pos0 = 0;
+            if (mm) {
+                if (lane == __ffsll((long long)mm) - 1)
+                    pos0 = atomicAdd(&a.ws.ctr[0], (unsigned long long)__popcll(mm));
+                pos0 = __shfl(pos0, __ffsll((long long)mm) - 1, WAVE);
+            }
+            if (leader) {
+                if (kind == 0) {
+                    a.row_off[ir] = (int64_t)val;
+                    a.ws.flag[ir] = 0;
+                } else if (kind == 1) {
+                    const unsigned long long below = mm & ((1ull << lane) - 1);
+                    a.ws.miss_list[pos0 + __popcll(below)] = (uint32_t)ir;
+                    a.ws.slot_of[ir] = slot_idx;
+                    a.ws.flag[ir] = 1;
+                    a.row_off[ir] = -1;
                 } else {
-                    kind = 2;
+                    a.row_off[ir] = -1;
+                    a.ws.flag[ir] = 0;
+                    if (kind == 3) a.ws.ctr[1] = 1;
                 }
-            } else {
-                const TableDir d = a.dir[region];
-                int64_t b = reduce_range(fmix64(key ^ d.salt), d.n_buckets);
-                int64_t probes = 0;
-                while (true) {
-                    const int64_t sidx = d.slot_base + b * BUCKET;
-                    const Slot s = a.slots[sidx + sub];
-                    const uint32_t m = (uint32_t)(__ballot(s.key == key) >> gshift) & 0xFFu;
-                    if (m) {
-                        const int src = __ffs(m) - 1;
-                        const uint64_t v = shfl_idx(s.val, gshift + src);
-                        if (v < PENDING_BASE) {
-                            kind = 0;
-                            val = v;
-                        } else {
-                            // inserted by another lookup of this batch: join it
-                            if (sub == 0)
-                                atomicMin((unsigned long long*)&a.slots[sidx + src].val,
-                                          (unsigned long long)(PENDING_BASE + (uint64_t)i));
-                            kind = 1;
-                            slot_idx = (uint32_t)(sidx + src);
-                        }
-                        break;
-                    }
-                    const uint32_t e = (uint32_t)(__ballot(s.key == EMPTY_KEY) >> gshift) & 0xFFu;
-                    if (e) {
-                        if (!a.insert) {
-                            kind = 2;
-                            break;
-                        }
-                        // Claim the first truly empty slot of the bucket, in slot
-                        // order.  A slot never returns to empty within the call,
-                        // so slots seen as non-empty are skipped safely; a CAS
-                        // that returns our key means another lookup got there first.
-                        int claimed = -1;
-                        if (sub == 0) {
-                            uint32_t rem = e;
-                            while (rem) {
-                                const int q = __ffs(rem) - 1;
-                                rem &= rem - 1;
-                                const unsigned long long old = atomicCAS(
-                                    (unsigned long long*)&a.slots[sidx + q].key,
-                                    (unsigned long long)EMPTY_KEY, (unsigned long long)key);
-                                if (old == EMPTY_KEY || old == key) {
-                                    atomicMin((unsigned long long*)&a.slots[sidx + q].val,
-                                              (unsigned long long)(PENDING_BASE + (uint64_t)i));
-                                    claimed = q;
-                                    break;
-                                }
-                            }
-                        }
-                        claimed = shfl_idx(claimed, gshift);
-                        if (claimed >= 0) {
-                            kind = 1;
-                            slot_idx = (uint32_t)(sidx + claimed);
-                            break;
-                        }
-                        // bucket filled up meanwhile: continue with the next one
-                    }
-                    if (++probes >= d.n_buckets) {
-                        kind = 3;
-                        break;
-                    }
-                    b = (b + 1 == d.n_buckets) ? 0 : b + 1;
-                }
-            }
-        }
-        // write results (one lane per group) and append misses to the list
-        const bool leader = active && sub == 0;
-        const bool is_miss = leader && kind == 1;
-        const unsigned long long mm = __ballot(is_miss);
-        unsigned long long pos0 = 0;
-        if (mm) {
-            if (lane == __ffsll((long long)mm) - 1)
-                pos0 = atomicAdd(&a.ws.ctr[0], (unsigned long long)__popcll(mm));
-            pos0 = __shfl(pos0, __ffsll((long long)mm) - 1, WAVE);
-        }
-        if (leader) {
-            if (kind == 0) {
-                a.row_off[i] = (int64_t)val;
-                a.ws.flag[i] = 0;
-            } else if (kind == 1) {
-                const unsigned long long below = mm & ((1ull << lane) - 1);
-                a.ws.miss_list[pos0 + __popcll(below)] = (uint32_t)i;
-                a.ws.slot_of[i] = slot_idx;
-                a.ws.flag[i] = 1;
-                a.row_off[i] = -1;
-            } else {
-                a.row_off[i] = -1;
-                a.ws.flag[i] = 0;
-                if (kind == 3) a.ws.ctr[1] = 1;
-                if (kind == 4) a.ws.ctr[2] = 1;
             }
         }
     }
@@ -350,9 +418,13 @@ __global__ __launch_bounds__(256) void k_scan_reduce(Ws ws, int64_t n) {
     if (threadIdx.x == 0) ws.tile_sum[blockIdx.x] = red[0];
 }
 
-// Block-wide exclusive scan of 1024 values (one per thread); returns the total.
-__device__ uint32_t block_exclusive_scan_1024(uint32_t v, uint32_t* out_excl) {
-    __shared__ uint32_t wsum[16];
+constexpr int DECIDE_BLOCK = 256;   // small, so that it finds room beside other streams' kernels
+
+// Block-wide exclusive scan of DECIDE_BLOCK values (one per thread); returns
+// the total.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* out_excl) {
+    constexpr int NW = DECIDE_BLOCK / WAVE;
+    __shared__ uint32_t wsum[NW];
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     uint32_t x = v;
@@ -363,7 +435,7 @@ __device__ uint32_t block_exclusive_scan_1024(uint32_t v, uint32_t* out_excl) {
     if (lane == WAVE - 1) wsum[w] = x;
     __syncthreads();
     uint32_t wprefix = 0, total = 0;
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < NW; ++k) {
         if (k < w) wprefix += wsum[k];
         total += wsum[k];
     }
@@ -384,9 +456,9 @@ struct DecideArgs {
     Ws ws;
 };
 
-// Single block of 1024 threads: scans the tile sums, then decides whether the
-// call commits and advances the counters.
-__global__ __launch_bounds__(1024) void k_decide(DecideArgs a) {
+// Single block: scans the tile sums, then decides whether the call commits
+// and advances the counters.
+__global__ __launch_bounds__(DECIDE_BLOCK) void k_decide(DecideArgs a) {
     __shared__ int s_fail;
     __shared__ uint32_t s_carry;
     const bool any_miss = a.ws.ctr[0] != 0;
@@ -394,11 +466,11 @@ __global__ __launch_bounds__(1024) void k_decide(DecideArgs a) {
     if (any_miss) {
         if (threadIdx.x == 0) s_carry = 0;
         __syncthreads();
-        for (int64_t base = 0; base < a.n_tiles; base += 1024) {
+        for (int64_t base = 0; base < a.n_tiles; base += DECIDE_BLOCK) {
             const int64_t k = base + threadIdx.x;
             const uint32_t v = k < a.n_tiles ? a.ws.tile_sum[k] : 0;
             uint32_t ex;
-            const uint32_t t = block_exclusive_scan_1024(v, &ex);
+            const uint32_t t = block_exclusive_scan(v, &ex);
             const uint32_t carry = s_carry;
             if (k < a.n_tiles) a.ws.tile_sum[k] = carry + ex;
             __syncthreads();
@@ -766,7 +838,7 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     pa.row_off = d_row_off_out;
     pa.ws = ws;
     // 8 lookups per wave per iteration; enough waves to fill 256 CUs
-    const int probe_blocks = fill_blocks((n_ids + 7) / 8, PROBE_BLOCK / 64, 256 * 16);
+    const int probe_blocks = fill_blocks((n_ids + WAVE - 1) / WAVE, PROBE_BLOCK / 64, 256 * 16);
     {
         TraceScope ts(RSE_K_PROBE, s);
         hipLaunchKernelGGL(k_probe, dim3(probe_blocks), dim3(PROBE_BLOCK), 0, s, pa);
@@ -799,7 +871,7 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     da.n_new_out = d_n_new_out;
     da.n_tiles = n_tiles;
     da.ws = ws;
-    hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, s, da);
+    hipLaunchKernelGGL(k_decide, dim3(1), dim3(DECIDE_BLOCK), 0, s, da);
     hipLaunchKernelGGL(k_scan_down, tiles_grid, dim3(256), 0, s, ws, n_ids);
 
     CommitArgs ca;
