@@ -373,7 +373,7 @@ def main():
     TB = T * B
     w_bytes = D * (2 if cfg.wdtype == synth.BF16 else 4)
     fwd_bytes = float(np.mean([b["L"] * 8 + (TB + 1) * 8 + b["U"] * w_bytes + TB * D * 4 for b in sel]))
-    traffic = read_traffic("seg_update_clicklog.txt", KERNEL_REV)
+    traffic = read_traffic("seg_update_clicklog.txt", KERNEL_REV) if args.config == 2 else None
     roofline = {"bound": "hbm", "kernel": f"k_seg_work<{D},{'bf16' if cfg.wdtype else 'f32'}>",
                 "achieved": round(seg_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(seg_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,

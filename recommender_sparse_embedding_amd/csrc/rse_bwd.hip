@@ -22,11 +22,11 @@
 //   - long: the sorted lookups are cut into pieces of P = 64; each piece
 //     sums the part of a long segment it holds (at its start, continuing an
 //     earlier piece, and/or at its end, continuing past it) into a carry
-//     slot, 8 gradient rows in flight, in lookup order, in fp64;
+//     slot, 4-8 gradient rows in flight, in lookup order, in fp64;
 //   - singles: each group of lanes takes a few one-lookup segments and loads
 //     all their rows (weights + state) and gradient rows at once;
 //   - short: each group takes one short segment, loads its row, sums its
-//     gradient rows 8 at a time in lookup order, and updates the row.
+//     gradient rows 4-8 at a time in lookup order, and updates the row.
 // The combine kernel adds each long segment's carries in a fixed order
 // (round-robin over a block's groups, then group order) and updates its row.
 // The lists' order depends on timing, but every segment is reduced and
@@ -107,6 +107,10 @@ struct Geo {
     static constexpr int BLOCK = (64 * LPR < 256) ? 64 * LPR : 256;
     static constexpr int GPB = BLOCK / LPR;      // pieces (groups) per block, <= 64
     static constexpr int WIN = GPB * P + 2 * HALO;
+    // gradient rows a group keeps in flight: 128 bytes per lane either way
+    // (a bf16 row holds 8 elements per lane, so its fp32 gradient row takes
+    // 32 bytes per lane); fewer registers, more resident waves
+    static constexpr int GRAD_U = VEC >= 8 ? 4 : 8;
 };
 
 // ------------------------------------------------------------- pairs -----
@@ -220,7 +224,7 @@ template <int D, bool BF16>
 __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_vals, int x, int y, int li,
                                           double* acc) {
     constexpr int VEC = Geo<D, BF16>::VEC;
-    constexpr int U = 8;
+    constexpr int U = Geo<D, BF16>::GRAD_U;
     int q = x;
     for (; q + U <= y; q += U) {
         float gv[U][VEC];
@@ -546,7 +550,7 @@ template <int D, bool BF16, int OPT>
 __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
                                             int64_t n_groups, int li) {
     constexpr int VEC = Geo<D, BF16>::VEC;
-    constexpr int U = 8;
+    constexpr int U = Geo<D, BF16>::GRAD_U;
     const int64_t nm = (int64_t)a.ctr->n_multi;
     for (int64_t i = gid; i < nm; i += n_groups) {
         const Multi m = a.multis[i];

@@ -204,6 +204,21 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
 }
 
 // ----------------------------------------------------- group per bags ----
+// Each group owns BPG = 4 consecutive bags: their 5 offsets are loaded
+// together and kept in registers, and the group walks the bags' lookups as
+// one flat range, UNROLL rows in flight, closing a bag (one store, no load)
+// whenever the range crosses its end.  The row offsets of the next UNROLL
+// lookups are requested while the current rows are in flight, so each step
+// waits for one memory round trip instead of two.
+// Offsets of a chunk's 4 bags, as five scalars so that they stay in
+// registers (an array indexed in a loop would be moved to LDS).
+struct BagOffs4 {
+    int64_t o0, o1, o2, o3, o4;
+    __device__ __forceinline__ int64_t at(int k) const {
+        return k <= 0 ? o0 : k == 1 ? o1 : k == 2 ? o2 : k == 3 ? o3 : o4;
+    }
+};
+
 template <int D, bool BF16, int BPG, int UNROLL>
 __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
     using G = Geo<D, BF16>;
@@ -219,87 +234,92 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
     const char* dummy = can_load ? dummy_row(s_chunks, a.rv) : nullptr;
 
     for (int64_t jb = gid * BPG; jb < a.n_bags; jb += n_groups * BPG) {
-        const int64_t je = jb + BPG < a.n_bags ? jb + BPG : a.n_bags;
-        {
-            bool ok = true;
-            int64_t prev = a.bag_off[jb];
-            if (prev < 0 || prev > a.n_ids) ok = false;
-            for (int64_t jj = jb + 1; jj <= je; ++jj) {
-                const int64_t o = a.bag_off[jj];
-                if (o < prev || o > a.n_ids) ok = false;
-                prev = o;
-            }
-            if (!ok) {
-                if (li == 0) flag_bad(a);
-                continue;
-            }
+        const int nb = (int)(a.n_bags - jb < BPG ? a.n_bags - jb : BPG);
+        // start of bag jb + k for k < nb; the end of the last bag after that
+        static_assert(BPG == 4, "BagOffs4");
+        BagOffs4 bo;
+        bo.o0 = a.bag_off[jb];
+        bo.o1 = a.bag_off[jb + (1 < nb ? 1 : nb)];
+        bo.o2 = a.bag_off[jb + (2 < nb ? 2 : nb)];
+        bo.o3 = a.bag_off[jb + (3 < nb ? 3 : nb)];
+        bo.o4 = a.bag_off[jb + nb];
+        const bool ok = bo.o0 >= 0 && bo.o1 >= bo.o0 && bo.o2 >= bo.o1 && bo.o3 >= bo.o2 && bo.o4 >= bo.o3 &&
+                        bo.o4 <= a.n_ids;
+        if (!ok) {
+            if (li == 0) flag_bad(a);
+            continue;
         }
-        int64_t j = jb;
-        int64_t bag_start = a.bag_off[jb];
-        int64_t bag_end = a.bag_off[jb + 1];
-        const int64_t last = a.bag_off[je];
+        const int64_t first = bo.o0, last = bo.o4;
         uint32_t t = (uint32_t)((uint64_t)jb / (uint64_t)a.batch);
         uint32_t b = (uint32_t)(jb - (int64_t)t * a.batch);
         double acc[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
+        int k = 0;                     // open bag of the chunk
+        int64_t bag_start = first;
+        int64_t bag_end = bo.at(1);
+// closes the open bag: one store, then the next bag opens
+#define RSE_CLOSE_BAG()                                                              \
+    do {                                                                             \
+        const int64_t len = bag_end - bag_start;                                     \
+        float* dst = a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC;          \
+        store_out<VEC>(dst, acc, (double)len, a.mean && len > 0);                    \
+        for (int c = 0; c < VEC; ++c) acc[c] = 0.0;                                  \
+        if (++b == (uint32_t)a.batch) {                                              \
+            b = 0;                                                                   \
+            ++t;                                                                     \
+        }                                                                            \
+        ++k;                                                                         \
+        bag_start = bag_end;                                                         \
+        bag_end = bo.at(k + 1);                                                      \
+    } while (0)
 
-        auto close_bag = [&](int64_t len) {
-            float* dst = a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC;
-            store_out<VEC>(dst, acc, (double)len, a.mean && len > 0);
+        if (last > first) {
+            int64_t rn[UNROLL];
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
-            if (++b == (uint32_t)a.batch) {
-                b = 0;
-                ++t;
-            }
-        };
-
-        for (int64_t i = bag_start; i < last; i += UNROLL) {
-            int64_t r[UNROLL];
-            bool v[UNROLL];
-            u32x4 q[UNROLL];
+            for (int u = 0; u < UNROLL; ++u) rn[u] = a.row_off[first + u < last ? first + u : last - 1];
+            for (int64_t i = first; i < last; i += UNROLL) {
+                int64_t r[UNROLL];
+                bool v[UNROLL];
+                u32x4 q[UNROLL];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                r[u] = a.row_off[i + u < last ? i + u : last - 1];
-                v[u] = i + u < last && r[u] >= 0 && r[u] < a.capacity;
-                if (i + u < last && r[u] >= a.capacity && li == 0) flag_bad(a);
-            }
-            if (can_load) {
-#pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
-                    q[u] = gload_u4((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
-            }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int64_t ii = i + u;
-                if (ii >= last) break;
-                while (ii >= bag_end) {      // close finished (possibly empty) bags
-                    close_bag(bag_end - bag_start);
-                    ++j;
-                    bag_start = bag_end;
-                    bag_end = a.bag_off[j + 1];
+                for (int u = 0; u < UNROLL; ++u) {
+                    r[u] = rn[u];
+                    v[u] = i + u < last && r[u] >= 0 && r[u] < a.capacity;
+                    if (i + u < last && r[u] >= a.capacity && li == 0) flag_bad(a);
                 }
-                if (v[u]) widen_add<BF16>(acc, q[u]);
+                if (can_load) {
+#pragma unroll
+                    for (int u = 0; u < UNROLL; ++u)
+                        q[u] = gload_u4((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
+                }
+                const int64_t inx = i + UNROLL;
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) rn[u] = a.row_off[inx + u < last ? inx + u : last - 1];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int64_t ii = i + u;
+                    if (ii >= last) break;
+                    while (ii >= bag_end) RSE_CLOSE_BAG();   // finished (possibly empty) bags
+                    if (v[u]) widen_add<BF16>(acc, q[u]);
+                }
             }
         }
-        // close the remaining bags of the run (including trailing empty ones)
-        while (j < je) {
-            close_bag(bag_end - bag_start);
-            ++j;
-            if (j < je) {
-                bag_start = bag_end;
-                bag_end = a.bag_off[j + 1];
-            }
-        }
+        // close the open bag and any trailing empty ones
+        while (k < nb) RSE_CLOSE_BAG();
+#undef RSE_CLOSE_BAG
     }
 }
 
 // ------------------------------------------------------- wave per bag ----
+// The wave's groups split one bag's lookups round-robin (the next step's row
+// offsets requested while the current rows are in flight) and combine with
+// xor-shuffles in a fixed tree.
 template <int D, bool BF16, int UNROLL>
 __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
+    constexpr int64_t STEP = (int64_t)GROUPS * UNROLL;
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
     stage_chunks(s_chunks, a.rv);
     const int lane = lane_id();
@@ -319,24 +339,39 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
         double acc[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[k] = 0.0;
-        for (int64_t i = s + g; i < e; i += (int64_t)GROUPS * UNROLL) {
-            int64_t r[UNROLL];
-            bool v[UNROLL];
-            u32x4 q[UNROLL];
+        if (e > s) {
+            int64_t rn[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                const int64_t ii = i + (int64_t)u * GROUPS;
-                r[u] = a.row_off[ii < e ? ii : e - 1];
-                v[u] = ii < e && r[u] >= 0 && r[u] < a.capacity;
-                if (ii < e && r[u] >= a.capacity && li == 0) flag_bad(a);
+                const int64_t ii = s + g + (int64_t)u * GROUPS;
+                rn[u] = a.row_off[ii < e ? ii : e - 1];
             }
-            if (can_load) {
+            for (int64_t i = s + g; i < e + g; i += STEP) {
+                int64_t r[UNROLL];
+                bool v[UNROLL];
+                u32x4 q[UNROLL];
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
-                    q[u] = gload_u4((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int64_t ii = i + (int64_t)u * GROUPS;
+                    r[u] = rn[u];
+                    v[u] = ii < e && r[u] >= 0 && r[u] < a.capacity;
+                    if (ii < e && r[u] >= a.capacity && li == 0) flag_bad(a);
+                }
+                if (can_load) {
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
-                    if (v[u]) widen_add<BF16>(acc, q[u]);
+                    for (int u = 0; u < UNROLL; ++u)
+                        q[u] = gload_u4((v[u] ? a.rv.row(s_chunks, r[u]) : dummy) + li * 16);
+                }
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int64_t ii = i + STEP + (int64_t)u * GROUPS;
+                    rn[u] = a.row_off[ii < e ? ii : e - 1];
+                }
+                if (can_load) {
+#pragma unroll
+                    for (int u = 0; u < UNROLL; ++u)
+                        if (v[u]) widen_add<BF16>(acc, q[u]);
+                }
             }
         }
         // fixed xor tree across the groups

@@ -251,12 +251,15 @@ def test_split_backward_overlapping_forward(which):
         run_steps(cfg, 3, split=True)
 
 
+@pytest.mark.parametrize("schedule", ["pipelined", "lookahead"])
 @pytest.mark.parametrize("which", ["click_log", "fresh_keys_adam"])
-def test_pipelined_next_find_overlaps_apply(which):
-    """The find and sort of batch s+1 on a second stream run while batch s's
-    forward and apply run on the first (the forward of s+1 waits for both):
-    every step matches the oracle run in plain order, including new keys
-    inserted while the previous batch's rows are being updated."""
+def test_pipelined_next_find_overlaps_apply(which, schedule):
+    """Two-stream schedules.  pipelined: the find and sort of batch s+1 on a
+    second stream run while batch s's forward and apply run on the first (the
+    forward of s+1 waits for both).  lookahead: the second stream sorts batch
+    s+1 (found a step earlier) and then finds batch s+2 while batch s runs.
+    Every step matches the oracle run in plain order, including new keys
+    inserted while earlier batches' rows are being updated."""
     if which == "click_log":
         cfg = synth.config(2, batch=2048, cardinality=("loguniform", 10, 200_000))
     else:
@@ -289,22 +292,42 @@ def test_pipelined_next_find_overlaps_apply(which):
     plans = [None, None]
     n_new = torch.zeros(1, dtype=torch.int64, device=dev)
 
-    def front(s):
+    found = [torch.cuda.Event() for _ in range(3)]
+
+    def find(s):
         x = inputs[s]
-        side.wait_event(applied[s % 2])
         rse.idmap_find_or_insert(gpu.map, gpu.blocks, x["ids"], x["bo"], cfg.batch, cfg.n_tables, x["ro"], n_new,
                                  ws=fws, stream=side)
+        found[s % 3].record(side)
+
+    def prepare(s):
+        x = inputs[s]
+        side.wait_event(applied[s % 2])
         plans[s % 2] = rse.embedding_bag_bwd_prepare(gpu.blocks, x["ro"], x["bo"], cfg.n_tables, cfg.batch,
                                                      ws[s % 2], stream=side)
         fronted[s % 2].record(side)
 
-    front(0)
+    if schedule == "pipelined":
+        find(0)
+        prepare(0)
+    else:
+        find(0)
+        prepare(0)
+        find(1)
     for s in range(steps):
-        if s + 1 < steps:
-            front(s + 1)
+        if schedule == "pipelined":
+            if s + 1 < steps:
+                find(s + 1)
+                prepare(s + 1)
+        else:
+            if s + 1 < steps:
+                prepare(s + 1)
+            if s + 2 < steps:
+                find(s + 2)
         x = inputs[s]
-        main.wait_event(fronted[s % 2])
+        main.wait_event(found[s % 3])
         rse.embedding_bag_fwd(gpu.blocks, x["ro"], x["bo"], cfg.n_tables, cfg.batch, cfg.pooling, x["out"])
+        main.wait_event(fronted[s % 2])
         rse.embedding_bag_bwd_apply(gpu.blocks, plans[s % 2], x["bo"], cfg.n_tables, cfg.batch, cfg.pooling,
                                     x["g"], gpu.optim, s + 1, x["nu"], ws[s % 2])
         applied[s % 2].record(main)
