@@ -131,47 +131,85 @@ __global__ void k_zero_count(int64_t* n_unique) {
     if (threadIdx.x == 0) *n_unique = 0;
 }
 
-// One thread per bag: key = row (or `invalid`), value = bag.  Malformed bag
+// Key = row (or `invalid`), value = the lookup's gradient row b * n_tables + t
+// (the layout of grad), so the reduction reads gradients without any
+// division.  Each block takes a contiguous run of bags, PAIRS_BAGS bags at a
+// time: their offsets are staged in LDS (and checked), then the threads take
+// the lookups of those bags in coalesced strides, PAIRS_U per thread in
+// flight, each finding its bag by binary search in LDS.  Malformed bag
 // offsets or rows beyond the capacity mark the call bad (nothing is updated).
-// The value is the lookup's gradient row b * n_tables + t (the layout of
-// grad), so the reduction reads gradients without any division.  The kernel
-// also builds the radix sort's digit histograms of every pass (block-local in
-// LDS, then added to the totals) and clears the sort's look-back state; on bad
-// input it raises the sort's error flag so that no pass runs (unwritten keys
-// would not match the totals).
-__global__ __launch_bounds__(256) void k_pairs(const int64_t* row_off, const int64_t* bag_off, int64_t n_bags,
-                                               int64_t n_ids, int64_t batch, int32_t n_tables, int64_t capacity,
-                                               uint32_t invalid, uint32_t* keys, uint32_t* vals, Ctr* ctr,
-                                               int32_t* status, SortPrep sp, int passes, int width) {
+// The kernel also builds the radix sort's digit histograms of every pass
+// (block-local in LDS, then added to the totals) and clears the sort's
+// look-back state; on bad input it raises the sort's error flag so that no
+// pass runs (unwritten keys would not match the totals).
+constexpr int PAIRS_BLOCK = 256;
+constexpr int PAIRS_BAGS = 1024;     // bags staged at a time (one-hot: 4 lookups per thread)
+constexpr int PAIRS_U = 4;
+constexpr int PAIRS_GRID = 1024;     // bounds the histogram flush: a few thousand atomics per bin
+
+__global__ __launch_bounds__(PAIRS_BLOCK) void k_pairs(const int64_t* row_off, const int64_t* bag_off,
+                                                       int64_t n_bags, int64_t n_ids, int64_t batch,
+                                                       int32_t n_tables, int64_t capacity, uint32_t invalid,
+                                                       uint32_t* keys, uint32_t* vals, Ctr* ctr, int32_t* status,
+                                                       SortPrep sp, int passes, int width) {
     __shared__ uint32_t s_hist[SORT_MAX_PASSES * SORT_MAX_BINS];
+    __shared__ int64_t s_off[PAIRS_BAGS + 1];
+    __shared__ int s_bad;
     for (int q = threadIdx.x; q < SORT_MAX_PASSES * SORT_MAX_BINS; q += blockDim.x) s_hist[q] = 0;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < sp.state_words;
          q += (int64_t)gridDim.x * blockDim.x)
         sp.state[q] = 0;
-    __syncthreads();
-    bool bad = false;
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_bags;
-         j += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t s = bag_off[j], e = bag_off[j + 1];
-        if (s < 0 || e < s || e > n_ids || (j == 0 && s != 0) || (j == n_bags - 1 && e != n_ids)) {
-            bad = true;
-            continue;
+    if (threadIdx.x == 0) s_bad = 0;
+    bool bad = false;                  // a row beyond the capacity (this thread)
+    const int64_t per = (n_bags + gridDim.x - 1) / gridDim.x;
+    const int64_t jb0 = (int64_t)blockIdx.x * per;
+    const int64_t jb1 = jb0 + per < n_bags ? jb0 + per : n_bags;
+    for (int64_t j0 = jb0; j0 < jb1; j0 += PAIRS_BAGS) {
+        const int nbk = (int)(jb1 - j0 < PAIRS_BAGS ? jb1 - j0 : PAIRS_BAGS);
+        __syncthreads();               // s_off of the previous run has been read
+        for (int q = threadIdx.x; q <= nbk; q += PAIRS_BLOCK) s_off[q] = bag_off[j0 + q];
+        __syncthreads();
+        for (int q = threadIdx.x; q < nbk; q += PAIRS_BLOCK) {
+            const int64_t j = j0 + q;
+            const int64_t s = s_off[q], e = s_off[q + 1];
+            if (s < 0 || e < s || e > n_ids || (j == 0 && s != 0) || (j == n_bags - 1 && e != n_ids)) s_bad = 1;
         }
-        const uint32_t t = (uint32_t)((uint64_t)j / (uint64_t)batch);
-        const uint32_t gr = (uint32_t)(j - (int64_t)t * batch) * (uint32_t)n_tables + t;
-        for (int64_t i = s; i < e; ++i) {
-            const int64_t r = row_off[i];
-            uint32_t k = invalid;
-            if (r >= 0) {
-                if (r >= capacity) bad = true;
-                else k = (uint32_t)r;
+        __syncthreads();
+        if (s_bad) break;
+        const int64_t L0 = s_off[0], L1 = s_off[nbk];
+        for (int64_t i0 = L0 + threadIdx.x; i0 < L1; i0 += (int64_t)PAIRS_BLOCK * PAIRS_U) {
+            int64_t r[PAIRS_U];
+#pragma unroll
+            for (int u = 0; u < PAIRS_U; ++u) {
+                const int64_t i = i0 + (int64_t)u * PAIRS_BLOCK;
+                r[u] = row_off[i < L1 ? i : L1 - 1];
             }
-            keys[i] = k;
-            vals[i] = gr;
-            sort_hist_add(s_hist, k, passes, width);
+#pragma unroll
+            for (int u = 0; u < PAIRS_U; ++u) {
+                const int64_t i = i0 + (int64_t)u * PAIRS_BLOCK;
+                if (i >= L1) break;
+                // the bag of lookup i: the last k < nbk with s_off[k] <= i
+                int lo = 0, hi = nbk;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_off[mid] <= i) lo = mid;
+                    else hi = mid;
+                }
+                const int64_t j = j0 + lo;
+                const uint32_t t = (uint32_t)((uint64_t)j / (uint64_t)batch);
+                const uint32_t gr = (uint32_t)(j - (int64_t)t * batch) * (uint32_t)n_tables + t;
+                uint32_t k = invalid;
+                if (r[u] >= 0) {
+                    if (r[u] >= capacity) bad = true;
+                    else k = (uint32_t)r[u];
+                }
+                keys[i] = k;
+                vals[i] = gr;
+                sort_hist_add(s_hist, k, passes, width);
+            }
         }
     }
-    if (bad) {
+    if (bad || (threadIdx.x == 0 && s_bad)) {
         ctr->bad = 1;
         atomicExch(sp.error, 2u);
         atomicCAS(status, 0, (int32_t)RSE_ERR_BAD_INPUT);
@@ -508,16 +546,23 @@ __device__ __forceinline__ void walk_long(const BwdArgs& a, const uint32_t* s_ke
 }
 
 // Singles role: SPG one-lookup segments per group, their rows and gradient
-// rows all requested before any is used.
+// rows all requested before any is used; the group's next entries are
+// requested before this round's rows, so a round waits for one memory round
+// trip.
 template <int D, bool BF16, int OPT, int SPG>
 __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
                                              int64_t n_groups, int li) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     const int64_t ns = (int64_t)a.ctr->n_single;
-    for (int64_t i0 = gid * SPG; i0 < ns; i0 += n_groups * SPG) {
-        uint2 e[SPG];
+    if (gid * SPG >= ns) return;
+    uint2 e[SPG];
 #pragma unroll
-        for (int u = 0; u < SPG; ++u) e[u] = a.singles[i0 + u < ns ? i0 + u : ns - 1];
+    for (int u = 0; u < SPG; ++u) e[u] = a.singles[gid * SPG + u < ns ? gid * SPG + u : ns - 1];
+    for (int64_t i0 = gid * SPG; i0 < ns; i0 += n_groups * SPG) {
+        const int64_t inx = i0 + n_groups * SPG;
+        uint2 en[SPG];
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) en[u] = a.singles[inx + u < ns ? inx + u : ns - 1];
         char* rp[SPG];
         RowRegs<D, BF16> rr[SPG];
         float gv[SPG][VEC];
@@ -541,29 +586,38 @@ __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s
                 finish_row<D, BF16, OPT>(a, rp[u], li, rr[u], acc);
             }
         }
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) e[u] = en[u];
     }
 }
 
 // Short role: one segment of 2..LONG_T lookups per group; its row is
-// requested with its first gradient rows, which are summed U at a time.
+// requested with its first gradient rows, which are summed U at a time.  The
+// group's next segment descriptor is requested with this segment's row, and
+// that segment's first U bag ids before this one's update, so a segment
+// waits for one memory round trip per U lookups.
 template <int D, bool BF16, int OPT>
 __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
                                             int64_t n_groups, int li) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     constexpr int U = Geo<D, BF16>::GRAD_U;
     const int64_t nm = (int64_t)a.ctr->n_multi;
+    if (gid >= nm) return;
+    Multi m = a.multis[gid];
+    uint32_t j[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) j[u] = a.vals[m.start + (u < (int)m.len ? u : m.len - 1)];
     for (int64_t i = gid; i < nm; i += n_groups) {
-        const Multi m = a.multis[i];
+        const int64_t inx = i + n_groups;
+        const Multi mn = a.multis[inx < nm ? inx : nm - 1];
         char* rp = a.rv.row(s_chunks, m.key);
         RowRegs<D, BF16> rr;
         load_row<D, BF16, OPT>(rp, li, rr);
         double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-        for (uint32_t c0 = 0; c0 < m.len; c0 += U) {
-            uint32_t j[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) j[u] = a.vals[m.start + (c0 + u < m.len ? c0 + u : m.len - 1)];
+        uint32_t c0 = 0;
+        while (true) {
             float gv[U][VEC];
 #pragma unroll
             for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
@@ -573,8 +627,15 @@ __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (c0 + u < m.len) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+            c0 += U;
+            if (c0 >= m.len) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) j[u] = a.vals[m.start + (c0 + u < m.len ? c0 + u : m.len - 1)];
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) j[u] = a.vals[mn.start + (u < (int)mn.len ? u : mn.len - 1)];
         finish_row<D, BF16, OPT>(a, rp, li, rr, acc);
+        m = mn;
     }
 }
 
@@ -664,14 +725,18 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
 // group order, so the sum is the same on every run.  Block 0 also writes the
 // number of distinct rows (one-lookup + short + long segments).  The row
 // address is read from the global chunk table (one row per block, nothing
-// staged in LDS).  512 threads: the longest segment's partials are read in a
-// few rounds.
-constexpr int COMBINE_BLOCK = 512;
+// staged in LDS).  16 groups per block (64 to 512 threads): the longest
+// segment's partials are read in a few rounds, and a block does not hold
+// more lanes and LDS than the typical long segment's few pieces can use.
+template <int D, bool BF16>
+constexpr int combine_block() {
+    return 16 * Geo<D, BF16>::LPR < 64 ? 64 : (16 * Geo<D, BF16>::LPR > 512 ? 512 : 16 * Geo<D, BF16>::LPR);
+}
 
 template <int D, bool BF16, int OPT>
-__global__ __launch_bounds__(COMBINE_BLOCK) void k_combine(BwdArgs a) {
+__global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs a) {
     using G = Geo<D, BF16>;
-    constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = COMBINE_BLOCK, GPB = BLOCK / LPR;
+    constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = combine_block<D, BF16>(), GPB = BLOCK / LPR;
     constexpr int U = 4;
     __shared__ double s_part[GPB][D];
     if (a.ctr->bad || *a.sort_err) {
@@ -778,14 +843,15 @@ int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     a.s_blocks = fill_blocks(n_ids, G::GPB * singles_per_group<D, BF16>() * 8, 2048);
     const int m_blocks = fill_blocks(n_ids, G::GPB * 16, 2048);
     const int64_t work_blocks = (int64_t)a.l_blocks + a.s_blocks + m_blocks;
-    const int cblocks = fill_blocks(n_pieces, 1, 2048);
+    constexpr int CB = combine_block<D, BF16>();
+    const int cblocks = fill_blocks(n_pieces, 1, 2048 * 512 / CB);
     {
         TraceScope ts(RSE_K_SEG_UPDATE, s);
         hipLaunchKernelGGL((k_seg_work<D, BF16, OPT>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s, a);
     }
     {
         TraceScope ts(RSE_K_COMBINE, s);
-        hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(COMBINE_BLOCK), 0, s, a);
+        hipLaunchKernelGGL((k_combine<D, BF16, OPT>), dim3(cblocks), dim3(CB), 0, s, a);
     }
     return launch_status();
 }
@@ -860,8 +926,8 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
     if (n_ids > 0 && n_bags > 0) {
         const SortPlan sp_plan = sort_plan(bits);
         sp.state_words = sp.state_words / SORT_MAX_PASSES * sp_plan.passes;   // only the passes that run
-        // grid bounded so the per-block histogram flush stays a few hundred atomics per bin
-        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, 256, 512)), dim3(256), 0, s, d_row_off,
+        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, PAIRS_BLOCK, PAIRS_GRID)), dim3(PAIRS_BLOCK), 0, s,
+                           d_row_off,
                            d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
                            &blocks->header()->status, sp, sp_plan.passes, sp_plan.width);
         bool alt = false;
