@@ -145,7 +145,7 @@ __global__ void k_zero_count(int64_t* n_unique) {
 constexpr int PAIRS_BLOCK = 256;
 constexpr int PAIRS_BAGS = 1024;     // bags staged at a time (one-hot: 4 lookups per thread)
 constexpr int PAIRS_U = 4;
-constexpr int PAIRS_GRID = 1024;     // bounds the histogram flush: a few thousand atomics per bin
+constexpr int PAIRS_GRID = 2048;     // bounds the histogram flush: a few thousand atomics per bin
 
 __global__ __launch_bounds__(PAIRS_BLOCK) void k_pairs(const int64_t* row_off, const int64_t* bag_off,
                                                        int64_t n_bags, int64_t n_ids, int64_t batch,
@@ -509,8 +509,9 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
 // Long role, one piece per group: the part of a long segment at the
 // piece's start (continuing an earlier piece) goes to carry slot 0, the part
 // of a long segment starting in the piece (continuing past it) to slot 1.
+// Returns whether slot 0 was written.
 template <int D, bool BF16, int NMASK>
-__device__ __forceinline__ void walk_long(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
+__device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
                                           const unsigned long long* s_head, int wn, int64_t k, int x0, int xb,
                                           int li) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -523,7 +524,8 @@ __device__ __forceinline__ void walk_long(const BwdArgs& a, const uint32_t* s_ke
     // lookups without a row sort last: stop at the head of that run
     int lim = xb;
     if (s_keys[xb - 1] == a.invalid) lim = prev_head(s_head, xb - 1);
-    if (lim <= x0) return;
+    if (lim <= x0) return false;
+    bool wrote0 = false;
     if (!is_head(x0)) {
         const int h = prev_head(s_head, x0);
         const int e = next_head<NMASK>(s_head, x0, wn);
@@ -533,6 +535,7 @@ __device__ __forceinline__ void walk_long(const BwdArgs& a, const uint32_t* s_ke
             for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
             sum_range<D, BF16>(a, s_vals, x0, e < lim ? e : lim, li, acc);
             carry(0, acc);
+            wrote0 = true;
         }
     }
     const int hl = prev_head(s_head, lim - 1);
@@ -543,6 +546,7 @@ __device__ __forceinline__ void walk_long(const BwdArgs& a, const uint32_t* s_ke
         sum_range<D, BF16>(a, s_vals, hl, xb, li, acc);
         carry(1, acc);
     }
+    return wrote0;
 }
 
 // Singles role: SPG one-lookup segments per group, their rows and gradient
@@ -653,6 +657,7 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     __shared__ uint32_t s_vals[WIN];
     __shared__ unsigned long long s_head[NMASK];
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    __shared__ int s_run[GPB];     // per piece: 1 slot 0 written, 2 segment goes on into the next piece
     stage_chunks(s_chunks, a.rv);
     if (a.ctr->bad) return;
     if (*a.sort_err) {
@@ -709,20 +714,47 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
         }
         __syncthreads();
         const int64_t k = pb + g;
-        if (k >= n_pieces) continue;
-        const int x0 = (int)(k * P - w0);
-        const int xb = (int)((k * P + P < n ? k * P + P : n) - w0);
-        walk_long<D, BF16, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
+        bool wrote0 = false, spans = false;
+        if (k < n_pieces) {
+            const int x0 = (int)(k * P - w0);
+            const int xb = (int)((k * P + P < n ? k * P + P : n) - w0);
+            wrote0 = walk_long<D, BF16, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
+            // no head in [x0, xb]: the segment at the piece's start fills the
+            // piece and goes on into the next one
+            spans = k + 1 < n_pieces && next_head<NMASK>(s_head, x0 - 1, wn) > xb;
+        }
+        if (li == 0) s_run[g] = (wrote0 ? 1 : 0) | (spans ? 2 : 0);
+        __syncthreads();       // the window's carries are written and visible to the block
+        // Runs of slot-0 partials of one long segment over consecutive pieces
+        // of this window are added (in piece order) into the run's first
+        // piece: the combine then reads one partial per run, the run's first
+        // piece being the segment's second piece or a multiple of GPB.
+        const bool lead = (s_run[g] & 1) && (g == 0 || (s_run[g - 1] & 3) != 3);
+        if (lead && g + 1 < GPB && (s_run[g] & 2) && (s_run[g + 1] & 1)) {
+            double* dst = a.carry + (k * 2) * D + li * G::VEC;
+            double acc[G::VEC];
+#pragma unroll
+            for (int c = 0; c < G::VEC; ++c) acc[c] = dst[c];
+            for (int q = g + 1; q < GPB && (s_run[q] & 1) && (s_run[q - 1] & 2); ++q) {
+                const double* src = a.carry + ((pb + q) * 2) * D + li * G::VEC;
+#pragma unroll
+                for (int c = 0; c < G::VEC; ++c) acc[c] += src[c];
+            }
+#pragma unroll
+            for (int c = 0; c < G::VEC; ++c) dst[c] = acc[c];
+        }
     }
 }
 
 // ------------------------------------------------- long segment combine --
 // One block per owner (grid-stride).  The pieces a long segment covers are
 // its head's piece k0 (partial in carry slot 1) and the following pieces
-// whose first key is still the segment's (slot 0); they form a prefix, so
-// one block-wide count per 2^8 pieces finds the last one.  Partials are added
-// round-robin per group (U loads in flight, added in piece order) then in
-// group order, so the sum is the same on every run.  Block 0 also writes the
+// k0+1..k1 whose first key is still the segment's; they form a prefix, so
+// one block-wide count per block size finds k1.  The work kernel has added
+// the slot-0 partials of each of its windows' runs into the run's first piece:
+// k0+1 and every multiple of its GPB in (k0+1, k1].  Those partials are added
+// round-robin per group (U loads in flight, in list order) then in group
+// order, so the sum is the same on every run.  Block 0 also writes the
 // number of distinct rows (one-lookup + short + long segments).  The row
 // address is read from the global chunk table (one row per block, nothing
 // staged in LDS).  16 groups per block (64 to 512 threads): the longest
@@ -762,21 +794,29 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
             k1 += cnt;
             if (cnt < BLOCK) break;
         }
+        // partial t of the list: t = 0 slot 1 of k0, t = 1 slot 0 of k0+1,
+        // t >= 2 slot 0 of the (t-1)-th multiple of WG after k0+1
+        constexpr int64_t WG = G::GPB;
+        const int64_t base = (k0 + 1) / WG;
+        const int64_t n_items = k1 > k0 ? 2 + (k1 / WG - base) : 1;
+        auto item = [&](int64_t t) -> const double* {
+            const int64_t k = t == 0 ? k0 : (t == 1 ? k0 + 1 : (base + t - 1) * WG);
+            return a.carry + (k * 2 + (t == 0 ? 1 : 0)) * D + li * VEC;
+        };
         double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-        for (int64_t kq = k0 + g; kq <= k1; kq += U * GPB) {
+        for (int64_t tq = g; tq < n_items; tq += U * GPB) {
             double src[U][VEC];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t k = kq + u * GPB <= k1 ? kq + u * GPB : k1;
-                const double* p = a.carry + (k * 2 + (k == k0 ? 1 : 0)) * D + li * VEC;
+                const double* p = item(tq + u * GPB < n_items ? tq + u * GPB : n_items - 1);
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) src[u][c] = p[c];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (kq + u * GPB <= k1)
+                if (tq + u * GPB < n_items)
 #pragma unroll
                     for (int c = 0; c < VEC; ++c) acc[c] += src[u][c];
         }
@@ -926,7 +966,7 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
     if (n_ids > 0 && n_bags > 0) {
         const SortPlan sp_plan = sort_plan(bits);
         sp.state_words = sp.state_words / SORT_MAX_PASSES * sp_plan.passes;   // only the passes that run
-        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, PAIRS_BLOCK, PAIRS_GRID)), dim3(PAIRS_BLOCK), 0, s,
+        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, PAIRS_BAGS, PAIRS_GRID)), dim3(PAIRS_BLOCK), 0, s,
                            d_row_off,
                            d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
                            &blocks->header()->status, sp, sp_plan.passes, sp_plan.width);
