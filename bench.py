@@ -429,7 +429,7 @@ def main():
 
 
 # identifies the kernel source the stored traffic counters were taken on
-KERNEL_REV = "seg-v5"
+KERNEL_REV = "seg-v6"
 
 
 def read_traffic(name, rev):

@@ -31,6 +31,7 @@
 // (round-robin over a block's groups, then group order) and updates its row.
 // The lists' order depends on timing, but every segment is reduced and
 // updated independently, so results do not.  Only integer atomics are used.
+#include <algorithm>
 #include <cmath>
 
 #include "rse_sort.h"
@@ -966,7 +967,11 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
     if (n_ids > 0 && n_bags > 0) {
         const SortPlan sp_plan = sort_plan(bits);
         sp.state_words = sp.state_words / SORT_MAX_PASSES * sp_plan.passes;   // only the passes that run
-        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(n_bags, PAIRS_BAGS, PAIRS_GRID)), dim3(PAIRS_BLOCK), 0, s,
+        // enough blocks for the bags (one staging run each) and for the lookups
+        // (a few strides per thread when bags are long)
+        const int64_t pairs_units = std::max((n_bags + PAIRS_BAGS - 1) / PAIRS_BAGS,
+                                             (n_ids + PAIRS_BLOCK * PAIRS_U * 4 - 1) / (PAIRS_BLOCK * PAIRS_U * 4));
+        hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(pairs_units, 1, PAIRS_GRID)), dim3(PAIRS_BLOCK), 0, s,
                            d_row_off,
                            d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
                            &blocks->header()->status, sp, sp_plan.passes, sp_plan.width);
