@@ -124,7 +124,7 @@ __global__ void k_bwd_reset(Ctr* ctr, SortPrep sp) {
         *sp.error = 0;
     }
     if (threadIdx.x < SORT_MAX_PASSES) sp.tile_ctr[threadIdx.x] = 0;
-    for (int k = threadIdx.x; k < SORT_MAX_PASSES * SORT_MAX_BINS; k += blockDim.x) sp.totals[k] = 0;
+    for (int k = threadIdx.x; k < SORT_TOTAL_COPIES * SORT_COPY_STRIDE; k += blockDim.x) sp.totals[k] = 0;
 }
 
 // An apply with no lookups still reports its distinct-row count (0).
@@ -140,7 +140,7 @@ __global__ void k_zero_count(int64_t* n_unique) {
 // flight, each finding its bag by binary search in LDS.  Malformed bag
 // offsets or rows beyond the capacity mark the call bad (nothing is updated).
 // The kernel also builds the radix sort's digit histograms of every pass
-// (block-local in LDS, then added to the totals) and clears the sort's
+// (block-local in LDS, then added to one of the totals' copies) and clears the sort's
 // look-back state; on bad input it raises the sort's error flag so that no
 // pass runs (unwritten keys would not match the totals).
 constexpr int PAIRS_BLOCK = 256;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(PAIRS_BLOCK) void k_pairs(const int64_t* row_off, c
     }
     __syncthreads();
     for (int q = threadIdx.x; q < passes * SORT_MAX_BINS; q += blockDim.x)
-        if (s_hist[q]) atomicAdd(&sp.totals[q], s_hist[q]);
+        if (s_hist[q]) atomicAdd(&sp.totals[(blockIdx.x % SORT_TOTAL_COPIES) * SORT_COPY_STRIDE + q], s_hist[q]);
 }
 
 // ------------------------------------------------------ grad gather ------

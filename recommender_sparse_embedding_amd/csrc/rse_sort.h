@@ -8,6 +8,11 @@ namespace rse_host {
 constexpr int SORT_TILE = 4096;      // keys per sort block (512 threads x 8)
 constexpr int SORT_MAX_PASSES = 4;   // 32-bit keys
 constexpr int SORT_MAX_BINS = 512;   // digits of up to 9 bits
+// The digit totals are kept in several copies that blocks of the pair
+// kernel add to in turn (the totals are the sum over copies): a few hundred
+// blocks adding to one word each would queue behind each other.
+constexpr int SORT_TOTAL_COPIES = 8;
+constexpr int64_t SORT_COPY_STRIDE = (int64_t)SORT_MAX_PASSES * SORT_MAX_BINS;
 
 // Digit plan for keys of `bits` bits: passes of at most 9 bits each.
 struct SortPlan {
@@ -20,11 +25,12 @@ SortPlan sort_plan(int bits);
 size_t sort_workspace(int64_t n, int64_t* n_tiles_out);
 
 // Device pointers inside the sort workspace that the pair-building kernel
-// fills before the passes: per-pass digit totals (SORT_MAX_PASSES x
-// SORT_MAX_BINS, must start at zero) and the look-back state (zeroed by the
-// pair kernel).  `error` is nonzero if a pass failed or was skipped.
+// fills before the passes: per-pass digit totals (SORT_TOTAL_COPIES copies
+// of SORT_MAX_PASSES x SORT_MAX_BINS, must start at zero) and the look-back
+// state (zeroed by the pair kernel).  `error` is nonzero if a pass failed or
+// was skipped.
 struct SortPrep {
-    uint32_t* totals;        // [SORT_MAX_PASSES][SORT_MAX_BINS]
+    uint32_t* totals;        // [SORT_TOTAL_COPIES][SORT_MAX_PASSES][SORT_MAX_BINS]
     uint32_t* state;         // [SORT_MAX_PASSES][n_tiles][SORT_MAX_BINS]
     uint32_t* tile_ctr;      // [SORT_MAX_PASSES] dynamic tile counters
     uint32_t* error;         // look-back timeout flag
@@ -34,8 +40,8 @@ SortPrep sort_prep(void* ws, int64_t n);
 
 // Sorts (k0, v0) by the low `bits` bits, stably, ping-ponging through
 // (k1, v1); the result ends in (k1, v1) if *result_in_alt.  Requires the
-// digit totals of every pass to be in prep.totals and the rest of prep to be
-// zero (the caller's pair kernel does both).
+// digit totals of every pass to be in prep.totals (summed over its copies)
+// and the rest of prep to be zero (the caller's pair kernel does both).
 int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n, int bits,
                      void* ws, bool* result_in_alt, hipStream_t s);
 

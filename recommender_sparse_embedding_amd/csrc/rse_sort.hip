@@ -91,6 +91,16 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
     const int bins = 1 << width;
     const uint32_t dmask = (uint32_t)bins - 1u;
+    // global exclusive prefix per digit, once per block: the digit totals
+    // are the sum of their copies
+    for (int d = tid; d < bins; d += SB) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int c = 0; c < SORT_TOTAL_COPIES; ++c) t += totals[c * SORT_COPY_STRIDE + d];
+        s_cnt[d] = t;
+    }
+    __syncthreads();
+    block_scan_bins(s_cnt, s_base, bins, s_tmp);
     // persistent: take tiles until none is left (or the pass has failed)
     for (;;) {
     if (tid == 0) {
@@ -145,7 +155,6 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
     }
     __syncthreads();
     block_scan_bins(s_cnt, s_pre, bins, s_tmp);
-    block_scan_bins(totals, s_base, bins, s_tmp);
     // 3. decoupled look-back per digit, LOOK predecessors read at once: their
     // counts are added newest first until an inclusive prefix is found
     // (tile 0 always publishes one, so the walk ends); a predecessor that
@@ -241,7 +250,7 @@ static int64_t tiles_of(int64_t n) { return (n + SORT_TILE - 1) / SORT_TILE; }
 size_t sort_workspace(int64_t n, int64_t* n_tiles_out) {
     const int64_t n_tiles = tiles_of(n > 0 ? n : 1);
     if (n_tiles_out) *n_tiles_out = n_tiles;
-    return align_up((size_t)SORT_MAX_PASSES * SORT_MAX_BINS * 4, 256) +
+    return align_up((size_t)SORT_TOTAL_COPIES * SORT_COPY_STRIDE * 4, 256) +
            align_up((size_t)SORT_MAX_PASSES * n_tiles * SORT_MAX_BINS * 4, 256) + 256 + 256;
 }
 
@@ -249,7 +258,7 @@ SortPrep sort_prep(void* ws, int64_t n) {
     const int64_t n_tiles = tiles_of(n > 0 ? n : 1);
     Carver c(ws);
     SortPrep p;
-    p.totals = c.take<uint32_t>((size_t)SORT_MAX_PASSES * SORT_MAX_BINS);
+    p.totals = c.take<uint32_t>((size_t)SORT_TOTAL_COPIES * SORT_COPY_STRIDE);
     p.state = c.take<uint32_t>((size_t)SORT_MAX_PASSES * n_tiles * SORT_MAX_BINS);
     p.tile_ctr = c.take<uint32_t>(SORT_MAX_PASSES);
     p.error = c.take<uint32_t>(1);
