@@ -226,6 +226,52 @@ def test_config5_merged_bf16_twin():
     run_steps(synth.config(5, batch=128, cardinality=("fixed", 10_000)), 2)
 
 
+@pytest.mark.parametrize("dim,wdtype,optim", [(128, synth.F32, synth.ADAGRAD), (32, synth.BF16, synth.ADAGRAD),
+                                              (16, synth.F32, synth.SGD), (64, synth.F32, synth.ADAM)])
+def test_long_segment_boundaries(dim, wdtype, optim):
+    """Segments placed on purpose in the sorted order (rows are numbered in
+    insertion order and the backward sorts by row): a segment whose head and
+    end fall exactly on 64-lookup piece boundaries, segments of exactly 128
+    lookups (the longest reduced by one group) and 129 (the shortest split
+    into pieces), one-lookup and short segments between them, and hot rows
+    spanning many pieces and more than one work-kernel window (8 pieces for
+    dim 128 fp32, 16 for dim 64, 64 for dim 32 bf16 and dim 16).  Two steps
+    with different lookup orders; pooled outputs, every row and the
+    distinct-row count against the oracle."""
+    counts = [64, 320, 128, 129, 1, 2, 63, 65, 191, 1, 1, 9000, 130, 2 * 4096 + 64, 127, 3, 1, 640]
+    K = len(counts)
+    L = int(sum(counts))
+    rng = np.random.default_rng(11)
+    keys = rng.integers(0, 1 << 62, K, dtype=np.int64)
+    assert len(np.unique(keys)) == K
+    cfg = synth.config(2, n_tables=1, batch=L, dim=dim, wdtype=wdtype, optim=optim,
+                       lr=0.1 if optim == synth.SGD else 0.01, cardinality=("fixed", K), seed=77)
+    orc = make_oracle(cfg)
+    gpu = GpuTables(cfg, [K], K + 1024)
+    bounds = np.array([0, K], np.int64)
+    ro_r, nn_r = orc.find_or_insert(keys, bounds, 1)
+    ro_g, nn_g = gpu.find_or_insert(keys, bounds, 1)
+    assert nn_g == nn_r == K
+    assert np.array_equal(ro_g.cpu().numpy(), ro_r) and np.array_equal(ro_r, np.arange(K))
+    bo = np.arange(L + 1, dtype=np.int64)
+    rtol = rtol_for(wdtype)
+    offs = np.arange(K, dtype=np.int64)
+    for step in range(2):
+        ids = keys[rng.permutation(np.repeat(np.arange(K), counts))]
+        ro_r, _ = orc.find_or_insert(ids, bo, cfg.batch)
+        ro_g, _ = gpu.find_or_insert(ids, bo, cfg.batch)
+        assert np.array_equal(ro_g.cpu().numpy(), ro_r), f"row offsets, step {step}"
+        out_g = gpu.fwd(ro_g, bo)
+        out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
+        assert_close(out_g.cpu().numpy(), out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol, "pooled output")
+        G = rng.standard_normal((L, 1, dim)).astype(np.float32)
+        prev_w, _ = orc.get_rows(offs)
+        U_r = orc.bwd_update(ro_r, bo, cfg.batch, G, cfg.pooling)
+        U_g = gpu.bwd(ro_g, bo, G)
+        assert U_g == U_r == K
+        compare_rows(gpu, orc, prev_w, offs, rtol, f"step {step}")
+
+
 def test_run_to_run_bit_identical():
     cfg = synth.config(2, n_tables=4, batch=4096, cardinality=("fixed", 3000))
     res = []
