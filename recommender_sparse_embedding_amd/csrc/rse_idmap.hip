@@ -13,10 +13,11 @@
 // find_or_insert runs as a fixed chain of kernels on one stream:
 //   reset -> probe (hits resolved; misses CAS-claim a slot and record their
 //   lookup index as a pending value with atomicMin, so the slot ends up
-//   holding the FIRST lookup of that key) -> mark first-sight lookups ->
-//   exclusive scan over lookups (rank of each first sight in lookup order)
-//   -> decide (capacity / load checks, single block) -> commit (or roll
-//   back every pending slot) -> resolve pending lookups -> init new rows.
+//   holding the FIRST lookup of that key) -> mark first-sight lookups and
+//   count them per tile of lookups -> decide (capacity / load checks and the
+//   scan of the tile counts, single block) -> rank each tile's first sights
+//   in lookup order and commit them (or roll back every pending slot) ->
+//   resolve pending lookups and initialise new rows.
 // New offsets are therefore rows_used + rank, identical to inserting the
 // keys one by one in lookup order, and independent of thread timing.  Only
 // integer atomics are used.  Kernels after the probe exit at once when the
@@ -46,7 +47,6 @@ struct Ws {
     uint32_t* miss_list;       // lookup indices that missed (any order)
     uint32_t* slot_of;         // per lookup: claimed slot (SIDE_MARK for the side slot)
     uint32_t* flag;            // per lookup: 0 hit, 1 pending, 2 first sight
-    uint32_t* rank;            // per first-sight lookup: new-row rank
     uint32_t* tile_sum;        // per scan tile
     uint64_t* new_key;         // per new row (by rank): key
     uint32_t* new_tab;         // per new row: table index used by the init
@@ -61,7 +61,6 @@ Ws carve(void* base, int64_t n_ids, size_t* total) {
     w.miss_list = c.take<uint32_t>(n);
     w.slot_of = c.take<uint32_t>(n);
     w.flag = c.take<uint32_t>(n);
-    w.rank = c.take<uint32_t>(n);
     w.tile_sum = c.take<uint32_t>(tiles + 1);
     w.new_key = c.take<uint64_t>(n);
     w.new_tab = c.take<uint32_t>(n);
@@ -85,10 +84,11 @@ struct ProbeArgs {
 };
 
 // -------------------------------------------------------------- reset ----
-__global__ void k_reset(Ws ws, TableDir* dir, int32_t n_regions) {
+__global__ void k_reset(Ws ws, TableDir* dir, int32_t n_regions, int64_t n_tiles) {
     const int tid = threadIdx.x;
     if (tid < 32) ws.ctr[tid] = 0;
     for (int r = tid; r < n_regions; r += blockDim.x) dir[r].new_keys = 0;
+    for (int64_t k = tid; k <= n_tiles; k += blockDim.x) ws.tile_sum[k] = 0;
 }
 
 // Table of lookup i: the t with bounds[t] <= i < bounds[t+1] (bounds in LDS,
@@ -365,7 +365,9 @@ struct MarkArgs {
 };
 
 // A pending lookup is the first sight of its key iff the slot's pending value
-// names it.  First sights are counted per region for the load check.
+// names it.  First sights are counted per region for the load check, and per
+// tile of SCAN_TILE lookups for the ranks (one atomic add per tile per wave:
+// a wave's entries of the miss list come from few tiles).
 __global__ void k_mark(MarkArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
     __shared__ uint32_t s_new[RSE_MAX_TABLES];   // per-region first sights of this block
@@ -387,35 +389,24 @@ __global__ void k_mark(MarkArgs a) {
             region = region_of_slot(a.dir, a.n_regions, s);
             v = a.slots[s].val;
         }
-        if (v == PENDING_BASE + (uint64_t)i) {
+        const bool first = v == PENDING_BASE + (uint64_t)i;
+        if (first) {
             a.ws.flag[i] = 2;
             atomicAdd(&s_new[region], 1u);
+        }
+        const uint32_t tile = i / SCAN_TILE;
+        unsigned long long pend = __ballot(first);
+        while (pend) {
+            const int src = __ffsll((long long)pend) - 1;
+            const uint32_t tl = __shfl(tile, src, WAVE);
+            const unsigned long long same = __ballot(first && tile == tl) & pend;
+            if (lane_id() == src) atomicAdd(&a.ws.tile_sum[tl], (uint32_t)__popcll(same));
+            pend &= ~same;
         }
     }
     __syncthreads();
     for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x)
         if (s_new[r]) atomicAdd((unsigned long long*)&a.dir[r].new_keys, (unsigned long long)s_new[r]);
-}
-
-// ---------------------------------------------------------------- scan ---
-// Exclusive scan of (flag == 2) over all lookups: reduce per tile, scan the
-// tile sums in one block, then rescan each tile.
-__global__ __launch_bounds__(256) void k_scan_reduce(Ws ws, int64_t n) {
-    if (ws.ctr[0] == 0) return;
-    const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
-    uint32_t c = 0;
-    for (int k = 0; k < SCAN_TILE / 256; ++k) {
-        const int64_t i = base + k * 256 + threadIdx.x;
-        if (i < n) c += ws.flag[i] == 2;
-    }
-    __shared__ uint32_t red[256];
-    red[threadIdx.x] = c;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) ws.tile_sum[blockIdx.x] = red[0];
 }
 
 constexpr int DECIDE_BLOCK = 256;   // small, so that it finds room beside other streams' kernels
@@ -513,41 +504,7 @@ __global__ __launch_bounds__(DECIDE_BLOCK) void k_decide(DecideArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void k_scan_down(Ws ws, int64_t n) {
-    if (ws.ctr[0] == 0 || ws.ctr[3] == 0) return;
-    const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
-    // each thread owns 16 consecutive lookups
-    const int64_t i0 = base + (int64_t)threadIdx.x * 16;
-    uint32_t f[16];
-    uint32_t c = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int64_t i = i0 + k;
-        f[k] = (i < n && ws.flag[i] == 2) ? 1u : 0u;
-        c += f[k];
-    }
-    // block exclusive scan of c (256 threads)
-    __shared__ uint32_t wsum[4];
-    const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
-    uint32_t x = c;
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, WAVE);
-        if (lane >= o) x += y;
-    }
-    if (lane == WAVE - 1) wsum[w] = x;
-    __syncthreads();
-    uint32_t pre = ws.tile_sum[blockIdx.x];
-    for (int k = 0; k < w; ++k) pre += wsum[k];
-    uint32_t r = pre + x - c;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if (f[k]) ws.rank[i0 + k] = r;
-        r += f[k];
-    }
-}
-
-// ------------------------------------------------------------ commit -----
+// --------------------------------------------------- rank and commit ----
 struct CommitArgs {
     Slot* slots;
     TableDir* dir;
@@ -558,27 +515,52 @@ struct CommitArgs {
     int64_t stride;
     int32_t n_tables;
     int32_t pad;
+    int64_t n;
     Ws ws;
 };
 
-// First sights publish their offset (or, on failure, release the slot).
-__global__ void k_commit(CommitArgs a) {
+// One block per tile of SCAN_TILE lookups (16 per thread).  If the call
+// commits, the tile's first sights get their ranks (the tile's prefix from
+// k_decide plus a block scan, i.e. the exclusive scan over all lookups) and
+// publish offset rows_used + rank into their slot; otherwise they release
+// their slot.
+__global__ __launch_bounds__(256) void k_rank_commit(CommitArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
-    const unsigned long long n_miss = a.ws.ctr[0];
-    if (n_miss == 0) return;
+    __shared__ uint32_t wsum[4];
+    if (a.ws.ctr[0] == 0) return;
     for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
-    __syncthreads();
     const bool ok = a.ws.ctr[3] != 0;
     const uint64_t used = a.ws.ctr[4];
-    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
-         q += (unsigned long long)gridDim.x * blockDim.x) {
-        const uint32_t i = a.ws.miss_list[q];
-        if (a.ws.flag[i] != 2) continue;
+    const int64_t i0 = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * 16;
+    uint32_t f[16];
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t i = i0 + k;
+        f[k] = (i < a.n && a.ws.flag[i] == 2) ? 1u : 0u;
+        c += f[k];
+    }
+    // block exclusive scan of c (256 threads); the barrier also covers sb
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t x = c;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = a.ws.tile_sum[blockIdx.x];
+    for (int k = 0; k < w; ++k) pre += wsum[k];
+    uint32_t rk = pre + x - c;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (!f[k]) continue;
+        const int64_t i = i0 + k;
         const uint32_t s = a.ws.slot_of[i];
         const int t = table_of(sb, a.n_tables, i);
         const int region = a.merged ? 0 : t;
         if (ok) {
-            const uint32_t rk = a.ws.rank[i];
             const uint64_t off = used + rk;
             uint64_t key = (uint64_t)a.ids[i];
             if (a.merged) key = ((uint64_t)t << 56) | key;
@@ -586,74 +568,86 @@ __global__ void k_commit(CommitArgs a) {
             else a.slots[s].val = off;
             a.ws.new_key[rk] = key;
             a.ws.new_tab[rk] = (uint32_t)region;
+        } else if (s == SIDE_MARK) {
+            a.dir[region].side_val = EMPTY_VAL;
         } else {
-            if (s == SIDE_MARK) {
-                a.dir[region].side_val = EMPTY_VAL;
-            } else {
-                a.slots[s].key = EMPTY_KEY;
-                a.slots[s].val = EMPTY_VAL;
-            }
+            a.slots[s].key = EMPTY_KEY;
+            a.slots[s].val = EMPTY_VAL;
         }
+        ++rk;
     }
 }
 
-// Every pending lookup reads its key's final offset.
-__global__ void k_resolve(Slot* slots, TableDir* dir, int32_t merged, const int64_t* bounds,
-                          int64_t stride, int32_t n_tables, Ws ws, int64_t* row_off) {
-    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
-    const unsigned long long n_miss = ws.ctr[0];
-    if (n_miss == 0) return;
-    for (int t = threadIdx.x; t <= n_tables; t += blockDim.x) sb[t] = bounds[(int64_t)t * stride];
-    __syncthreads();
-    const bool ok = ws.ctr[3] != 0;
-    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
-         q += (unsigned long long)gridDim.x * blockDim.x) {
-        const uint32_t i = ws.miss_list[q];
-        int64_t v = -1;
-        if (ok) {
-            const uint32_t s = ws.slot_of[i];
-            if (s == SIDE_MARK) {
-                const int region = merged ? 0 : table_of(sb, n_tables, i);
-                v = (int64_t)dir[region].side_val;
-            } else {
-                v = (int64_t)slots[s].val;
-            }
-        }
-        row_off[i] = v;
-    }
-}
+// ------------------------------------------------- resolve and init -----
+struct FinishArgs {
+    Slot* slots;
+    TableDir* dir;
+    int32_t merged;
+    int32_t n_tables;
+    const int64_t* bounds;
+    int64_t stride;
+    int64_t* row_off;
+    RowsView rv;
+    int64_t row_bytes;
+    uint64_t seed;
+    int32_t dim;
+    int32_t pad;
+    Ws ws;
+};
 
-// New rows: weights from the key hash, state zero.  One thread per 16 bytes
-// of a row; rows are consecutive so the writes are contiguous.
+// One grid-stride range over two kinds of items: first every pending lookup
+// (it reads its key's final offset, or -1 if the call did not commit), then
+// every 16 bytes of the new rows (weights from the key hash, state zero;
+// rows are consecutive so the writes are contiguous).
 template <bool BF16>
-__global__ void k_init_rows(RowsView rv, int dim, int64_t row_bytes, uint64_t seed, Ws ws) {
-    if (ws.ctr[3] == 0) return;
-    const uint64_t n_new = ws.ctr[5];
-    if (n_new == 0) return;
-    const uint64_t used = ws.ctr[4];
-    const int64_t q_per_row = row_bytes / 16;
-    const int64_t w_q = (int64_t)dim * (BF16 ? 2 : 4) / 16;   // 16-byte units of weights
+__global__ void k_finish(FinishArgs a) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const uint64_t n_miss = a.ws.ctr[0];
+    if (n_miss == 0) return;
+    for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    __syncthreads();
+    const bool ok = a.ws.ctr[3] != 0;
+    const uint64_t n_new = ok ? a.ws.ctr[5] : 0;
+    const uint64_t used = a.ws.ctr[4];
+    const int64_t q_per_row = a.row_bytes / 16;
+    const int64_t w_q = (int64_t)a.dim * (BF16 ? 2 : 4) / 16;   // 16-byte units of weights
     const int per_q = BF16 ? 8 : 4;
-    const uint64_t total = n_new * (uint64_t)q_per_row;
+    const uint64_t total = n_miss + n_new * (uint64_t)q_per_row;
     for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t r = e / (uint64_t)q_per_row;
-        const int64_t qi = (int64_t)(e - r * (uint64_t)q_per_row);
-        char* row = rv.row((int64_t)(used + r));
+        if (e < n_miss) {
+            const uint32_t i = a.ws.miss_list[e];
+            int64_t v = -1;
+            if (ok) {
+                const uint32_t s = a.ws.slot_of[i];
+                if (s == SIDE_MARK) {
+                    const int region = a.merged ? 0 : table_of(sb, a.n_tables, i);
+                    v = (int64_t)a.dir[region].side_val;
+                } else {
+                    v = (int64_t)a.slots[s].val;
+                }
+            }
+            a.row_off[i] = v;
+            continue;
+        }
+        const uint64_t ee = e - n_miss;
+        const uint64_t r = ee / (uint64_t)q_per_row;
+        const int64_t qi = (int64_t)(ee - r * (uint64_t)q_per_row);
+        char* row = a.rv.row((int64_t)(used + r));
         u32x4 out = u32x4{0u, 0u, 0u, 0u};
         if (qi < w_q) {
-            const uint64_t key = ws.new_key[r];
-            const uint32_t tab = ws.new_tab[r];
+            const uint64_t key = a.ws.new_key[r];
+            const uint32_t tab = a.ws.new_tab[r];
             uint32_t wv[4];
             if (!BF16) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    wv[k] = __float_as_uint(init_value(key, tab, (int)(qi * per_q + k), seed, false));
+                    wv[k] = __float_as_uint(init_value(key, tab, (int)(qi * per_q + k), a.seed, false));
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const uint32_t lo = f32_to_bf16_exact(init_value(key, tab, (int)(qi * per_q + 2 * k), seed, true));
-                    const uint32_t hi = f32_to_bf16_exact(init_value(key, tab, (int)(qi * per_q + 2 * k + 1), seed, true));
+                    const uint32_t lo = f32_to_bf16_exact(init_value(key, tab, (int)(qi * per_q + 2 * k), a.seed, true));
+                    const uint32_t hi = f32_to_bf16_exact(init_value(key, tab, (int)(qi * per_q + 2 * k + 1), a.seed, true));
                     wv[k] = lo | (hi << 16);
                 }
             }
@@ -822,7 +816,8 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
 
-    hipLaunchKernelGGL(k_reset, dim3(1), dim3(256), 0, s, ws, map->d_dir(), map->n_tables);
+    const int64_t n_tiles = (n_ids + SCAN_TILE - 1) / SCAN_TILE;
+    hipLaunchKernelGGL(k_reset, dim3(1), dim3(256), 0, s, ws, map->d_dir(), map->n_tables, n_tiles);
 
     ProbeArgs pa;
     pa.slots = map->d_slots();
@@ -837,7 +832,7 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     pa.pad = 0;
     pa.row_off = d_row_off_out;
     pa.ws = ws;
-    // 8 lookups per wave per iteration; enough waves to fill 256 CUs
+    // 64 lookups per wave per iteration; enough waves to fill 256 CUs
     const int probe_blocks = fill_blocks((n_ids + WAVE - 1) / WAVE, PROBE_BLOCK / 64, 256 * 16);
     {
         TraceScope ts(RSE_K_PROBE, s);
@@ -858,9 +853,7 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     ma.ws = ws;
     hipLaunchKernelGGL(k_mark, dim3(miss_blocks), dim3(256), 0, s, ma);
 
-    const int64_t n_tiles = (n_ids + SCAN_TILE - 1) / SCAN_TILE;
     const dim3 tiles_grid((unsigned)(n_tiles > 0 ? n_tiles : 1));
-    hipLaunchKernelGGL(k_scan_reduce, tiles_grid, dim3(256), 0, s, ws, n_ids);
     DecideArgs da;
     da.dir = pa.dir;
     da.n_regions = map->n_tables;
@@ -872,7 +865,6 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     da.n_tiles = n_tiles;
     da.ws = ws;
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(DECIDE_BLOCK), 0, s, da);
-    hipLaunchKernelGGL(k_scan_down, tiles_grid, dim3(256), 0, s, ws, n_ids);
 
     CommitArgs ca;
     ca.slots = pa.slots;
@@ -884,18 +876,30 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     ca.stride = stride;
     ca.n_tables = n_tables;
     ca.pad = 0;
+    ca.n = n_ids;
     ca.ws = ws;
-    hipLaunchKernelGGL(k_commit, dim3(miss_blocks), dim3(256), 0, s, ca);
-    hipLaunchKernelGGL(k_resolve, dim3(miss_blocks), dim3(256), 0, s, pa.slots, pa.dir, map->merged,
-                       d_bounds, stride, n_tables, ws, d_row_off_out);
-    const int64_t init_work = n_ids * (blocks->row_bytes / 16);
-    const dim3 init_grid(fill_blocks(init_work, 256, 8192));
+    hipLaunchKernelGGL(k_rank_commit, tiles_grid, dim3(256), 0, s, ca);
+
+    FinishArgs fa;
+    fa.slots = pa.slots;
+    fa.dir = pa.dir;
+    fa.merged = map->merged;
+    fa.n_tables = n_tables;
+    fa.bounds = d_bounds;
+    fa.stride = stride;
+    fa.row_off = d_row_off_out;
+    fa.rv = blocks->view();
+    fa.row_bytes = blocks->row_bytes;
+    fa.seed = blocks->seed;
+    fa.dim = blocks->dim;
+    fa.pad = 0;
+    fa.ws = ws;
+    const int64_t finish_work = n_ids * (1 + blocks->row_bytes / 16);
+    const dim3 finish_grid(fill_blocks(finish_work, 256, 8192));
     if (blocks->w_dtype == RSE_BF16)
-        hipLaunchKernelGGL(k_init_rows<true>, init_grid, dim3(256), 0, s, blocks->view(), blocks->dim,
-                           blocks->row_bytes, blocks->seed, ws);
+        hipLaunchKernelGGL(k_finish<true>, finish_grid, dim3(256), 0, s, fa);
     else
-        hipLaunchKernelGGL(k_init_rows<false>, init_grid, dim3(256), 0, s, blocks->view(), blocks->dim,
-                           blocks->row_bytes, blocks->seed, ws);
+        hipLaunchKernelGGL(k_finish<false>, finish_grid, dim3(256), 0, s, fa);
     return launch_status();
 }
 
