@@ -69,6 +69,16 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 10}))
 
 
+def logical_bytes(cfg, L, U, row_bytes):
+    """Bytes the step moves with no reuse across lookups: the compulsory
+    bytes plus, for every lookup beyond the first of its row, the forward's
+    row-weight gather and one map slot."""
+    import synth
+
+    w_bytes = cfg.dim * (2 if cfg.wdtype == synth.BF16 else 4)
+    return compulsory_bytes(cfg, L, U, 0, row_bytes) + (L - U) * (w_bytes + 16)
+
+
 def compulsory_bytes(cfg, L, U, n_new, row_bytes):
     """Bytes the step must move at least once: ids, bag offsets, one map slot
     per distinct key, read+write of every touched row (weights + state), the
@@ -363,6 +373,7 @@ def main():
     lookups_s = L_avg / (ms_step * 1e-3)
     rows_s = U_avg / (ms_step * 1e-3)
     step_gbs = comp / (ms_step * 1e-3) / 1e9
+    logical = float(np.mean([logical_bytes(cfg, b["L"], b["U"], rb) for b in sel]))
 
     # roofline of the segmented-update kernel: algorithmic bytes per launch =
     # sorted (row, gradient-row) pairs read (8 B per lookup) + one gradient row
@@ -409,6 +420,8 @@ def main():
         "step_compulsory_bytes": int(comp),
         "step_hbm_gbs": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4),
+        "step_logical_bytes": int(logical),
+        "step_logical_gbs": round(logical / (ms_step * 1e-3) / 1e9, 1),
         "schedule": {"serial": "find; fwd; bwd update (one stream)",
                      "overlap": "find; fwd (stream 1) || bwd prepare = pairs + sort (stream 2); bwd apply",
                      "lookahead": "fwd + bwd apply of batch i (stream 1) || bwd prepare of batch i+1, then "
