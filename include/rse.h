@@ -255,8 +255,8 @@ int rse_bwd_workspace_size(int64_t n_ids, int32_t n_tables, int64_t batch, int32
  * Lookup i of bag j = t*batch + b contributes g_i = grad[b, t, :] (divided
  * by the bag length for RSE_MEAN) to row d_row_off[i].  The (row, bag)
  * pairs are radix-sorted by row (stable), so each touched row's g is the
- * fp64 sum of its contributions in lookup order (segments longer than 128
- * are summed in 64-lookup pieces and the pieces added in a fixed tree); no
+ * fp64 sum of its contributions in lookup order (segments longer than 64
+ * are summed in 64-lookup pieces and the pieces added in a fixed order); no
  * floating-point atomics are used and the result is run-to-run identical.
  * Then, once per touched row, in fp64 and rounded once to the storage type:
  *   SGD:     w -= lr * g

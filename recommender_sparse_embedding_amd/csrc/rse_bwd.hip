@@ -42,7 +42,10 @@ using namespace rse_host;
 namespace {
 
 constexpr int P = 64;            // lookups per piece
-constexpr int LONG_T = 128;      // longest segment reduced by one group
+// Longest segment reduced by one group.  At least P - 1, so that a longer
+// segment cannot lie strictly inside one piece (the long role handles the
+// segments at a piece's start and at its last head only).
+constexpr int LONG_T = 64;
 constexpr int HALO = LONG_T + 1;
 constexpr int MAX_SEG_BLOCKS = 65535;
 

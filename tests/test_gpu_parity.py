@@ -231,14 +231,14 @@ def test_config5_merged_bf16_twin():
 def test_long_segment_boundaries(dim, wdtype, optim):
     """Segments placed on purpose in the sorted order (rows are numbered in
     insertion order and the backward sorts by row): a segment whose head and
-    end fall exactly on 64-lookup piece boundaries, segments of exactly 128
-    lookups (the longest reduced by one group) and 129 (the shortest split
+    end fall exactly on 64-lookup piece boundaries, segments of exactly 64
+    lookups (the longest reduced by one group) and 65 (the shortest split
     into pieces), one-lookup and short segments between them, and hot rows
     spanning many pieces and more than one work-kernel window (8 pieces for
     dim 128 fp32, 16 for dim 64, 64 for dim 32 bf16 and dim 16).  Two steps
     with different lookup orders; pooled outputs, every row and the
     distinct-row count against the oracle."""
-    counts = [64, 320, 128, 129, 1, 2, 63, 65, 191, 1, 1, 9000, 130, 2 * 4096 + 64, 127, 3, 1, 640]
+    counts = [64, 320, 64, 65, 1, 2, 63, 128, 129, 191, 1, 1, 9000, 130, 2 * 4096 + 64, 127, 3, 1, 640, 66]
     K = len(counts)
     L = int(sum(counts))
     rng = np.random.default_rng(11)
