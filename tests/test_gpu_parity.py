@@ -484,6 +484,43 @@ def test_plan_mismatch_rejected():
     del orc
 
 
+def test_empty_batch_through_every_call():
+    """A batch with no lookups at all (every bag empty): find writes no
+    offsets and inserts nothing, the forward writes zeros, the backward
+    (whole and in two halves) reports 0 distinct rows and changes no row."""
+    import recommender_sparse_embedding_amd as rse
+
+    cfg = synth.config(3, n_tables=3, batch=40, dim=16, cardinality=("fixed", 500), fresh_frac=0.0)
+    wl = synth.Workload(cfg)
+    gpu = GpuTables(cfg, wl.card, int(wl.card.sum()) + 1024)
+    for ids, bounds in wl.prepopulation():
+        gpu.find_or_insert(ids, bounds, 1)
+    used0, _ = gpu.blocks.status()
+    offs = np.arange(used0, dtype=np.int64)
+    w0, s0 = gpu.rows(offs)
+    ids = np.zeros(0, dtype=np.int64)
+    bo = np.zeros(cfg.n_bags + 1, dtype=np.int64)
+    ro, n_new = gpu.find_or_insert(ids, bo, cfg.batch)
+    assert n_new == 0 and ro.numel() == 0
+    out = gpu.fwd(ro, bo)
+    assert out.shape == (cfg.batch, cfg.n_tables, cfg.dim) and not out.any()
+    G = torch.ones((cfg.batch, cfg.n_tables, cfg.dim), dtype=torch.float32, device="cuda")
+    gpu.n_unique.fill_(7)
+    assert gpu.bwd(ro, bo, G) == 0
+    t_bo = torch.from_numpy(bo).cuda()
+    ws = rse.bwd_workspace(0, cfg.n_tables, cfg.batch, cfg.dim)
+    plan = rse.embedding_bag_bwd_prepare(gpu.blocks, ro, t_bo, cfg.n_tables, cfg.batch, ws)
+    gpu.n_unique.fill_(7)
+    rse.embedding_bag_bwd_apply(gpu.blocks, plan, t_bo, cfg.n_tables, cfg.batch, cfg.pooling, G, gpu.optim, 2,
+                                gpu.n_unique, ws)
+    assert int(gpu.n_unique.item()) == 0
+    used1, st = gpu.blocks.status()
+    assert used1 == used0 and st == 0 and gpu.map.status()[0] == 0
+    w1, s1 = gpu.rows(offs)
+    assert np.array_equal(w0.view(np.uint32), w1.view(np.uint32))
+    assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+
+
 # ----------------------------------------------------------- failures ----
 def test_need_grow_commits_nothing_and_retry_matches():
     cfg = synth.config(1, n_tables=1, batch=40, dim=16, bag=("fixed", 1), prepopulate=False)
