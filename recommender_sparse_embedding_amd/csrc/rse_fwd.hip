@@ -10,10 +10,13 @@
 // order, so the pooled value is the exactly rounded fp32 of the sum in all
 // but pathological cases.
 //
-// Two schedules:
-//  - group-per-bags: each group owns BPG consecutive bags and walks their
+// Three schedules, chosen by the mean bag length:
+//  - one-hot (mean <= 1.5): a group takes a chunk of up to 8 bags with no
+//    loop, all its rows in flight at once; chunks that are not one-hot fall
+//    back to a bag-by-bag walk;
+//  - group-per-bags: each group owns 4 consecutive bags and walks their
 //    lookups as one flat range, UNROLL rows in flight, closing a bag whenever
-//    the range crosses its end offset (short bags, one-hot);
+//    the range crosses its end offset (short bags);
 //  - wave-per-bag: the wave's groups split one bag's lookups round-robin and
 //    combine with xor-shuffles in a fixed tree (long bags).
 #include "rse_host.h"
