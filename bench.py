@@ -442,7 +442,7 @@ def main():
 
 
 # identifies the kernel source the stored traffic counters were taken on
-KERNEL_REV = "seg-v8"
+KERNEL_REV = "seg-v9"
 
 
 def read_traffic(name, rev):

@@ -261,32 +261,26 @@ __device__ __forceinline__ void add_grad(double* acc, const float* gv, bool mean
 
 // acc += sum over window positions [x, y) of the LDS-staged bag ids, in
 // order.  U gradient rows are loaded together (all loads issued before any
-// is used); a tail shorter than U is loaded one row at a time.
+// is used); a last step shorter than U repeats the range's last row (masked
+// out of the sum), so a ragged end costs one round trip, not one per row.
 template <int D, bool BF16>
 __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_vals, int x, int y, int li,
                                           double* acc) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     constexpr int U = Geo<D, BF16>::GRAD_U;
-    int q = x;
-    for (; q + U <= y; q += U) {
+    for (int q = x; q < y; q += U) {
         float gv[U][VEC];
         uint32_t j[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) j[u] = s_vals[q + u];
+        for (int u = 0; u < U; ++u) j[u] = s_vals[q + u < y ? q + u : y - 1];
 #pragma unroll
         for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
         double len[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
-    }
-    for (; q < y; ++q) {
-        float gv[VEC];
-        const uint32_t j = s_vals[q];
-        load_grad<VEC>(gv, grad_row<D, BF16>(a, j, li));
-        const double len = a.mean ? bag_len(a, j) : 1.0;
-        add_grad<VEC>(acc, gv, a.mean, len);
+        for (int u = 0; u < U; ++u)
+            if (q + u < y) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
     }
 }
 
