@@ -12,7 +12,7 @@ compulsory HBM bytes per second against the 8 TB/s peak, a roofline entry for
 the dominant kernel (timed live with HIP events on the library's stream) and
 the CPU oracle timed on the host.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -38,8 +38,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2, help="workload number (2 = click-log, the headline)")
     p.add_argument("--batches", type=int, default=4, help="distinct batches cycled through")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -124,7 +124,7 @@ def main():
     # lookups draw from it), else the never-seen keys of every find the run
     # makes (warmup and timed steps of each schedule, plus look-ahead finds)
     max_bag = {"fixed": cfg.bag[1], "uniform": cfg.bag[-1], "poisson": 3 * cfg.bag[1]}[cfg.bag[0]]
-    n_finds = 4 * args.warmup + 3 * args.steps + 8
+    n_finds = 5 * (args.warmup + 2) + 5 * (args.steps + 2)   # five schedules, each primed
     if not cfg.prepopulate:
         headroom = total_keys
     else:
