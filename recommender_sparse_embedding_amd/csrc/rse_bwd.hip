@@ -156,6 +156,7 @@ __global__ __launch_bounds__(PAIRS_BLOCK) void k_pairs(const int64_t* row_off, c
                                                        int32_t n_tables, int64_t capacity, uint32_t invalid,
                                                        uint32_t* keys, uint32_t* vals, Ctr* ctr, int32_t* status,
                                                        SortPrep sp, int passes, int width) {
+    latency_bound_priority();
     __shared__ uint32_t s_hist[SORT_MAX_PASSES * SORT_MAX_BINS];
     __shared__ int64_t s_off[PAIRS_BAGS + 1];
     __shared__ int s_bad;
@@ -433,6 +434,7 @@ __device__ __forceinline__ uint64_t block_scan_u64(uint64_t v, uint64_t* s_wsum,
 }
 
 __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
+    latency_bound_priority();
     __shared__ uint32_t s_keys[IX_WIN];
     __shared__ unsigned long long s_head[IX_MASKS];
     __shared__ uint64_t s_wsum[IX_BLOCK / WAVE];

@@ -222,6 +222,7 @@ __device__ __forceinline__ void probe_full(const ProbeArgs& a, int64_t i, uint64
 // time.  Most lookups of a steady-state batch are settled by (2), which costs
 // three dependent memory round trips per 64 lookups.
 __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
+    latency_bound_priority();
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
     const bool ok_bounds = load_bounds(sb, a.bounds, a.stride, a.n_tables, a.n_ids);
     if (!ok_bounds) {

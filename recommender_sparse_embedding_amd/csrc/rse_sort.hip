@@ -78,6 +78,7 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
                                                 uint32_t* keys_out, uint32_t* vals_out, int64_t n, int shift,
                                                 int width, const uint32_t* totals, uint32_t* state,
                                                 uint32_t* tile_ctr, uint32_t* error, uint32_t n_tiles) {
+    latency_bound_priority();
     __shared__ uint32_t s_wcnt[SWAVES][SORT_MAX_BINS];   // wave running counts -> wave prefixes
     __shared__ uint32_t s_cnt[SORT_MAX_BINS];            // tile count per digit
     __shared__ uint32_t s_pre[SORT_MAX_BINS];            // tile-local exclusive prefix per digit
