@@ -15,7 +15,7 @@
 //   optimizer fused in -> combine of long segments.
 //
 // Segmented reduction.  A segment is all lookups of one row (a run of the
-// sorted keys).  An index kernel classifies every segment once: one lookup,
+// sorted keys).  An index kernel classifies every segment: one lookup,
 // 2..LONG_T lookups ("short"), or longer ("long", whose head is listed as
 // owner); the first two kinds go to lists.  The work kernel then runs three
 // kinds of blocks side by side:
@@ -27,7 +27,9 @@
 //     all their rows (weights + state) and gradient rows at once;
 //   - short: each group takes one short segment, loads its row, sums its
 //     gradient rows 4-8 at a time in lookup order, and updates the row.
-// The combine kernel adds each long segment's carries in a fixed order
+// After each window of pieces, the work kernel adds every run of one long
+// segment's piece partials into the run's first piece (in piece order); the
+// combine kernel adds those run sums of each long segment in a fixed order
 // (round-robin over a block's groups, then group order) and updates its row.
 // The lists' order depends on timing, but every segment is reduced and
 // updated independently, so results do not.  Only integer atomics are used.
