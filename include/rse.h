@@ -226,8 +226,13 @@ int rse_idmap_export(rse_idmap* map, int64_t* d_keys_out, int32_t* d_table_out,
  * out[b, t, :] = sum over the rows of bag j = t*batch + b ("DLRM ... 2.1":
  * EmbeddingBag sum), divided by the bag length for RSE_MEAN.  Rows are
  * accumulated in fp64 in bag order and rounded once to fp32; an empty bag
- * gives 0; offset -1 contributes nothing.  n_ids must equal
- * bag_offsets[n_tables*batch].
+ * gives 0; offset -1 contributes nothing.  bag_offsets[0] must be 0 and
+ * bag_offsets[n_tables*batch] must equal n_ids.  Malformed offsets (those
+ * endpoints, a decreasing pair, an offset outside [0, n_ids]) and rows at or
+ * beyond the blocks' capacity set the blocks' sticky status to
+ * RSE_ERR_BAD_INPUT; the bags they concern are skipped (their output is not
+ * written) or the row is left out of the sum, and nothing is read out of
+ * bounds.
  */
 int embedding_bag_fwd(const rse_blocks* blocks, const int64_t* d_row_off, int64_t n_ids,
                       const int64_t* d_bag_offsets, int32_t n_tables, int64_t batch,

@@ -17,6 +17,7 @@ missing (there is no CPU fallback).
 from __future__ import annotations
 
 import ctypes
+import weakref
 from dataclasses import dataclass
 
 import torch
@@ -101,12 +102,9 @@ class EmbeddingBlocks:
               "rse_blocks_create")
         self.handle = h
         self.chunks: list[torch.Tensor] = []
-
-    def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            lib.rse_blocks_destroy(h)
-            self.handle = None
+        # the handle holds host memory only; freed when the object goes, or
+        # at interpreter exit (before module globals are torn down)
+        self._finalizer = weakref.finalize(self, lib.rse_blocks_destroy, h)
 
     @property
     def state_per_elem(self) -> int:
@@ -173,12 +171,7 @@ class IdMap:
                                    int(merged), hash_seed, _stream(stream)), "rse_idmap_create")
         self.handle = h
         self._ws = None
-
-    def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            lib.rse_idmap_destroy(h)
-            self.handle = None
+        self._finalizer = weakref.finalize(self, lib.rse_idmap_destroy, h)
 
     def workspace(self, n_ids: int) -> torch.Tensor:
         sz = ctypes.c_size_t()
@@ -213,6 +206,17 @@ def idmap_find_or_insert(idmap: IdMap, blocks: EmbeddingBlocks, ids: torch.Tenso
                          stride: int, n_tables: int, row_off: torch.Tensor, n_new: torch.Tensor,
                          insert_missing: bool = True, ws: torch.Tensor | None = None, stream=None):
     """Table t's lookups are ids[bounds[t*stride] : bounds[(t+1)*stride]]."""
+    # sizes first: the kernels write row_off[i] for every lookup i and read
+    # bounds[t * stride] for t <= n_tables
+    if row_off.numel() != ids.numel():
+        raise ValueError(f"row_off must hold one offset per id ({ids.numel()}), got {row_off.numel()}")
+    if stride <= 0 or n_tables <= 0:
+        raise ValueError("stride and n_tables must be positive")
+    if bounds.numel() < n_tables * stride + 1:
+        raise ValueError(f"bounds must hold at least n_tables * stride + 1 = {n_tables * stride + 1} entries, "
+                         f"got {bounds.numel()}")
+    if n_new.numel() < 1:
+        raise ValueError("n_new must hold one int64")
     _need(ids, torch.int64, "ids")
     _need(bounds, torch.int64, "bounds")
     _need(row_off, torch.int64, "row_off")
@@ -228,13 +232,13 @@ def idmap_find_or_insert(idmap: IdMap, blocks: EmbeddingBlocks, ids: torch.Tenso
 def embedding_bag_fwd(blocks: EmbeddingBlocks, row_off: torch.Tensor, bag_offsets: torch.Tensor,
                       n_tables: int, batch: int, pooling: int, out: torch.Tensor, stream=None):
     """out [batch, n_tables, dim] fp32 = pooled rows of each bag."""
-    _need(row_off, torch.int64, "row_off")
-    _need(bag_offsets, torch.int64, "bag_offsets")
-    _need(out, torch.float32, "out")
     if out.numel() != batch * n_tables * blocks.dim:
         raise ValueError("out must hold batch * n_tables * dim floats")
     if bag_offsets.numel() != n_tables * batch + 1:
         raise ValueError("bag_offsets must hold n_tables * batch + 1 entries")
+    _need(row_off, torch.int64, "row_off")
+    _need(bag_offsets, torch.int64, "bag_offsets")
+    _need(out, torch.float32, "out")
     check(lib.embedding_bag_fwd(blocks.handle, _ptr(row_off), row_off.numel(), _ptr(bag_offsets),
                                 n_tables, batch, pooling, _ptr(out), _stream(stream)), "embedding_bag_fwd")
 

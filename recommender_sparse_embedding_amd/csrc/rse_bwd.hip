@@ -962,6 +962,8 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
     int bits = bit_length((uint64_t)capacity);
     if (bits < 1) bits = 1;
     const uint32_t invalid = bits >= 32 ? 0xFFFFFFFFu : ((1u << bits) - 1u);
+    // every host-side check comes before the first launch
+    if (!sort_supported(n_ids, bits)) return RSE_ERR_UNSUPPORTED;
     rse_bwd_plan plan;
     plan.n_ids = n_ids;
     plan.n_bags = n_bags;

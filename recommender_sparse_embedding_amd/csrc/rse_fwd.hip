@@ -89,6 +89,14 @@ __device__ __forceinline__ void flag_bad(const FwdArgs& a) {
     atomicCAS(a.status, 0, (int32_t)RSE_ERR_BAD_INPUT);
 }
 
+// The bag offsets must start at 0 and end at n_ids; checked once per call
+// (block 0).  Offsets that break this are reported, and every bag is still
+// bounded by [0, n_ids], so nothing is read out of bounds.
+__device__ __forceinline__ void check_endpoints(const FwdArgs& a) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (a.bag_off[0] != 0 || a.bag_off[a.n_bags] != a.n_ids))
+        flag_bad(a);
+}
+
 // Row loads are issued unconditionally (a missing or rejected row reads a
 // dummy row and is masked out of the sum), so all UNROLL loads of a group
 // are in flight together instead of being serialised behind branches.
@@ -141,6 +149,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
     static_assert(BPG <= LPR && BPG <= 32, "one lane per bag of a chunk");
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
+    check_endpoints(a);
     const int lane = lane_id();
     const int g = lane / LPR;
     const int li = lane % LPR;
@@ -228,6 +237,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
     stage_chunks(s_chunks, a.rv);
+    check_endpoints(a);
     const int lane = lane_id();
     const int g = lane / LPR;
     const int li = lane % LPR;
@@ -325,6 +335,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
     constexpr int64_t STEP = (int64_t)GROUPS * UNROLL;
     __shared__ uint64_t s_chunks[LDS_CHUNKS];
     stage_chunks(s_chunks, a.rv);
+    check_endpoints(a);
     const int lane = lane_id();
     const int g = lane / LPR;
     const int li = lane % LPR;

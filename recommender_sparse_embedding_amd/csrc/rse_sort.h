@@ -38,6 +38,10 @@ struct SortPrep {
 };
 SortPrep sort_prep(void* ws, int64_t n);
 
+// Whether radix_sort_pairs accepts n pairs of `bits`-bit keys (host only;
+// callers check this before enqueueing anything).
+bool sort_supported(int64_t n, int bits);
+
 // Sorts (k0, v0) by the low `bits` bits, stably, ping-ponging through
 // (k1, v1); the result ends in (k1, v1) if *result_in_alt.  Requires the
 // digit totals of every pass to be in prep.totals (summed over its copies)

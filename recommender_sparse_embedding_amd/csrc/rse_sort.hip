@@ -267,11 +267,17 @@ SortPrep sort_prep(void* ws, int64_t n) {
     return p;
 }
 
+bool sort_supported(int64_t n, int bits) {
+    // a digit count or an inclusive prefix is at most n and must fit the
+    // 30-bit value field of the look-back state
+    return bits >= 1 && bits <= 32 && sort_plan(bits).passes <= SORT_MAX_PASSES && n >= 0 &&
+           n <= (int64_t)ST_VAL;
+}
+
 int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n, int bits,
                      void* ws, bool* result_in_alt, hipStream_t s) {
+    if (!sort_supported(n, bits)) return RSE_ERR_UNSUPPORTED;
     const SortPlan plan = sort_plan(bits);
-    if (plan.passes > SORT_MAX_PASSES) return RSE_ERR_UNSUPPORTED;
-    if (n >= (int64_t)ST_VAL) return RSE_ERR_UNSUPPORTED;
     const int64_t n_tiles = tiles_of(n);
     SortPrep p = sort_prep(ws, n);
     bool alt = false;

@@ -145,3 +145,82 @@ def compare_rows(gpu: GpuTables, orc, prev_w, offs, rtol, what):
     if s_r.size:
         assert_close(s_g, s_r, np.abs(s_r.astype(np.float64)) + 1e-30, 1e-5, what + " state")
     return w_g, w_r
+
+
+class ChunkSnapshot:
+    """State of every chunk of a blocks object, kept on the device;
+    changed_rows() lists (ascending, global row numbers) the rows whose
+    bytes differ from it, weights and state alike.  Bytes of a chunk past
+    its last row must not change either.
+
+    mode "copy" keeps a clone of the chunks and compares bytes exactly;
+    mode "fingerprint" (for tables too large to hold twice) keeps one 64-bit
+    linear hash per row, sum of the row's 8-byte words times fixed random
+    odd multipliers mod 2^64: a changed row keeps its fingerprint only if the
+    change lies in the kernel of that map, about 2^-64 for a random change.
+    "auto" copies when the device has room for a second copy."""
+
+    def __init__(self, blocks, mode="auto"):
+        self.blocks = blocks
+        R, rb = blocks.rows_per_chunk, blocks.row_bytes
+        total = sum(c.numel() for c in blocks.chunks)
+        if mode == "auto":
+            free, _ = torch.cuda.mem_get_info()
+            mode = "copy" if total + (8 << 30) < free else "fingerprint"
+        self.mode = mode
+        if mode == "copy":
+            self.copies = [c.clone() for c in blocks.chunks]
+        else:
+            g = torch.Generator().manual_seed(12345)
+            w = torch.randint(-(2**62), 2**62, (rb // 8,), generator=g, dtype=torch.int64) * 2 + 1
+            self.w = w.to(blocks.chunks[0].device)
+            self.copies = [self._fp(c) for c in blocks.chunks]
+
+    def _fp(self, c):
+        R, rb = self.blocks.rows_per_chunk, self.blocks.row_bytes
+        n = R * rb
+        rows = c[:n].view(torch.int64).view(R, rb // 8)
+        fp = (rows * self.w).sum(dim=1)
+        tail = c[n:].clone() if c.numel() > n else None
+        return fp, tail
+
+    def changed_rows(self) -> np.ndarray:
+        R, rb = self.blocks.rows_per_chunk, self.blocks.row_bytes
+        n = R * rb
+        out = []
+        for k, (cur, old) in enumerate(zip(self.blocks.chunks, self.copies)):
+            if self.mode == "copy":
+                a = cur[:n].view(torch.int32).view(R, rb // 4)
+                b = old[:n].view(torch.int32).view(R, rb // 4)
+                diff = (a != b).any(dim=1)
+                tail_ok = cur.numel() <= n or torch.equal(cur[n:], old[n:])
+            else:
+                fp, tail = self._fp(cur)
+                diff = fp != old[0]
+                tail_ok = tail is None or torch.equal(tail, old[1])
+            assert tail_ok, f"bytes past the last row of chunk {k} changed"
+            ch = torch.nonzero(diff).flatten()
+            if ch.numel():
+                out.append(ch.cpu().numpy().astype(np.int64) + k * R)
+        return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def assert_only_touched_changed(snap: ChunkSnapshot, touched: np.ndarray, what: str):
+    """Every row outside `touched` keeps its bits exactly."""
+    changed = snap.changed_rows()
+    stray = np.setdiff1d(changed, touched)
+    assert stray.size == 0, f"{what}: {stray.size} rows outside the batch changed, first {stray[:8]}"
+
+
+def assert_never_touched_match_oracle(gpu, orc, ever_touched: np.ndarray, what: str, batch_rows=1 << 18):
+    """Rows never updated hold the oracle's values bit for bit (their key-
+    derived initial weights and zero state)."""
+    n = orc.n_rows
+    rest = np.setdiff1d(np.arange(n, dtype=np.int64), ever_touched)
+    for a in range(0, len(rest), batch_rows):
+        part = rest[a:a + batch_rows]
+        w_g, s_g = gpu.rows(part)
+        w_r, s_r = orc.get_rows(part)
+        assert np.array_equal(w_g.view(np.uint32), w_r.view(np.uint32)), f"{what}: untouched weights differ"
+        assert np.array_equal(s_g.view(np.uint32), s_r.view(np.uint32)), f"{what}: untouched state differs"
+    return len(rest)

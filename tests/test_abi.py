@@ -108,3 +108,23 @@ def test_bwd_plan_layout_matches_header():
     body = re.search(r"typedef struct rse_bwd_plan \{(.*?)\} rse_bwd_plan;", text, flags=re.S).group(1)
     fields = re.findall(r"^\s*(\w+)\s+(\w+);", body, flags=re.M)
     assert [f for _, f in fields] == [n for n, _ in RseBwdPlan._fields_]
+
+
+def test_binding_rejects_short_buffers_before_any_call():
+    """The find writes one offset per lookup and reads the table bounds at
+    t * stride for t <= n_tables: buffers too short for that are refused in
+    the binding, before the library is called (so no device work starts)."""
+    import torch
+
+    import recommender_sparse_embedding_amd as rse
+
+    ids = torch.zeros(10, dtype=torch.int64)
+    bounds = torch.tensor([0, 4, 10], dtype=torch.int64)
+    n_new = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises(ValueError, match="row_off"):
+        rse.idmap_find_or_insert(None, None, ids, bounds, 1, 2, torch.zeros(9, dtype=torch.int64), n_new)
+    with pytest.raises(ValueError, match="bounds"):
+        rse.idmap_find_or_insert(None, None, ids, bounds, 2, 2, torch.zeros(10, dtype=torch.int64), n_new)
+    with pytest.raises(ValueError, match="stride"):
+        rse.idmap_find_or_insert(None, None, ids, bounds, 0, 2, torch.zeros(10, dtype=torch.int64), n_new)
+

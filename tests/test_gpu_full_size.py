@@ -11,6 +11,10 @@ rows of sampled keys (a fresh oracle table fed exactly the lookups of those
 keys, in lookup order: a row's update depends only on its key's initial
 value and its own lookups), and sampled untouched rows against their initial
 values.
+
+In every workload, every row outside the step's batch is compared on the
+device before and after the update (a copy of all chunks, or for the 154 GB
+table a 64-bit fingerprint per row): no byte of such a row may change.
 """
 
 from __future__ import annotations
@@ -23,7 +27,7 @@ import pytest
 import torch
 
 import synth
-from harness import assert_close, make_oracle, pooled_magnitude, rtol_for
+from harness import ChunkSnapshot, assert_close, assert_only_touched_changed, make_oracle, pooled_magnitude, rtol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +78,8 @@ class Full:
 
     def step(self, ids: np.ndarray, bo: np.ndarray, G: np.ndarray):
         """find; the backward's prepare on a second stream beside the
-        forward; apply.  Returns row offsets, n_new, pooled output, U."""
+        forward; apply.  Returns row offsets, n_new, pooled output, U, and a
+        snapshot of every chunk taken after the find (before the update)."""
         rse, cfg, dev = self.rse, self.cfg, self.dev
         T, B, D = cfg.n_tables, cfg.batch, cfg.dim
         t_ids = torch.from_numpy(ids).to(dev)
@@ -83,6 +88,7 @@ class Full:
         ro = torch.empty_like(t_ids)
         n_new = torch.zeros(1, dtype=torch.int64, device=dev)
         rse.idmap_find_or_insert(self.map, self.blk, t_ids, t_bo, B, T, ro, n_new, ws=self.map.workspace(len(ids)))
+        snap = ChunkSnapshot(self.blk)
         main = torch.cuda.current_stream()
         side = torch.cuda.Stream(device=dev)
         found = torch.cuda.Event()
@@ -104,7 +110,7 @@ class Full:
         idm_st, _ = self.map.status()
         _, st = self.blk.status()
         assert idm_st == 0 and st == 0, (idm_st, st)
-        return ro.cpu().numpy(), int(n_new.item()), out.cpu().numpy(), int(nu.item())
+        return ro.cpu().numpy(), int(n_new.item()), out.cpu().numpy(), int(nu.item()), snap
 
     def rows(self, offs: np.ndarray):
         w, s = self.blk.read_rows(torch.from_numpy(np.ascontiguousarray(offs, np.int64)).to(self.dev))
@@ -134,7 +140,7 @@ def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float):
     for s in range(steps):
         ids, bo = wl.batch_inputs(s)
         G = wl.grad(s)
-        ro_g, nn_g, out_g, nu_g = gpu.step(ids, bo, G)
+        ro_g, nn_g, out_g, nu_g, snap = gpu.step(ids, bo, G)
         ro_r, nn_r = orc.find_or_insert(ids, bo, cfg.batch)
         assert nn_g == nn_r, (nn_g, nn_r)
         assert np.array_equal(ro_g, ro_r), f"row offsets, step {s}"
@@ -154,6 +160,10 @@ def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float):
         w_r, s_r = orc.get_rows(offs)
         _compare_updated(w_g, s_g, prev_w, w_r, s_r, rtol, f"step {s}")
         ever = np.union1d(ever, offs)
+        # every row outside the batch keeps its bytes (all rows, on the device)
+        assert_only_touched_changed(snap, offs, f"step {s}")
+        _say(f"  step {s}: every row outside the batch unchanged ({snap.mode} of all chunks)")
+        del snap
         untouched = np.setdiff1d(rng.choice(n_rows, 40_000, replace=False), ever)[:20_000]
         w_g, s_g = gpu.rows(untouched)
         w_r, s_r = orc.get_rows(untouched)
@@ -217,7 +227,7 @@ def _sampled_checks(cfg: synth.Config, map_load: float, n_rows_sample: int, n_ba
     _say(f"  {cfg.name}: {int(wl.card.sum())} rows, {len(ids)} lookups")
     gpu = Full(cfg, wl, map_load)
     _say("  prepopulated")
-    ro_g, nn_g, out_g, nu_g = gpu.step(ids, bo, G)
+    ro_g, nn_g, out_g, nu_g, snap = gpu.step(ids, bo, G)
     rtol = rtol_for(cfg.wdtype)
     # properties at full size: offset = insertion index (tables inserted in
     # order, each in generation order), no new keys, touched-row count
@@ -229,6 +239,10 @@ def _sampled_checks(cfg: synth.Config, map_load: float, n_rows_sample: int, n_ba
     rowid = expect
     assert nu_g == len(np.unique(rowid))
     _say("  offsets and counts hold")
+    assert_only_touched_changed(snap, np.unique(rowid), "the step")
+    _say(f"  every row outside the batch unchanged ({snap.mode} of all chunks)")
+    del snap
+    _free()
     lookup_bag = np.repeat(np.arange(T * B), np.diff(bo))
     rng = np.random.default_rng(5)
     # pooled outputs of sampled samples b (all tables): a fresh oracle

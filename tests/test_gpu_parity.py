@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import synth
-from harness import GpuTables, assert_close, compare_rows, make_oracle, pooled_magnitude, rtol_for
+from harness import (ChunkSnapshot, GpuTables, assert_close, assert_never_touched_match_oracle,
+                     assert_only_touched_changed, compare_rows, make_oracle, pooled_magnitude, rtol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,21 +20,27 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64, split=False):
+def run_steps(cfg, steps, prepop_chunk=None, max_new=None, split=False, rows_per_chunk_log2=14):
+    """Free-running steps against the oracle: row offsets and new-key counts
+    bit-exact, pooled outputs and updated rows within tolerance, the set of
+    rows whose bytes change in each update a subset of the rows in the batch
+    (every row compared on the device), and at the end every row never
+    updated bit-identical to the oracle's."""
     wl = synth.Workload(cfg)
     orc = make_oracle(cfg)
     L_est = int(cfg.n_bags * (cfg.bag[2] if cfg.bag[0] == "uniform" else
                               cfg.bag[1] * 3 if cfg.bag[0] == "poisson" else cfg.bag[1]))
     max_rows = int(wl.card.sum() if cfg.prepopulate else 0) + (max_new or L_est * steps) + 1024
     extra = (max_new or L_est * steps) if (cfg.fresh_frac > 0 or not cfg.prepopulate) else 0
-    gpu = GpuTables(cfg, wl.card, max_rows, extra_keys=extra, split=split)
+    gpu = GpuTables(cfg, wl.card, max_rows, extra_keys=extra, split=split,
+                    rows_per_chunk_log2=rows_per_chunk_log2)
     rtol = rtol_for(cfg.wdtype)
     for ids, bounds in wl.prepopulation(prepop_chunk):
         ro_r, nn_r = orc.find_or_insert(ids, bounds, 1)
         ro_g, nn_g = gpu.find_or_insert(ids, bounds, 1)
         assert nn_g == nn_r
         assert np.array_equal(ro_g.cpu().numpy(), ro_r)
-    rng = np.random.default_rng(5)
+    ever = np.zeros(0, np.int64)
     for step in range(steps):
         _say(f"  step {step}")
         ids, bo = wl.batch_inputs(step)
@@ -41,6 +48,7 @@ def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64, s
         ro_g, nn_g = gpu.find_or_insert(ids, bo, cfg.batch)
         assert nn_g == nn_r, (nn_g, nn_r)
         assert np.array_equal(ro_g.cpu().numpy(), ro_r), "row offsets"
+        snap = ChunkSnapshot(gpu.blocks)
         gpu.prepare(ro_g, bo)
         out_g = gpu.fwd(ro_g, bo)
         out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
@@ -53,18 +61,15 @@ def run_steps(cfg, steps, prepop_chunk=None, max_new=None, check_untouched=64, s
             G_g = torch.from_numpy(G_r).to(gpu.dev)
         offs = np.unique(ro_r[ro_r >= 0])
         prev_w, _ = orc.get_rows(offs)
-        n_rows = orc.n_rows
         U_r = orc.bwd_update(ro_r, bo, cfg.batch, G_r, cfg.pooling)
         U_g = gpu.bwd(ro_g, bo, G_g)
         assert U_g == U_r == len(offs)
         compare_rows(gpu, orc, prev_w, offs, rtol, f"step {step}")
-        if check_untouched and n_rows > len(offs):
-            untouched = np.setdiff1d(rng.choice(n_rows, min(n_rows, check_untouched * 4), replace=False), offs)
-            untouched = untouched[:check_untouched]
-            w_g, s_g = gpu.rows(untouched)
-            w_r, s_r = orc.get_rows(untouched)
-            assert np.array_equal(w_g.view(np.uint32), w_r.view(np.uint32)), "untouched rows changed"
-            assert np.array_equal(s_g.view(np.uint32), s_r.view(np.uint32))
+        assert_only_touched_changed(snap, offs, f"step {step}")
+        del snap
+        ever = np.union1d(ever, offs)
+    n_rest = assert_never_touched_match_oracle(gpu, orc, ever, f"after {steps} steps")
+    _say(f"  {len(ever)} rows updated, {n_rest} never-updated rows bit-identical to the oracle")
     return gpu, orc
 
 
@@ -202,6 +207,24 @@ def test_update_variants(optim, wdtype):
     run_steps(cfg, 3)
 
 
+@pytest.mark.parametrize("which", ["one_hot", "short_bags", "long_bags"])
+def test_global_chunk_table_path(which):
+    """Blocks of more than 512 chunks (16-row chunks here) address rows
+    through the chunk table in device memory instead of its LDS copy: find,
+    insert and row init, the one-hot, group-per-bags and wave-per-bag
+    forwards, and the update's one-lookup, short and long segments."""
+    if which == "one_hot":      # one-hot forward, Adagrad dim 128
+        cfg = synth.config(2, n_tables=4, batch=4096, cardinality=("fixed", 4000))
+        gpu, _ = run_steps(cfg, 2, rows_per_chunk_log2=4, max_new=1024)
+    elif which == "short_bags":  # bags U[1,8]: group-per-bags forward, SGD dim 16, tables start empty
+        cfg = synth.config(1, n_tables=8, batch=1024, cardinality=("fixed", 2000))
+        gpu, _ = run_steps(cfg, 3, rows_per_chunk_log2=4, max_new=16000)
+    else:                        # bags U[1,100]: wave-per-bag forward, mean, Adam dim 64, fresh ids
+        cfg = synth.config(3, n_tables=2, batch=256, cardinality=("fixed", 8000))
+        gpu, _ = run_steps(cfg, 2, rows_per_chunk_log2=4, max_new=2048)
+    assert len(gpu.blocks.chunks) > 512
+
+
 def test_config1_multi_hot_sgd_full():
     """8 tables, dim 16, batch 1024, bags U[1,8], Zipf(1.05) over 1e5 keys,
     sum-of-squares loss, SGD 0.1, tables start empty: 10 free-running steps."""
@@ -276,7 +299,7 @@ def test_run_to_run_bit_identical():
     cfg = synth.config(2, n_tables=4, batch=4096, cardinality=("fixed", 3000))
     res = []
     for _ in range(2):
-        gpu, orc = run_steps(cfg, 2, check_untouched=0)
+        gpu, orc = run_steps(cfg, 2)
         w, s = gpu.rows(np.arange(orc.n_rows))
         res.append((w.view(np.uint32).copy(), s.view(np.uint32).copy()))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
@@ -395,6 +418,7 @@ def test_pipelined_next_find_overlaps_apply(which, schedule):
     assert_close(w_g, w_r, np.abs(w_r.astype(np.float64)) + 1e-3, rtol_for(cfg.wdtype), "rows after the steps")
     if s_r.size:
         assert_close(s_g, s_r, np.abs(s_r.astype(np.float64)) + 1e-30, 1e-5, "state after the steps")
+    assert_never_touched_match_oracle(gpu, orc, offs, "after the pipelined steps")
 
 
 def _small_split_setup(rows_per_chunk_log2=4, n_chunks=1):
@@ -597,3 +621,43 @@ def test_bad_inputs_are_reported_not_faulted():
     assert b.status()[1] == -9 and int(nu.item()) == 0
     w1, _ = b.read_rows(torch.tensor([0, 1], device="cuda"))
     assert torch.equal(w0, w1)                                  # nothing updated
+
+
+def test_objects_alive_at_interpreter_exit_are_released_cleanly():
+    """A process that ends while an IdMap and an EmbeddingBlocks are still
+    alive exits with status 0 and prints no error from their release."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import recommender_sparse_embedding_amd as rse\n"
+            "m = rse.IdMap([64], max_load=0.7)\n"
+            "b = rse.EmbeddingBlocks(16, rse.F32, rse.SGD, 6).grow(1)\n"
+            "print('alive', flush=True)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "alive" in r.stdout, r.stderr
+    assert "Exception ignored" not in r.stderr and "Error" not in r.stderr.replace("amdgpu.ids", ""), r.stderr
+
+
+def test_forward_offset_endpoints_checked_on_device():
+    """bag_offsets[0] must be 0 and bag_offsets[n_bags] must equal n_ids:
+    the forward reports either violation in the blocks' sticky status (every
+    read stays within [0, n_ids]), for the one-hot and the multi-hot
+    schedules alike."""
+    import recommender_sparse_embedding_amd as rse
+
+    b = rse.EmbeddingBlocks(8, 0, 0, 6, device="cuda").grow(1)
+    m = rse.IdMap([64], max_load=0.7, device="cuda")
+    n_new = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ids = torch.tensor([5, 6, 7], dtype=torch.int64, device="cuda")
+    ro = torch.empty_like(ids)
+    rse.idmap_find_or_insert(m, b, ids, torch.tensor([0, 3], device="cuda"), 1, 1, ro, n_new)
+    out = torch.zeros((2, 1, 8), dtype=torch.float32, device="cuda")
+    for bo in ([1, 2, 3], [0, 1, 2], [0, 2, 2], [1, 1, 3]):   # one-hot-like and multi-hot, bad ends
+        b.clear_status()
+        rse.embedding_bag_fwd(b, ro, torch.tensor(bo, device="cuda"), 1, 2, 0, out)
+        assert b.status()[1] == -9, bo
+    b.clear_status()
+    rse.embedding_bag_fwd(b, ro, torch.tensor([0, 2, 3], device="cuda"), 1, 2, 0, out)
+    assert b.status()[1] == 0
