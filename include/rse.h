@@ -206,6 +206,27 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
                          int32_t n_tables, int32_t insert_missing, int64_t* d_row_off_out,
                          int64_t* d_n_new_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/*
+ * idmap_find_or_insert without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results, errors and
+ * stream semantics as idmap_find_or_insert; the scratch is a static array of
+ * the library on each GPU (about 52 MiB, allocated when the library's code
+ * is loaded on that GPU and held until the process ends), so the call
+ * allocates nothing.  It uses the scratch of the current device (hipGetDevice);
+ * `stream` must belong to that device.
+ *
+ * Limit: n_ids <= RSE_NOALLOC_MAX_IDS, else RSE_ERR_WORKSPACE with nothing
+ * enqueued.  All calls on one GPU share its scratch: two calls that may run
+ * at the same time on that GPU (different streams, or different host threads)
+ * race and give wrong results; order them on one stream.
+ */
+#define RSE_NOALLOC_MAX_IDS 2097152LL
+int idmap_find_or_insert_noalloc(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids,
+                                 int64_t n_ids, const int64_t* d_bounds, int64_t stride,
+                                 int32_t n_tables, int32_t insert_missing,
+                                 int64_t* d_row_off_out, int64_t* d_n_new_out, void* stream);
+
 /* Sticky status and per-table key counts (host array of the map's n_tables,
  * may be NULL).  Synchronises `stream`. */
 int rse_idmap_status(rse_idmap* map, int32_t* status_out, int64_t* n_keys_out, void* stream);

@@ -229,6 +229,31 @@ def idmap_find_or_insert(idmap: IdMap, blocks: EmbeddingBlocks, ids: torch.Tenso
                                    _ptr(ws), ws.numel(), _stream(stream)), "idmap_find_or_insert")
 
 
+NOALLOC_MAX_IDS = 2097152
+
+
+def idmap_find_or_insert_noalloc(idmap: IdMap, blocks: EmbeddingBlocks, ids: torch.Tensor, bounds: torch.Tensor,
+                                 stride: int, n_tables: int, row_off: torch.Tensor, n_new: torch.Tensor,
+                                 insert_missing: bool = True, stream=None):
+    """idmap_find_or_insert over the library's static per-GPU scratch (no
+    workspace, no allocation); at most NOALLOC_MAX_IDS lookups, and calls on
+    one GPU must not overlap."""
+    if row_off.numel() != ids.numel():
+        raise ValueError(f"row_off must hold one offset per id ({ids.numel()}), got {row_off.numel()}")
+    if stride <= 0 or n_tables <= 0:
+        raise ValueError("stride and n_tables must be positive")
+    if bounds.numel() < n_tables * stride + 1:
+        raise ValueError(f"bounds must hold at least n_tables * stride + 1 = {n_tables * stride + 1} entries, "
+                         f"got {bounds.numel()}")
+    _need(ids, torch.int64, "ids")
+    _need(bounds, torch.int64, "bounds")
+    _need(row_off, torch.int64, "row_off")
+    _need(n_new, torch.int64, "n_new")
+    check(lib.idmap_find_or_insert_noalloc(idmap.handle, blocks.handle, _ptr(ids), ids.numel(), _ptr(bounds),
+                                           stride, n_tables, int(bool(insert_missing)), _ptr(row_off),
+                                           _ptr(n_new), _stream(stream)), "idmap_find_or_insert_noalloc")
+
+
 def embedding_bag_fwd(blocks: EmbeddingBlocks, row_off: torch.Tensor, bag_offsets: torch.Tensor,
                       n_tables: int, batch: int, pooling: int, out: torch.Tensor, stream=None):
     """out [batch, n_tables, dim] fp32 = pooled rows of each bag."""
@@ -321,7 +346,7 @@ def trace_stop():
 
 __all__ = [
     "F32", "BF16", "SGD", "ADAGRAD", "ADAM", "SUM", "MEAN", "Optim", "EmbeddingBlocks", "IdMap",
-    "RseError", "blocks_grow", "idmap_find_or_insert", "embedding_bag_fwd", "embedding_bag_bwd_update",
+    "RseError", "blocks_grow", "idmap_find_or_insert", "idmap_find_or_insert_noalloc", "embedding_bag_fwd", "embedding_bag_bwd_update",
     "embedding_bag_bwd_prepare", "embedding_bag_bwd_apply",
     "bwd_workspace", "row_bytes", "status_str", "lib", "trace_start", "trace_stop", "K_PROBE", "K_FWD",
     "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE",

@@ -22,6 +22,7 @@
 // keys one by one in lookup order, and independent of thread timing.  Only
 // integer atomics are used.  Kernels after the probe exit at once when the
 // batch has no miss.
+#include <mutex>
 #include <new>
 
 #include "rse_host.h"
@@ -799,10 +800,16 @@ int rse_idmap_workspace_size(int64_t n_ids, size_t* bytes_out) {
     return RSE_OK;
 }
 
-int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids, int64_t n_ids,
-                         const int64_t* d_bounds, int64_t stride, int32_t n_tables,
-                         int32_t insert_missing, int64_t* d_row_off_out, int64_t* d_n_new_out,
-                         void* d_ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The find-or-insert chain over a given workspace (caller memory or the
+// library's static scratch).
+int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids, int64_t n_ids,
+                        const int64_t* d_bounds, int64_t stride, int32_t n_tables,
+                        int32_t insert_missing, int64_t* d_row_off_out, int64_t* d_n_new_out,
+                        void* d_ws, size_t ws_bytes, void* stream) {
     if (!map || !blocks || !d_bounds || !d_n_new_out || !d_ws) return RSE_ERR_INVALID_ARG;
     if (n_ids < 0 || stride <= 0 || n_tables <= 0) return RSE_ERR_INVALID_ARG;
     if (n_ids > 0 && (!d_ids || !d_row_off_out)) return RSE_ERR_INVALID_ARG;
@@ -902,6 +909,63 @@ int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_id
     else
         hipLaunchKernelGGL(k_finish<false>, finish_grid, dim3(256), 0, s, fa);
     return launch_status();
+}
+
+// ------------------------------------------------- allocation-free find --
+// Scratch of idmap_find_or_insert_noalloc: one copy per GPU, allocated by
+// the runtime when the library's code object is loaded on that GPU and held
+// until the process ends.  Its size is the workspace of
+// RSE_NOALLOC_MAX_IDS lookups (checked when a device is first used).
+constexpr size_t NOALLOC_SCRATCH_BYTES = 52ull << 20;
+__device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];   // device address of `scratch` per GPU
+
+// Device address of the current GPU's scratch.  In host code `scratch` is a
+// host-side stand-in, never a device address: kernels get this pointer.
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return RSE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        size_t need = 0;
+        carve(nullptr, RSE_NOALLOC_MAX_IDS, &need);
+        if (need > NOALLOC_SCRATCH_BYTES) return RSE_ERR_UNSUPPORTED;
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RSE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int idmap_find_or_insert(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids, int64_t n_ids,
+                         const int64_t* d_bounds, int64_t stride, int32_t n_tables,
+                         int32_t insert_missing, int64_t* d_row_off_out, int64_t* d_n_new_out,
+                         void* d_ws, size_t ws_bytes, void* stream) {
+    return find_or_insert_impl(map, blocks, d_ids, n_ids, d_bounds, stride, n_tables, insert_missing,
+                               d_row_off_out, d_n_new_out, d_ws, ws_bytes, stream);
+}
+
+int idmap_find_or_insert_noalloc(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids, int64_t n_ids,
+                                 const int64_t* d_bounds, int64_t stride, int32_t n_tables,
+                                 int32_t insert_missing, int64_t* d_row_off_out, int64_t* d_n_new_out,
+                                 void* stream) {
+    if (!map || !blocks) return RSE_ERR_INVALID_ARG;
+    if (n_ids > RSE_NOALLOC_MAX_IDS) return RSE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const int rc = scratch_of_current_device(&ws);
+    if (rc) return rc;
+    // k_reset clears the scratch's counters and tile sums at the start of
+    // every call; everything else is written before it is read
+    return find_or_insert_impl(map, blocks, d_ids, n_ids, d_bounds, stride, n_tables, insert_missing,
+                               d_row_off_out, d_n_new_out, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int rse_idmap_status(rse_idmap* map, int32_t* status_out, int64_t* n_keys_out, void* stream) {
