@@ -1,25 +1,40 @@
-"""Benchmark: one training step of the sparse-embedding hot path on one MI355X.
+"""Benchmark: training steps of the sparse-embedding hot path on one MI355X.
 
 A step = idmap_find_or_insert -> embedding_bag_fwd -> embedding_bag_bwd_update
-over one batch of the click-log workload: 26 one-hot tables, dim 128 fp32,
-batch 65536, per-table cardinality log-uniform in [10, 4e7] (55.8M live rows
-for the seed used), Zipf(1.1) lookups over random 63-bit keys, Adagrad (lr
-0.01, eps 1e-8) with fp32 accumulator rows, N(0,1) upstream gradients.
-Inputs are synthetic, seeded, and resident in HBM before timing starts.
+over one batch, with inputs synthetic, seeded and resident in HBM before the
+timed region starts.  The default run measures all five workloads and prints
+ONE JSON line whose `value` is the click-log workload's lookups/s:
 
-Prints one JSON line: lookups/s (the metric), plus updated rows/s, the step's
-compulsory HBM bytes per second against the 8 TB/s peak, a roofline entry for
-the dominant kernel (timed live with HIP events on the library's stream) and
-the CPU oracle timed on the host.
+  1. multi-hot: 8 tables x batch 1024, bags U[1,8], dim 16 fp32, SGD, tables
+     start empty (new ids inserted on first sight), G = 2 * pooled output;
+  2. click-log (the headline): 26 one-hot tables x batch 65536, dim 128 fp32,
+     cardinalities log-uniform in [10, 4e7], Zipf(1.1), Adagrad;
+  3. behaviour sequence: 4 tables x batch 8192, bags U[1,100], mean pooling,
+     dim 64 fp32, Adam, 1% never-seen ids in every step;
+  4. billion-scale ID space: 2e8 live int64 keys at map load 0.7, batch
+     131072 x 50 uniform lookups, dim 64 fp32, Adam (154 GB of rows);
+  5. merged tables: 100 tables merged into one map keyed by (t << 56) | id,
+     bf16 weights + fp32 Adagrad state, dim 32, batch 32768, bags Poisson(20).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+Per workload: lookups/s and updated rows/s, the step's compulsory HBM bytes
+per second against the 8 TB/s peak, the segmented-update kernel's roofline
+(algorithmic bytes / its average launch time, timed live with HIP events on
+its stream; HBM traffic from committed rocprofv3 counter summaries when they
+were taken on the same kernel sources) and the CPU oracle timed on the host
+on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config N] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
 
 import argparse
+import gc
+import glob
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -29,6 +44,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+CHUNK_LOG2 = 20
+# map load of each workload's prepopulated key set (the billion-scale
+# workload is defined at 0.7)
+MAP_LOAD = {1: 0.5, 2: 0.5, 3: 0.5, 4: 0.7, 5: 0.5}
 
 
 def log(*a):
@@ -38,16 +57,16 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2, help="workload number (2 = click-log, the headline)")
-    p.add_argument("--batches", type=int, default=4, help="distinct batches cycled through")
+    p.add_argument("--config", type=int, default=0,
+                   help="run only this workload (1-5); default: all five, value = workload 2")
+    p.add_argument("--batches", type=int, default=4,
+                   help="distinct batches cycled through (workloads whose ids are all live)")
+    p.add_argument("--other-steps", type=int, default=10,
+                   help="timed steps of workloads 1, 3, 4 and 5 in the default run")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-steps", type=int, default=2)
-    p.add_argument("--map-load", type=float, default=0.5)
-    p.add_argument("--serial-bwd", action="store_true",
-                   help="report the serial schedule (find, fwd, bwd update on one stream) as the value instead "
-                        "of the lookahead one")
+    p.add_argument("--map-load", type=float, default=0.0, help="override the workload's map load")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (an elementwise kernel that reads and "
                         "writes each byte once), to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -69,14 +88,17 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 10}))
 
 
-def logical_bytes(cfg, L, U, row_bytes):
-    """Bytes the step moves with no reuse across lookups: the compulsory
-    bytes plus, for every lookup beyond the first of its row, the forward's
-    row-weight gather and one map slot."""
-    import synth
-
-    w_bytes = cfg.dim * (2 if cfg.wdtype == synth.BF16 else 4)
-    return compulsory_bytes(cfg, L, U, 0, row_bytes) + (L - U) * (w_bytes + 16)
+def kernel_sources_sha() -> str:
+    """Hash of the HIP sources and headers the library is built from: stored
+    counter summaries apply only to the kernels they were taken on."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "recommender_sparse_embedding_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "rse.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def compulsory_bytes(cfg, L, U, n_new, row_bytes):
@@ -88,107 +110,145 @@ def compulsory_bytes(cfg, L, U, n_new, row_bytes):
             + n_new * row_bytes)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def logical_bytes(cfg, L, U, n_new, row_bytes):
+    """Bytes the step moves with no reuse across lookups: the compulsory
+    bytes plus, for every lookup beyond the first of its row, the forward's
+    row-weight gather and one map slot."""
+    import synth
 
+    w_bytes = cfg.dim * (2 if cfg.wdtype == synth.BF16 else 4)
+    return compulsory_bytes(cfg, L, U, n_new, row_bytes) + (L - U) * (w_bytes + 16)
+
+
+def read_traffic(workload: int, sha: str):
+    """HBM bytes per launch of the segmented update from the committed
+    counter summary of this workload (profiles/seg_update_<name>.txt), or
+    None if absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"seg_update_{PROFILE_NAME[workload]}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.split("#")[0].strip()
+    if vals.get("kernel_sources_sha") != sha or "hbm_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["hbm_bytes_per_launch"]))
+
+
+PROFILE_NAME = {1: "multihot", 2: "clicklog", 3: "sequence", 4: "billion", 5: "merged"}
+
+
+def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) -> dict:
+    """Builds the workload's map and blocks, inserts every key, stages the
+    batches on the device and times the step.  Returns the workload's
+    result object; frees its device memory before returning."""
     import torch
 
     import recommender_sparse_embedding_amd as rse
     import synth
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = synth.config(args.config)
+    cfg = synth.config(n)
     wl = synth.Workload(cfg)
     T, B, D = cfg.n_tables, cfg.batch, cfg.dim
+    map_load = args.map_load or MAP_LOAD[n]
     t0 = time.time()
+    # every step of a workload with never-seen ids (or whose tables start
+    # empty) gets its own batch, so that every timed step inserts what the
+    # workload says it inserts; the others cycle a few batches
+    distinct = cfg.fresh_frac > 0 or not cfg.prepopulate
+    n_ref = max(2, steps // 2)
+    n_warm_sched = 4 if full_schedules else 2
+    n_ref_sched = 3 if full_schedules else 1
+    # batches the run finds: warmup runs (each primed up to two batches
+    # ahead), the timed run (two ahead), the reference runs (one ahead)
+    n_finds = n_warm_sched * (warmup + 2) + steps + 2 + n_ref_sched * (n_ref + 1) + 4
+    n_batches = n_finds if distinct else max(3, args.batches)
 
     # ---------------------------------------------------------- setup ----
     total_keys = int(wl.card.sum())
-    if cfg.merged:
-        slots = [int(total_keys / args.map_load) + 1024]
-    else:
-        slots = [int(c / args.map_load) + 1024 for c in wl.card]
-    idm = rse.IdMap(slots, max_load=0.9, merged=cfg.merged, hash_seed=12345, device=dev)
-    chunk_log2 = 20
-    blk = rse.EmbeddingBlocks(D, cfg.wdtype, cfg.optim, chunk_log2, max_chunks=4096, seed=cfg.seed,
-                              device=dev)
-    # rows the run can add: the whole universe when tables start empty (the
-    # lookups draw from it), else the never-seen keys of every find the run
-    # makes (warmup and timed steps of each schedule, plus look-ahead finds)
     max_bag = {"fixed": cfg.bag[1], "uniform": cfg.bag[-1], "poisson": 3 * cfg.bag[1]}[cfg.bag[0]]
-    n_finds = 5 * (args.warmup + 2) + 5 * (args.steps + 2)   # five schedules, each primed
     if not cfg.prepopulate:
         headroom = total_keys
     else:
-        headroom = int(cfg.fresh_frac * cfg.n_bags * max_bag * n_finds)
-    headroom += 1 << chunk_log2
-    blk.grow(-(-((total_keys if cfg.prepopulate else 0) + headroom) // (1 << chunk_log2)))
+        headroom = int(cfg.fresh_frac * cfg.n_bags * max_bag * n_finds * 1.1)
+    if cfg.merged:
+        slots = [int((total_keys + headroom) / map_load) + 1024]
+    else:
+        per_table = headroom // T if cfg.prepopulate else 0
+        slots = [int((int(c) + per_table) / map_load) + 1024 for c in wl.card]
+    idm = rse.IdMap(slots, max_load=0.9, merged=cfg.merged, hash_seed=12345, device=dev)
+    blk = rse.EmbeddingBlocks(D, cfg.wdtype, cfg.optim, CHUNK_LOG2, max_chunks=4096, seed=cfg.seed, device=dev)
+    blk.grow(-(-((total_keys if cfg.prepopulate else 0) + headroom + (1 << CHUNK_LOG2)) // (1 << CHUNK_LOG2)))
     opt = rse.Optim(cfg.optim, cfg.lr, cfg.eps, cfg.beta1, cfg.beta2)
     n_new = torch.zeros(1, dtype=torch.int64, device=dev)
     pre_ws = idm.workspace(1 << 24)
     for ids, bounds in wl.prepopulation(chunk=1 << 24):
         t_ids = torch.from_numpy(ids).to(dev)
         ro = torch.empty_like(t_ids)
-        rse.idmap_find_or_insert(idm, blk, t_ids, torch.from_numpy(bounds).to(dev), 1, T, ro, n_new,
-                                 ws=pre_ws)
+        rse.idmap_find_or_insert(idm, blk, t_ids, torch.from_numpy(bounds).to(dev), 1, T, ro, n_new, ws=pre_ws)
     torch.cuda.synchronize()
-    used, st = blk.status()
-    assert st == 0 and used == (total_keys if cfg.prepopulate else 0), (used, st)
-    log(f"prepopulated {total_keys} keys in {time.time() - t0:.1f}s")
+    del pre_ws
+    used0, st = blk.status()
+    assert st == 0 and used0 == (total_keys if cfg.prepopulate else 0), (used0, st)
+    log(f"[{n}] prepopulated {used0} keys in {time.time() - t0:.1f}s")
 
     batches = []
-    for k in range(args.batches):
+    for k in range(n_batches):
         ids, bo = wl.batch_inputs(k)
-        # distinct (table, key) pairs = rows the step updates (all keys are live)
-        tab = np.repeat(np.arange(T), np.diff(bo[::B]))
-        U = len(np.unique(np.stack([tab, ids], 1), axis=0)) if len(ids) else 0
-        g = torch.from_numpy(wl.grad(k)).to(dev) if cfg.grad == "normal" else None
-        batches.append(dict(ids=torch.from_numpy(ids).to(dev), bo=torch.from_numpy(bo).to(dev),
-                            grad=g, L=len(ids), U=U, ro=torch.empty(len(ids), dtype=torch.int64, device=dev)))
+        g = torch.from_numpy(wl.grad(k)).to(dev) if (cfg.grad == "normal" and k < max(3, args.batches)) else None
+        batches.append(dict(ids=torch.from_numpy(ids).to(dev), bo=torch.from_numpy(bo).to(dev), grad=g,
+                            L=len(ids), ro=torch.empty(len(ids), dtype=torch.int64, device=dev),
+                            nu=torch.zeros(1, dtype=torch.int64, device=dev),
+                            nn=torch.zeros(1, dtype=torch.int64, device=dev)))
+    if cfg.grad == "normal" and distinct:      # gradients cycle; the lookups do not
+        for k, b in enumerate(batches):
+            b["grad"] = batches[k % max(3, args.batches)]["grad"]
     L_max = max(b["L"] for b in batches)
     find_ws = idm.workspace(L_max)
-    bwd_ws = rse.bwd_workspace(L_max, T, B, D, dev)
+    ws2 = [rse.bwd_workspace(L_max, T, B, D, dev), rse.bwd_workspace(L_max, T, B, D, dev)]
     out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
-    n_u = torch.zeros(1, dtype=torch.int64, device=dev)
-    log(f"staged {len(batches)} batches, setup {time.time() - t0:.1f}s")
+    log(f"[{n}] staged {len(batches)} batches ({L_max} lookups max), setup {time.time() - t0:.1f}s")
 
     stream = torch.cuda.current_stream()
-    # second stream (default priority) for the work that does not wait for
-    # the previous phase: the backward's sort, and the next batch's find
+    # second stream (default priority) for work that does not wait for the
+    # previous phase: the backward's sort, and the next batch's find
     side = torch.cuda.Stream(device=dev)
-    ws2 = [bwd_ws, rse.bwd_workspace(L_max, T, B, D, dev)]
     step_no = [0]
+
+    def batch_at(k):
+        return batches[k % len(batches)]
 
     def grad_of(b):
         return b["grad"] if b["grad"] is not None else 2.0 * out
 
-    def step_serial(b):
-        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws)
+    def find(b, s=None):
+        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], b["nn"], ws=find_ws, stream=s)
+
+    def step_serial(i):
+        b = batch_at(i)
+        find(b)
         rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
         step_no[0] += 1
-        rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, grad_of(b), opt, step_no[0], n_u,
-                                     ws=bwd_ws)
+        rse.embedding_bag_bwd_update(blk, b["ro"], b["bo"], T, B, cfg.pooling, grad_of(b), opt, step_no[0],
+                                     b["nu"], ws=ws2[0])
 
-    def step_overlap(b, ev=None):
+    def step_overlap(i, ev=None):
         """find; then the forward (stream 1) and the backward's sort (stream
         2) together; then the apply."""
+        b = batch_at(i)
         if ev:
             ev[0].record(stream)
-        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws)
+        find(b)
         if ev:
             ev[1].record(stream)
-        found = torch.cuda.Event()
-        found.record(stream)
-        side.wait_event(found)
-        plan = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, bwd_ws, stream=side)
+        found_ = torch.cuda.Event()
+        found_.record(stream)
+        side.wait_event(found_)
+        plan = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, ws2[0], stream=side)
         srt = torch.cuda.Event()
         srt.record(side)
         rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
@@ -197,74 +257,49 @@ def main():
         g = grad_of(b)
         step_no[0] += 1
         stream.wait_event(srt)
-        rse.embedding_bag_bwd_apply(blk, plan, b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u, bwd_ws)
+        rse.embedding_bag_bwd_apply(blk, plan, b["bo"], T, B, cfg.pooling, g, opt, step_no[0], b["nu"], ws2[0])
         if ev:
             ev[3].record(stream)
 
-    # Pipelined steps: the find and sort of batch i+1 (stream 2) run while
-    # batch i's forward and apply run (stream 1).  The find of batch i+1 only
-    # touches the map, rows it creates and its own outputs, none of which
-    # batch i's apply reads or writes; the forward of batch i+1 waits for
-    # both.  Sort workspaces alternate; a sort waits for the apply that last
-    # used its workspace.
+    # Pipelined: the find and sort of batch i+1 (stream 2) run while batch
+    # i's forward and apply run (stream 1).  The find of batch i+1 touches
+    # only the map, rows it creates and its own outputs, none of which batch
+    # i's apply reads or writes; the forward of batch i+1 waits for both.
+    # Sort workspaces alternate; a sort waits for the apply that last used
+    # its workspace.
     applied = [torch.cuda.Event(), torch.cuda.Event()]
     fronted = [torch.cuda.Event(), torch.cuda.Event()]
     plans = [None, None]
 
-    def front(i, b):
+    def front(i):
+        b = batch_at(i)
         side.wait_event(applied[i % 2])
-        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws, stream=side)
+        find(b, side)
         plans[i % 2] = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, ws2[i % 2], stream=side)
         fronted[i % 2].record(side)
 
-    def back(i, b):
+    def back(i):
+        b = batch_at(i)
         stream.wait_event(fronted[i % 2])
         rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
         g = grad_of(b)
         step_no[0] += 1
-        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], b["nu"],
                                     ws2[i % 2])
         applied[i % 2].record(stream)
 
-    # "staggered": stream 2 sorts batch i while stream 1 runs its forward,
-    # then finds batch i+1 while stream 1 runs batch i's apply (the radix
-    # passes slow the segmented update down when they share the GPU with it,
-    # less so the forward).  Same per-step work and dependencies as above.
-    found = [torch.cuda.Event(), torch.cuda.Event()]
-    sorted_ = [torch.cuda.Event(), torch.cuda.Event()]
-
-    def find_ahead(i, b):
-        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws, stream=side)
-        found[i % 2].record(side)
-
-    def staggered_step(i, b, b_next):
-        side.wait_event(applied[(i + 1) % 2])         # apply(i-1) is done: stream 1 starts forward(i)
-        plans[i % 2] = rse.embedding_bag_bwd_prepare(blk, b["ro"], b["bo"], T, B, ws2[i % 2], stream=side)
-        sorted_[i % 2].record(side)
-        find_ahead(i + 1, b_next)
-        stream.wait_event(found[i % 2])
-        rse.embedding_bag_fwd(blk, b["ro"], b["bo"], T, B, cfg.pooling, out)
-        g = grad_of(b)
-        step_no[0] += 1
-        stream.wait_event(sorted_[i % 2])
-        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
-                                    ws2[i % 2])
-        applied[i % 2].record(stream)
-
-    # "lookahead": stream 2 runs one more batch ahead.  While stream 1 runs
-    # batch i's forward and apply, stream 2 sorts batch i+1 (found during the
-    # previous step) and then finds batch i+2.  The sort shares the GPU with
-    # the forward and the find with the segmented update, and stream 1 never
-    # waits for the tail of a sort.  The find of i+2 writes only the map, rows
-    # it creates and batch i+2's offsets (a buffer last read by the forward
-    # of batch i-2 when at least three batches cycle); finds still run in
-    # batch order, so every result is that of the plain order.
+    # Lookahead (the value): stream 2 runs one more batch ahead.  While
+    # stream 1 runs batch i's forward and apply, stream 2 sorts batch i+1
+    # (found during the previous step) and then finds batch i+2.  The find
+    # of i+2 writes only the map, rows it creates and batch i+2's offsets (a
+    # buffer last read by the forward of batch i-2 when at least three
+    # batches cycle); finds still run in batch order, so every result is
+    # that of the plain order.
     ready = [torch.cuda.Event() for _ in range(3)]        # find of batch k done: ready[k % 3]
     prepared = [torch.cuda.Event(), torch.cuda.Event()]   # prepare of batch k done: prepared[k % 2]
 
     def la_find(k):
-        b = batch_at(k)
-        rse.idmap_find_or_insert(idm, blk, b["ids"], b["bo"], B, T, b["ro"], n_new, ws=find_ws, stream=side)
+        find(batch_at(k), side)
         ready[k % 3].record(side)
 
     def la_prepare(k):
@@ -282,213 +317,274 @@ def main():
         g = grad_of(b)
         step_no[0] += 1
         stream.wait_event(prepared[i % 2])
-        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], n_u,
+        rse.embedding_bag_bwd_apply(blk, plans[i % 2], b["bo"], T, B, cfg.pooling, g, opt, step_no[0], b["nu"],
                                     ws2[i % 2])
         applied[i % 2].record(stream)
 
-    def batch_at(k):
-        return batches[k % len(batches)]
+    host_ms = {}
+    cursor = [0]       # next batch index: every batch is found exactly once per pass over them
 
-    host_ms = {}      # host time to enqueue one step, per schedule
-
-    def timed(schedule, first, n, evs=None):
-        """n steps over batches first.., timed between events on stream 1
-        (every stream's work inside is waited for); returns ms."""
+    def timed(schedule, n_steps, evs=None):
+        """n_steps steps starting at the next unused batch, timed between
+        events on stream 1 (every stream's work inside is waited for);
+        returns (ms, first batch index)."""
+        first = cursor[0]
         torch.cuda.synchronize()
         if schedule == "pipelined":
-            front(first, batch_at(first))
-        if schedule == "staggered":
-            find_ahead(first, batch_at(first))
+            front(first)
         if schedule == "lookahead":
             la_find(first)
             la_prepare(first)
             la_find(first + 1)
         torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         h0 = time.perf_counter()
-        for k in range(n):
+        for k in range(n_steps):
             i = first + k
             if schedule == "serial":
-                step_serial(batch_at(i))
+                step_serial(i)
             elif schedule == "overlap":
-                step_overlap(batch_at(i), evs[k] if evs else None)
-            elif schedule == "staggered":
-                staggered_step(i, batch_at(i), batch_at(i + 1))
+                step_overlap(i, evs[k] if evs else None)
             elif schedule == "lookahead":
                 la_step(i)
             else:
-                front(i + 1, batch_at(i + 1))      # the next batch: one find + sort per step
-                back(i, batch_at(i))
+                front(i + 1)          # the next batch: one find + sort per step
+                back(i)
         if schedule == "pipelined":
-            stream.wait_event(fronted[(first + n) % 2])
-        if schedule == "staggered":
-            stream.wait_event(found[(first + n) % 2])
+            stream.wait_event(fronted[(first + n_steps) % 2])
         if schedule == "lookahead":
-            stream.wait_event(prepared[(first + n) % 2])
-            stream.wait_event(ready[(first + n + 1) % 3])
-        t1.record(stream)
-        host_ms[schedule] = (time.perf_counter() - h0) * 1e3 / max(n, 1)
+            stream.wait_event(prepared[(first + n_steps) % 2])
+            stream.wait_event(ready[(first + n_steps + 1) % 3])
+        e1.record(stream)
+        host_ms[schedule] = (time.perf_counter() - h0) * 1e3 / max(n_steps, 1)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
+        # batches found ahead by the two-stream schedules are skipped: the
+        # next run starts at a batch nobody has found yet
+        cursor[0] = first + n_steps + (2 if schedule == "lookahead" else 1 if schedule == "pipelined" else 0)
+        return e0.elapsed_time(e1), first
 
-    schedule = "serial" if args.serial_bwd else ("lookahead" if len(batches) >= 3 else "overlap")
-    for name in ("serial", "overlap", "staggered", "pipelined", schedule):
-        timed(name, 0, args.warmup)
-    used, st = blk.status()
-    assert st == 0, st
+    others = ("serial", "overlap", "pipelined") if full_schedules else ("serial",)
+    for name in others + ("lookahead",):
+        timed(name, warmup)
+    idm_st, _ = idm.status()
+    _, st = blk.status()
+    assert idm_st == 0 and st == 0, (idm_st, st)
 
     # ----------------------------------------------------- timed region --
-    # The library brackets every launch of the segmented-update kernel (the
-    # step's largest) with HIP events on its stream while the trace is on.
+    # The library brackets every launch of the segmented-update kernel with
+    # HIP events on its stream while the trace is on.
     rse.trace_start(rse.K_SEG_UPDATE)
-    w0 = time.perf_counter()
-    ms_total = timed(schedule, args.warmup, args.steps)
-    wall = time.perf_counter() - w0
+    ms_total, first = timed("lookahead", steps)
     n_seg, seg_ms = rse.trace_stop()
-    ms_step = ms_total / args.steps
+    ms_step = ms_total / steps
     t_seg = seg_ms / max(n_seg, 1)
-    # the other schedules, and the phase split of the overlapped one, for reference
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    ms_overlap = timed("overlap", args.warmup, args.steps, evs) / args.steps
-    t_find = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    sel = [batch_at(first + k) for k in range(steps)]
+    L_sel = [b["L"] for b in sel]
+    U_sel = [int(b["nu"].item()) for b in sel]          # distinct rows each step updated
+    new_rows = float(np.mean([int(b["nn"].item()) for b in sel]))   # rows each step's find inserted
+
+    ms_by = {"lookahead": round(ms_step, 4)}
+    phase = None
     rse.trace_start(rse.K_FWD)
-    ms_serial = timed("serial", args.warmup, args.steps) / args.steps
-    ms_stag = timed("staggered", args.warmup, args.steps) / args.steps if len(batches) >= 2 else None
-    ms_pipe = timed("pipelined", args.warmup, args.steps) / args.steps if len(batches) >= 2 else None
+    ms_by["serial"] = round(timed("serial", n_ref)[0] / n_ref, 4)
+    if full_schedules:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ref)]
+        ms_by["overlap"] = round(timed("overlap", n_ref, evs)[0] / n_ref, 4)
+        phase = {k: round(float(np.mean([e[a].elapsed_time(e[a + 1]) for e in evs])), 4)
+                 for a, k in enumerate(("find", "fwd", "bwd_update"))}
+        ms_by["pipelined"] = round(timed("pipelined", n_ref)[0] / n_ref, 4)
     n_fwd, fwd_ms = rse.trace_stop()
-    t_fwd_kernel = fwd_ms / max(n_fwd, 1)
+    fwd_ms_kernel = fwd_ms / max(n_fwd, 1)
     idm_st, _ = idm.status()
-    used, st = blk.status()
+    live_rows, st = blk.status()
     assert idm_st == 0 and st == 0, (idm_st, st)
-    live_rows = used
 
-    sel = [batches[(args.warmup + k) % len(batches)] for k in range(args.steps)]
-    L_avg = float(np.mean([b["L"] for b in sel]))
-    U_avg = float(np.mean([b["U"] for b in sel]))
     rb = blk.row_bytes
-    comp = float(np.mean([compulsory_bytes(cfg, b["L"], b["U"], 0, rb) for b in sel]))
-    lookups_s = L_avg / (ms_step * 1e-3)
-    rows_s = U_avg / (ms_step * 1e-3)
+    L_avg, U_avg = float(np.mean(L_sel)), float(np.mean(U_sel))
+    comp = float(np.mean([compulsory_bytes(cfg, L, U, new_rows, rb) for L, U in zip(L_sel, U_sel)]))
+    logical = float(np.mean([logical_bytes(cfg, L, U, new_rows, rb) for L, U in zip(L_sel, U_sel)]))
     step_gbs = comp / (ms_step * 1e-3) / 1e9
-    logical = float(np.mean([logical_bytes(cfg, b["L"], b["U"], rb) for b in sel]))
-
     # roofline of the segmented-update kernel: algorithmic bytes per launch =
-    # sorted (row, gradient-row) pairs read (8 B per lookup) + one gradient row
-    # per lookup (dim * 4 B) + each touched row (weights + state) read and
-    # written once
-    seg_bytes = float(np.mean([b["L"] * 8 + b["L"] * D * 4 + b["U"] * rb * 2 for b in sel]))
+    # sorted (row, gradient-row) pairs read (8 B per lookup) + one gradient
+    # row per lookup (dim * 4 B) + each touched row (weights + state) read
+    # and written once
+    seg_bytes = float(np.mean([L * 8 + L * D * 4 + U * rb * 2 for L, U in zip(L_sel, U_sel)]))
+    # the same kernel by compulsory bytes: each bag's gradient row read once
+    seg_comp = float(np.mean([L * 8 + T * B * D * 4 + U * rb * 2 for L, U in zip(L_sel, U_sel)]))
     seg_gbs = seg_bytes / (t_seg * 1e-3) / 1e9
     TB = T * B
     w_bytes = D * (2 if cfg.wdtype == synth.BF16 else 4)
-    fwd_bytes = float(np.mean([b["L"] * 8 + (TB + 1) * 8 + b["U"] * w_bytes + TB * D * 4 for b in sel]))
-    traffic = read_traffic("seg_update_clicklog.txt", KERNEL_REV) if args.config == 2 else None
+    fwd_bytes = float(np.mean([L * 8 + (TB + 1) * 8 + U * w_bytes + TB * D * 4 for L, U in zip(L_sel, U_sel)]))
+    sha = kernel_sources_sha()
     roofline = {"bound": "hbm", "kernel": f"k_seg_work<{D},{'bf16' if cfg.wdtype else 'f32'}>",
                 "achieved": round(seg_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(seg_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "frac": round(seg_gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic(n, sha),
                 "algorithmic_bytes_per_launch": int(seg_bytes), "avg_launch_ms": round(t_seg, 4),
-                "launches_timed": n_seg}
-    fwd_roof = {"kernel": "embedding_bag_fwd", "achieved": round(fwd_bytes / (t_fwd_kernel * 1e-3) / 1e9, 1),
+                "launches_timed": n_seg,
+                "compulsory_bytes_per_launch": int(seg_comp),
+                "compulsory_frac": round(seg_comp / (t_seg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    fwd_roof = {"kernel": "embedding_bag_fwd", "achieved": round(fwd_bytes / (fwd_ms_kernel * 1e-3) / 1e9, 1),
                 "unit": "GB/s", "algorithmic_bytes_per_launch": int(fwd_bytes),
-                "avg_launch_ms": round(float(t_fwd_kernel), 4)}
-
-    # --------------------------------------------------- CPU baseline -----
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, wl, args.cpu_steps)
-
+                "avg_launch_ms": round(float(fwd_ms_kernel), 4), "launches_timed": n_fwd}
     res = {
-        "metric": "embedding lookups/sec (fwd+bwd+update), 1 MI355X",
-        "value": round(lookups_s, 1),
-        "unit": "lookups/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "workload": f"{cfg.name}: {T} tables x batch {B}, dim {D}, {live_rows} live rows, map load {map_load}",
+        "lookups_per_s": round(L_avg / (ms_step * 1e-3), 1),
+        "updated_rows_per_s": round(U_avg / (ms_step * 1e-3), 1),
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32 storage, f64 accumulate" if cfg.wdtype == synth.F32 else "bf16 storage, f64 accumulate",
-        "data": "synthetic (seeded Zipf lookups over random 63-bit keys, N(0,1) grads)",
-        "config": {"workload": f"{cfg.name}: {T} tables x batch {B}, dim {D}, "
-                               f"{live_rows} live rows", "tables": T, "batch": B, "dim": D,
-                   "lookups_per_step": L_avg, "unique_rows_per_step": U_avg, "live_rows": live_rows,
-                   "map_load": args.map_load},
-        "updated_rows_per_s": round(rows_s, 1),
+        "steps": steps, "warmup": warmup,
+        "lookups_per_step": L_avg, "unique_rows_per_step": U_avg, "new_rows_per_step": round(new_rows, 1),
+        "live_rows": live_rows, "map_load": map_load,
         "step_compulsory_bytes": int(comp),
         "step_hbm_gbs": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4),
         "step_logical_bytes": int(logical),
         "step_logical_gbs": round(logical / (ms_step * 1e-3) / 1e9, 1),
-        "schedule": {"serial": "find; fwd; bwd update (one stream)",
-                     "overlap": "find; fwd (stream 1) || bwd prepare = pairs + sort (stream 2); bwd apply",
-                     "lookahead": "fwd + bwd apply of batch i (stream 1) || bwd prepare of batch i+1, then "
-                                  "find of batch i+2 (stream 2)"}[schedule],
-        "ms_per_step_by_schedule": {"serial": round(ms_serial, 4), "overlap": round(ms_overlap, 4),
-                                    "staggered": round(ms_stag, 4) if ms_stag else None,
-                                    "pipelined": round(ms_pipe, 4) if ms_pipe else None,
-                                    "lookahead": round(ms_step, 4) if schedule == "lookahead" else None},
+        "ms_per_step_by_schedule": ms_by,
         "host_enqueue_ms_per_step": {k: round(v, 4) for k, v in host_ms.items()},
-        "overlap_phase_ms": {"find": round(float(t_find), 4), "fwd": round(float(t_fwd), 4),
-                             "bwd_update": round(float(t_bwd), 4)},
-        "wall_s": round(wall, 4),
         "roofline": roofline,
         "fwd_roofline": fwd_roof,
-        "cpu_baseline": cpu,
+        "kernel_sources_sha": sha,
+        "setup_s": round(time.time() - t0, 1),
     }
-    print(json.dumps(res), flush=True)
+    if phase:
+        res["overlap_phase_ms"] = phase
+    # release the workload's device memory before the next one
+    del batches, find_ws, ws2, out, idm, blk
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
-# identifies the kernel source the stored traffic counters were taken on
-KERNEL_REV = "seg-v9"
+# ------------------------------------------------------- CPU baseline ------
+# The oracle (plain single-threaded C++) on a bounded sample of each
+# workload, a few seconds to a few tens of seconds each.
+CPU_SAMPLE = {
+    1: dict(overrides={}, steps=10, what="all 10 steps of the workload, tables starting empty"),
+    2: dict(overrides={}, steps=2, what="2 full steps after inserting all {keys} keys"),
+    3: dict(overrides={"cardinality": ("fixed", 500_000)}, steps=2,
+            what="2 full-batch steps on a twin with 5e5 keys per table ({keys} keys)"),
+    4: dict(overrides={"cardinality": ("fixed", 2_000_000), "batch": 16384}, steps=1,
+            what="1 step of 16384 bags x 50 on a twin with 2e6 live keys"),
+    5: dict(overrides={"cardinality": ("fixed", 100_000), "batch": 4096}, steps=1,
+            what="1 step of 4096 x 100 bags (Poisson(20)) on a twin with 1e5 keys per table ({keys} keys)"),
+}
 
 
-def read_traffic(name, rev):
-    """HBM bytes per launch from a committed counter summary (profiles/),
-    or None if absent or taken on another kernel revision."""
-    path = os.path.join(ROOT, "profiles", name)
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                vals[k.strip()] = v.strip()
-    if vals.get("kernel_rev") != rev or "hbm_bytes_per_launch" not in vals:
-        return None
-    return int(float(vals["hbm_bytes_per_launch"]))
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
-def cpu_baseline(cfg, wl, steps):
-    """The oracle, single-threaded, on the same workload: the full key
-    universe inserted, then `steps` whole steps (find + forward + backward
-    with update); lookups per second of the timed steps."""
+def cpu_baseline(n: int) -> dict:
+    """The oracle on the workload's bounded sample: keys inserted (untimed),
+    then whole steps (find + forward + backward with update) timed; lookups
+    and updated rows per second."""
     import oracle
+    import synth
 
+    spec = CPU_SAMPLE[n]
+    cfg = synth.config(n, **spec["overrides"])
+    wl = synth.Workload(cfg)
     t0 = time.time()
     orc = oracle.OracleTable(cfg.dim, cfg.wdtype, cfg.optim, cfg.n_tables, cfg.merged, seed=cfg.seed,
                              lr=cfg.lr, eps=cfg.eps, beta1=cfg.beta1, beta2=cfg.beta2)
     for ids, bounds in wl.prepopulation(chunk=1 << 24):
         orc.find_or_insert(ids, bounds, 1)
-    log(f"oracle prepopulated in {time.time() - t0:.1f}s")
-    tot_L, tot_t = 0, 0.0
-    for k in range(steps):
+    prep = time.time() - t0
+    tot_L, tot_U, tot_t = 0, 0, 0.0
+    for k in range(spec["steps"]):
         ids, bo = wl.batch_inputs(k)
-        g = wl.grad(k)
+        g = wl.grad(k) if cfg.grad == "normal" else None
         s = time.perf_counter()
         ro, _ = orc.find_or_insert(ids, bo, cfg.batch)
         out = orc.fwd(ro, bo, cfg.batch, cfg.pooling)
-        if cfg.grad != "normal":
+        if g is None:
             g = (2.0 * out).astype(np.float32)
-        orc.bwd_update(ro, bo, cfg.batch, g, cfg.pooling)
+        tot_U += orc.bwd_update(ro, bo, cfg.batch, g, cfg.pooling)
         tot_t += time.perf_counter() - s
         tot_L += len(ids)
+    del orc
     return {"value": round(tot_L / tot_t, 1), "unit": "lookups/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full steps ({tot_L} lookups) after inserting all {int(wl.card.sum())} keys; "
-                      f"{tot_t:.1f}s timed"}
+            "updated_rows_per_s": round(tot_U / tot_t, 1),
+            "sample": spec["what"].format(keys=int(wl.card.sum())) + f": {tot_L} lookups in {tot_t:.2f}s timed "
+                      f"(key insertion {prep:.1f}s, untimed)",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    headline = args.config or 2
+    order = [headline] if args.config else [2, 1, 3, 4, 5]
+    results = {}
+    w0 = time.time()
+    for n in order:
+        t = time.time()
+        is_head = n == headline
+        steps = args.steps if is_head else min(args.steps, args.other_steps)
+        try:
+            results[n] = run_workload(n, args, full_schedules=is_head, steps=steps, warmup=args.warmup)
+        except Exception as e:      # one workload failing must not hide the others
+            if is_head:
+                raise
+            results[n] = {"error": f"{type(e).__name__}: {e}"}
+            gc.collect()
+            torch.cuda.empty_cache()
+        log(f"[{n}] done in {time.time() - t:.1f}s: "
+            f"{results[n].get('ms_per_step')} ms/step, {results[n].get('lookups_per_s')} lookups/s")
+    if not args.no_cpu_baseline:
+        for n in order:
+            t = time.time()
+            results[n]["cpu_baseline"] = cpu_baseline(n)
+            log(f"[{n}] oracle baseline in {time.time() - t:.1f}s: {results[n]['cpu_baseline']['value']} lookups/s")
+
+    h = results[headline]
+    cfg_keys = {k: h[k] for k in ("lookups_per_step", "unique_rows_per_step", "live_rows", "map_load")}
+    res = {
+        "metric": "embedding lookups/sec (fwd+bwd+update), 1 MI355X",
+        "value": h["lookups_per_s"],
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": h["steps"],
+        "warmup": h["warmup"],
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 storage, f64 accumulate" if headline != 5 else "bf16 storage, f64 accumulate",
+        "data": "synthetic (seeded Zipf or uniform lookups over random 63/64/56-bit keys, N(0,1) grads)",
+        "config": {"workload": h["workload"], **cfg_keys},
+        "updated_rows_per_s": h["updated_rows_per_s"],
+        "step_compulsory_bytes": h["step_compulsory_bytes"],
+        "step_hbm_gbs": h["step_hbm_gbs"],
+        "step_frac_of_peak": h["step_frac_of_peak"],
+        "roofline": h["roofline"],
+        "cpu_baseline": h.get("cpu_baseline"),
+        "schedule": "fwd + bwd apply of batch i (stream 1) || bwd prepare of batch i+1, then find of batch i+2 "
+                    "(stream 2)",
+        "workloads": {str(k): v for k, v in results.items()},
+        "wall_s": round(time.time() - w0, 1),
+    }
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -30,6 +30,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rse_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+# RSE_ORACLE_LIB selects another build of the same source (the sanitizer
+# build, loaded by a process that preloads the sanitizer runtimes)
+_LIB_OVERRIDE = os.environ.get("RSE_ORACLE_LIB")
 
 W_F32, W_BF16 = 0, 1
 OPT_SGD, OPT_ADAGRAD, OPT_ADAM = 0, 1, 2
@@ -38,22 +42,30 @@ POOL_SUM, POOL_MEAN = 0, 1
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with g++ (always rebuilds). Returns the .so path."""
-    tmp = _LIB + ".tmp"
-    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC]
+def build(sanitize: bool = False) -> str:
+    """Compile the oracle with g++ (always rebuilds). Returns the .so path.
+    sanitize=True builds liboracle_san.so with AddressSanitizer and
+    UndefinedBehaviorSanitizer (host code only)."""
+    out = _SAN_LIB if sanitize else _LIB
+    tmp = out + ".tmp"
+    flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+    cmd = ["g++", *flags, "-std=c++17", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC]
     subprocess.check_call(cmd)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
     lib.orc_create.restype = P
