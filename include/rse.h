@@ -289,8 +289,11 @@ int rse_bwd_workspace_size(int64_t n_ids, int32_t n_tables, int64_t batch, int32
  *   Adagrad: a = fp32(a + g*g);  w -= lr * (g / (sqrt(a) + eps))
  *   Adam:    m = fp32(b1 m + (1-b1) g);  v = fp32(b2 v + (1-b2) g g);
  *            w -= lr * ((m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps))
- * (Adam is the lazy form of Kingma & Ba 2015, Algorithm 1).  bf16 weights
- * round to nearest even.  Rows not in the batch are not read or written.
+ * (Adam is the lazy form of Kingma & Ba 2015, Algorithm 1).  The square
+ * roots and the quotients by (sqrt(.) + eps) are computed to about 1e-14
+ * relative (fp32 estimates refined by one Newton step in fp64), the mean
+ * pooling share as g * (1 / len), the bias corrections as products with
+ * precomputed reciprocals.  bf16 weights round to nearest even.  Rows not in the batch are not read or written.
  * The number of distinct touched rows is written to *d_n_unique_out.
  * n_ids may not exceed RSE_MAX_BWD_IDS.  The device sort waits on results of
  * other workgroups with a bounded spin; should a wait time out, nothing is

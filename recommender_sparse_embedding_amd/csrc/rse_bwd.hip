@@ -49,10 +49,15 @@ constexpr int P = 64;            // lookups per piece
 // segments at a piece's start and at its last head only).
 constexpr int LONG_T = 64;
 constexpr int HALO = LONG_T + 1;
-constexpr int MAX_SEG_BLOCKS = 65535;
+#ifndef RSE_N_XCD
+#define RSE_N_XCD 8
+#endif
+constexpr int N_XCD = RSE_N_XCD;
 
+// Optimizer constants.  The bias corrections are applied as products with
+// 1 / (1 - b1^t) and sqrt(1 / (1 - b2^t)), computed once on the host.
 struct OptParams {
-    double lr, eps, b1, b2, omb1, omb2, bc1, bc2;
+    double lr, eps, b1, b2, omb1, omb2, inv_bc1, sq_inv_bc2;
 };
 
 // Device counters of one call.  The three list lengths sit on separate
@@ -84,8 +89,7 @@ struct Multi {                   // a segment of 2..LONG_T lookups
 
 struct BwdArgs {
     RowsView rv;
-    const uint32_t* keys;        // sorted rows
-    const uint32_t* vals;        // bag of each sorted lookup
+    const uint2* pairs;          // sorted lookups: x = row, y = gradient row of its bag
     const int64_t* bag_off;
     const float* grad;           // [batch, n_tables, dim]; sorted values index its rows
     int64_t batch;
@@ -156,7 +160,7 @@ constexpr int PAIRS_GRID = 2048;     // bounds the histogram flush: a few thousa
 __global__ __launch_bounds__(PAIRS_BLOCK) void k_pairs(const int64_t* row_off, const int64_t* bag_off,
                                                        int64_t n_bags, int64_t n_ids, int64_t batch,
                                                        int32_t n_tables, int64_t capacity, uint32_t invalid,
-                                                       uint32_t* keys, uint32_t* vals, Ctr* ctr, int32_t* status,
+                                                       uint2* pairs, Ctr* ctr, int32_t* status,
                                                        SortPrep sp, int passes, int width) {
     latency_bound_priority();
     __shared__ uint32_t s_hist[SORT_MAX_PASSES * SORT_MAX_BINS];
@@ -210,8 +214,7 @@ __global__ __launch_bounds__(PAIRS_BLOCK) void k_pairs(const int64_t* row_off, c
                     if (r[u] >= capacity) bad = true;
                     else k = (uint32_t)r[u];
                 }
-                keys[i] = k;
-                vals[i] = gr;
+                pairs[i] = make_uint2(k, gr);
                 sort_hist_add(s_hist, k, passes, width);
             }
         }
@@ -232,12 +235,15 @@ __device__ __forceinline__ const float* grad_row(const BwdArgs& a, uint32_t gr, 
     return a.grad + (int64_t)gr * D + li * Geo<D, BF16>::VEC;
 }
 
-// Length of the bag whose gradient row is gr = b * n_tables + t (mean only).
-__device__ __forceinline__ double bag_len(const BwdArgs& a, uint32_t gr) {
+// 1 / length of the bag whose gradient row is gr = b * n_tables + t (mean
+// pooling only; a bag that holds a lookup is not empty).  One division per
+// lookup; each element's share is then a product (within one fp64 rounding
+// of the quotient).
+__device__ __forceinline__ double inv_bag_len(const BwdArgs& a, uint32_t gr) {
     const uint32_t b = gr / (uint32_t)a.n_tables;
     const uint32_t t = gr - b * (uint32_t)a.n_tables;
     const int64_t j = (int64_t)t * a.batch + b;
-    return (double)(a.bag_off[j + 1] - a.bag_off[j]);
+    return 1.0 / (double)(a.bag_off[j + 1] - a.bag_off[j]);
 }
 
 template <int VEC>
@@ -252,12 +258,12 @@ __device__ __forceinline__ void load_grad(float* out, const float* src) {
     }
 }
 
-template <int VEC>
-__device__ __forceinline__ void add_grad(double* acc, const float* gv, bool mean, double len) {
+template <int VEC, bool MEAN>
+__device__ __forceinline__ void add_grad(double* acc, const float* gv, double inv_len) {
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
         double g = (double)gv[k];
-        if (mean) g = g / len;
+        if (MEAN) g = g * inv_len;
         acc[k] += g;
     }
 }
@@ -266,7 +272,7 @@ __device__ __forceinline__ void add_grad(double* acc, const float* gv, bool mean
 // order.  U gradient rows are loaded together (all loads issued before any
 // is used); a last step shorter than U repeats the range's last row (masked
 // out of the sum), so a ragged end costs one round trip, not one per row.
-template <int D, bool BF16>
+template <int D, bool BF16, bool MEAN>
 __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_vals, int x, int y, int li,
                                           double* acc) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -278,19 +284,46 @@ __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_va
         for (int u = 0; u < U; ++u) j[u] = s_vals[q + u < y ? q + u : y - 1];
 #pragma unroll
         for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
-        double len[U];
+        double inv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
+        for (int u = 0; u < U; ++u) inv[u] = MEAN ? inv_bag_len(a, j[u]) : 1.0;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (q + u < y) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+            if (q + u < y) add_grad<VEC, MEAN>(acc, gv[u], inv[u]);
     }
 }
 
 // ---------------------------------------------------------- epilogue -----
-// Row update in fp64, rounded once to the storage types.  Lane li owns
-// elements [li*VEC, li*VEC + VEC).  The row and its state are loaded before
-// the gradient gather so both are in flight together.
+// sqrt(x) for fp32 x >= 0 (zero, normal, subnormal or infinite) to about
+// 1e-14 relative: the fp32 reciprocal square root refined by one Newton step
+// in fp64 (relative error e -> 1.5 e^2), then multiplied by x.  Small inputs
+// are scaled by an exact power of two first.  Far cheaper than a correctly
+// rounded fp64 square root, and the result rounds to the same fp32 / bf16
+// storage value except within ~1e-14 of a rounding boundary.
+__device__ __forceinline__ double sqrt_refined(float x) {
+    const bool small = x < 0x1p-100f;
+    const float xs = small ? x * 0x1p100f : x;
+    const double xd = (double)xs;
+    const double y0 = (double)__builtin_amdgcn_rsqf(xs);
+    const double y1 = y0 * (1.5 - 0.5 * xd * y0 * y0);
+    double r = xd * y1;
+    r = small ? r * 0x1p-50 : r;
+    r = xs == 0.0f ? 0.0 : r;
+    return xs == __builtin_inff() ? (double)xs : r;
+}
+
+// 1 / d for fp64 d >= 0 to about 1e-14 relative: d = m * 2^e with m in
+// [0.5, 1), the fp32 reciprocal of m refined by one Newton step in fp64
+// (error e -> e^2), then scaled by 2^-e.  d = 0 gives infinity, d = infinity
+// gives 0.
+__device__ __forceinline__ double rcp_refined(double d) {
+    const double m = __builtin_amdgcn_frexp_mant(d);
+    const int e = __builtin_amdgcn_frexp_exp(d);
+    const double r0 = (double)__builtin_amdgcn_rcpf((float)m);
+    const double r = __builtin_amdgcn_ldexp(r0 * (2.0 - m * r0), -e);
+    return d == 0.0 ? __builtin_inf() : (d == __builtin_inf() ? 0.0 : r);
+}
+
 template <int D, bool BF16>
 struct RowRegs {
     static constexpr int VEC = Geo<D, BF16>::VEC;
@@ -340,7 +373,7 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
         for (int k = 0; k < VEC; ++k) {
             const float an = (float)((double)r.st0[k] + g[k] * g[k]);
             acc[k] = an;
-            wn[k] = w[k] - a.op.lr * (g[k] / (sqrt((double)an) + a.op.eps));
+            wn[k] = w[k] - a.op.lr * (g[k] * rcp_refined(sqrt_refined(an) + a.op.eps));
         }
 #pragma unroll
         for (int k = 0; k < VEC; k += 4)
@@ -353,9 +386,10 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
             const float vn = (float)(a.op.b2 * (double)r.st1[k] + a.op.omb2 * g[k] * g[k]);
             m[k] = mn;
             v[k] = vn;
-            const double mh = (double)mn / a.op.bc1;
-            const double vh = (double)vn / a.op.bc2;
-            wn[k] = w[k] - a.op.lr * (mh / (sqrt(vh) + a.op.eps));
+            // m / (1 - b1^t) and sqrt(v / (1 - b2^t)) = sqrt(v) * sqrt(1 / (1 - b2^t))
+            const double mh = (double)mn * a.op.inv_bc1;
+            const double sv = sqrt_refined(vn) * a.op.sq_inv_bc2;
+            wn[k] = w[k] - a.op.lr * (mh * rcp_refined(sv + a.op.eps));
         }
 #pragma unroll
         for (int k = 0; k < VEC; k += 4) {
@@ -450,7 +484,7 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
     const int64_t w1 = t1 + HALO < n ? t1 + HALO : n;
     const int wn = (int)(w1 - w0);
     const int lane = lane_id();
-    for (int q = threadIdx.x; q < wn; q += IX_BLOCK) s_keys[q] = a.keys[w0 + q];
+    for (int q = threadIdx.x; q < wn; q += IX_BLOCK) s_keys[q] = a.pairs[w0 + q].x;
     __syncthreads();
     for (int c = threadIdx.x / WAVE; c < IX_MASKS; c += IX_BLOCK / WAVE) {
         const int q = c * 64 + lane;
@@ -493,7 +527,7 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
         const int x = x_first + u;
         const uint32_t p = (uint32_t)(w0 + x);
         if (cls[u] == 0) {
-            a.singles[pos[0]++] = make_uint2(s_keys[x], a.vals[p]);
+            a.singles[pos[0]++] = make_uint2(s_keys[x], a.pairs[p].y);
         } else if (cls[u] == 1) {
             Multi m;
             m.start = p;
@@ -512,7 +546,7 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
 // piece's start (continuing an earlier piece) goes to carry slot 0, the part
 // of a long segment starting in the piece (continuing past it) to slot 1.
 // Returns whether slot 0 was written.
-template <int D, bool BF16, int NMASK>
+template <int D, bool BF16, bool MEAN, int NMASK>
 __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
                                           const unsigned long long* s_head, int wn, int64_t k, int x0, int xb,
                                           int li) {
@@ -535,7 +569,7 @@ __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_ke
             double acc[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-            sum_range<D, BF16>(a, s_vals, x0, e < lim ? e : lim, li, acc);
+            sum_range<D, BF16, MEAN>(a, s_vals, x0, e < lim ? e : lim, li, acc);
             carry(0, acc);
             wrote0 = true;
         }
@@ -545,7 +579,7 @@ __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_ke
         double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-        sum_range<D, BF16>(a, s_vals, hl, xb, li, acc);
+        sum_range<D, BF16, MEAN>(a, s_vals, hl, xb, li, acc);
         carry(1, acc);
     }
     return wrote0;
@@ -555,16 +589,15 @@ __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_ke
 // rows all requested before any is used; the group's next entries are
 // requested before this round's rows, so a round waits for one memory round
 // trip.
-template <int D, bool BF16, int OPT, int SPG>
+template <int D, bool BF16, int OPT, bool MEAN, int SPG>
 __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
-                                             int64_t n_groups, int li) {
+                                             int64_t n_groups, int li, int64_t lo, int64_t ns) {
     constexpr int VEC = Geo<D, BF16>::VEC;
-    const int64_t ns = (int64_t)a.ctr->n_single;
-    if (gid * SPG >= ns) return;
+    if (lo + gid * SPG >= ns) return;
     uint2 e[SPG];
 #pragma unroll
-    for (int u = 0; u < SPG; ++u) e[u] = a.singles[gid * SPG + u < ns ? gid * SPG + u : ns - 1];
-    for (int64_t i0 = gid * SPG; i0 < ns; i0 += n_groups * SPG) {
+    for (int u = 0; u < SPG; ++u) e[u] = a.singles[lo + gid * SPG + u < ns ? lo + gid * SPG + u : ns - 1];
+    for (int64_t i0 = lo + gid * SPG; i0 < ns; i0 += n_groups * SPG) {
         const int64_t inx = i0 + n_groups * SPG;
         uint2 en[SPG];
 #pragma unroll
@@ -579,16 +612,16 @@ __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s
         }
 #pragma unroll
         for (int u = 0; u < SPG; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, e[u].y, li));
-        double len[SPG];
+        double inv[SPG];
 #pragma unroll
-        for (int u = 0; u < SPG; ++u) len[u] = a.mean ? bag_len(a, e[u].y) : 1.0;
+        for (int u = 0; u < SPG; ++u) inv[u] = MEAN ? inv_bag_len(a, e[u].y) : 1.0;
 #pragma unroll
         for (int u = 0; u < SPG; ++u) {
             if (i0 + u < ns) {
                 double acc[VEC];
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-                add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+                add_grad<VEC, MEAN>(acc, gv[u], inv[u]);
                 finish_row<D, BF16, OPT>(a, rp[u], li, rr[u], acc);
             }
         }
@@ -602,18 +635,17 @@ __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s
 // group's next segment descriptor is requested with this segment's row, and
 // that segment's first U bag ids before this one's update, so a segment
 // waits for one memory round trip per U lookups.
-template <int D, bool BF16, int OPT>
+template <int D, bool BF16, int OPT, bool MEAN>
 __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
-                                            int64_t n_groups, int li) {
+                                            int64_t n_groups, int li, int64_t lo, int64_t nm) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     constexpr int U = Geo<D, BF16>::GRAD_U;
-    const int64_t nm = (int64_t)a.ctr->n_multi;
-    if (gid >= nm) return;
-    Multi m = a.multis[gid];
+    if (lo + gid >= nm) return;
+    Multi m = a.multis[lo + gid];
     uint32_t j[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) j[u] = a.vals[m.start + (u < (int)m.len ? u : m.len - 1)];
-    for (int64_t i = gid; i < nm; i += n_groups) {
+    for (int u = 0; u < U; ++u) j[u] = a.pairs[m.start + (u < (int)m.len ? u : m.len - 1)].y;
+    for (int64_t i = lo + gid; i < nm; i += n_groups) {
         const int64_t inx = i + n_groups;
         const Multi mn = a.multis[inx < nm ? inx : nm - 1];
         char* rp = a.rv.row(s_chunks, m.key);
@@ -627,19 +659,19 @@ __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_
             float gv[U][VEC];
 #pragma unroll
             for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
-            double len[U];
+            double inv[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) len[u] = a.mean ? bag_len(a, j[u]) : 1.0;
+            for (int u = 0; u < U; ++u) inv[u] = MEAN ? inv_bag_len(a, j[u]) : 1.0;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (c0 + u < m.len) add_grad<VEC>(acc, gv[u], a.mean, len[u]);
+                if (c0 + u < m.len) add_grad<VEC, MEAN>(acc, gv[u], inv[u]);
             c0 += U;
             if (c0 >= m.len) break;
 #pragma unroll
-            for (int u = 0; u < U; ++u) j[u] = a.vals[m.start + (c0 + u < m.len ? c0 + u : m.len - 1)];
+            for (int u = 0; u < U; ++u) j[u] = a.pairs[m.start + (c0 + u < m.len ? c0 + u : m.len - 1)].y;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) j[u] = a.vals[mn.start + (u < (int)mn.len ? u : mn.len - 1)];
+        for (int u = 0; u < U; ++u) j[u] = a.pairs[mn.start + (u < (int)mn.len ? u : mn.len - 1)].y;
         finish_row<D, BF16, OPT>(a, rp, li, rr, acc);
         m = mn;
     }
@@ -650,7 +682,7 @@ constexpr int singles_per_group() {
     return 2;
 }
 
-template <int D, bool BF16, int OPT>
+template <int D, bool BF16, int OPT, bool MEAN>
 __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int LPR = G::LPR, GPB = G::GPB, WIN = G::WIN;
@@ -668,25 +700,33 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     }
     const int g = threadIdx.x / LPR;
     const int li = threadIdx.x % LPR;
-    // roles are spread evenly over the block index (blocks start roughly in
+    // Roles are spread evenly over the block index (blocks start roughly in
     // index order), so gathers of long pieces and row updates of short
-    // segments run side by side: block b is the floor(b*l/total)-th long
-    // block if that count steps at b, else a one-lookup or short block,
-    // spread the same way among the rest
-    const int64_t total = gridDim.x;
-    const int64_t b = blockIdx.x;
-    const int64_t lb = b * a.l_blocks / total, lb1 = (b + 1) * a.l_blocks / total;
-    const int blk = (int)lb;
-    if (lb1 == lb) {
-        const int64_t rest = total - a.l_blocks;
-        const int64_t r = b - lb1;
-        const int64_t sb = r * a.s_blocks / rest, sb1 = (r + 1) * a.s_blocks / rest;
-        if (sb1 > sb) {
-            role_singles<D, BF16, OPT, singles_per_group<D, BF16>()>(
-                a, s_chunks, sb * GPB + g, (int64_t)a.s_blocks * GPB, li);
+    // segments run side by side, in groups of N_XCD consecutive blocks (one
+    // per XCD: workgroups are dispatched to the XCDs round-robin): group q is
+    // the floor(q*L/Q)-th long group if that count steps at q, else a
+    // one-lookup or short group, spread the same way among the rest.  Within
+    // a role, XCD x takes the x-th contiguous band of the role's work (its
+    // windows, or its stretch of the segment lists, which the index kernel
+    // fills roughly in sorted order), so the rows and gradient rows one XCD
+    // touches at a time come from a narrow stretch of the sorted order.
+    const int64_t xcd = blockIdx.x % N_XCD;
+    const int64_t q = blockIdx.x / N_XCD;
+    const int64_t Q = gridDim.x / N_XCD;
+    const int64_t L8 = a.l_blocks / N_XCD, S8 = a.s_blocks / N_XCD;
+    const int64_t lq = q * L8 / Q, lq1 = (q + 1) * L8 / Q;
+    if (lq1 == lq) {
+        const int64_t rest = Q - L8;
+        const int64_t r = q - lq1;
+        const int64_t sq = r * S8 / rest, sq1 = (r + 1) * S8 / rest;
+        if (sq1 > sq) {
+            const int64_t ns = (int64_t)a.ctr->n_single;
+            role_singles<D, BF16, OPT, MEAN, singles_per_group<D, BF16>()>(
+                a, s_chunks, sq * GPB + g, S8 * GPB, li, xcd * ns / N_XCD, (xcd + 1) * ns / N_XCD);
         } else {
-            const int64_t m_blocks = rest - a.s_blocks;
-            role_multis<D, BF16, OPT>(a, s_chunks, (r - sb1) * GPB + g, m_blocks * GPB, li);
+            const int64_t nm = (int64_t)a.ctr->n_multi;
+            role_multis<D, BF16, OPT, MEAN>(a, s_chunks, (r - sq1) * GPB + g, (rest - S8) * GPB, li, xcd * nm / N_XCD,
+                                      (xcd + 1) * nm / N_XCD);
         }
         return;
     }
@@ -694,7 +734,9 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     const int64_t n_pieces = (n + P - 1) / P;
     const int lane = lane_id();
     const int wave = threadIdx.x / WAVE;
-    for (int64_t pb = (int64_t)blk * GPB; pb < n_pieces; pb += (int64_t)a.l_blocks * GPB) {
+    // one window of GPB pieces per long block, XCD x taking windows
+    // [x * L8, (x + 1) * L8)
+    for (int64_t pb = (xcd * L8 + lq) * GPB; pb < n_pieces && pb < (xcd + 1) * L8 * GPB; pb += L8 * GPB) {
         const int64_t blk_a = pb * P;
         const int64_t blk_b = (pb + GPB) * P < n ? (pb + GPB) * P : n;
         const int64_t w0 = blk_a - HALO > 0 ? blk_a - HALO : 0;
@@ -702,8 +744,9 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
         const int wn = (int)(w1 - w0);
         __syncthreads();
         for (int q = threadIdx.x; q < wn; q += G::BLOCK) {
-            s_keys[q] = a.keys[w0 + q];
-            s_vals[q] = a.vals[w0 + q];
+            const uint2 pr = a.pairs[w0 + q];
+            s_keys[q] = pr.x;
+            s_vals[q] = pr.y;
         }
         __syncthreads();
         // window position 0 counts as a head: a segment reaching back to it
@@ -720,7 +763,7 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
         if (k < n_pieces) {
             const int x0 = (int)(k * P - w0);
             const int xb = (int)((k * P + P < n ? k * P + P : n) - w0);
-            wrote0 = walk_long<D, BF16, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
+            wrote0 = walk_long<D, BF16, MEAN, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
             // no head in [x0, xb]: the segment at the piece's start fills the
             // piece and goes on into the next one
             spans = k + 1 < n_pieces && next_head<NMASK>(s_head, x0 - 1, wn) > xb;
@@ -786,12 +829,12 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
     for (int64_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
         __syncthreads();       // s_part of the previous owner has been read
         const int64_t h = a.owners[o];
-        const uint32_t key = a.keys[h];
+        const uint32_t key = a.pairs[h].x;
         const int64_t k0 = h / P;
         int64_t k1 = k0;
         for (int64_t kb = k0 + 1;; kb += BLOCK) {
             const int64_t k = kb + threadIdx.x;
-            const bool in = k < n_pieces && a.keys[k * P] == key;
+            const bool in = k < n_pieces && a.pairs[k * P].x == key;
             const int cnt = __syncthreads_count(in);
             k1 += cnt;
             if (cnt < BLOCK) break;
@@ -844,10 +887,8 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
 // Workspace of one call.
 struct BwdWs {
     Ctr* ctr;
-    uint32_t* k0;
-    uint32_t* v0;
-    uint32_t* k1;
-    uint32_t* v1;
+    uint2* p0;
+    uint2* p1;
     double* carry;
     uint32_t* owners;
     uint2* singles;
@@ -861,10 +902,8 @@ BwdWs carve(void* base, int64_t n_ids, int32_t dim, size_t* total) {
     const size_t n = (size_t)(n_ids > 0 ? n_ids : 1);
     const size_t n_pieces = (n + P - 1) / P;
     w.ctr = c.take<Ctr>(1);
-    w.k0 = c.take<uint32_t>(n);
-    w.v0 = c.take<uint32_t>(n);
-    w.k1 = c.take<uint32_t>(n);
-    w.v1 = c.take<uint32_t>(n);
+    w.p0 = c.take<uint2>(n);
+    w.p1 = c.take<uint2>(n);
     w.carry = c.take<double>(n_pieces * 2 * (size_t)dim);
     w.owners = c.take<uint32_t>(n / (LONG_T + 1) + 1);
     w.singles = c.take<uint2>(n);
@@ -881,20 +920,26 @@ int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     // long pieces: one block per GPB pieces; one-lookup and short segments:
     // grid-stride pools (their counts are only known on the device), sized
     // for a few passes when one lookup in ~16 starts a segment
-    a.l_blocks = fill_blocks(n_pieces, G::GPB, MAX_SEG_BLOCKS);
+    // every count a multiple of N_XCD (one block of each group of N_XCD per
+    // XCD); the long role has one block per window of GPB pieces
+    a.l_blocks = (int32_t)(N_XCD * ((n_pieces + (int64_t)G::GPB * N_XCD - 1) / ((int64_t)G::GPB * N_XCD)));
     // with 32 or more lanes per row (rows of 512 bytes and up) half as many
     // pool blocks keep as many bytes in flight, and more of them crowd out
     // the long-piece blocks (measured: click-log update 0.338 -> 0.328 ms;
     // the dim-64 and dim-32 workloads are slower with the smaller pools)
     constexpr int POOL_CAP = G::LPR >= 32 ? 1024 : 2048;
-    a.s_blocks = fill_blocks(n_ids, G::GPB * singles_per_group<D, BF16>() * 8, POOL_CAP);
-    const int m_blocks = fill_blocks(n_ids, G::GPB * 16, POOL_CAP);
+    a.s_blocks = N_XCD * ((fill_blocks(n_ids, G::GPB * singles_per_group<D, BF16>() * 8, POOL_CAP) + N_XCD - 1) / N_XCD);
+    const int m_blocks = N_XCD * ((fill_blocks(n_ids, G::GPB * 16, POOL_CAP) + N_XCD - 1) / N_XCD);
     const int64_t work_blocks = (int64_t)a.l_blocks + a.s_blocks + m_blocks;
     constexpr int CB = combine_block<D, BF16>();
     const int cblocks = fill_blocks(n_pieces, 1, 2048 * 512 / CB);
     {
         TraceScope ts(RSE_K_SEG_UPDATE, s);
-        hipLaunchKernelGGL((k_seg_work<D, BF16, OPT>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s, a);
+        if (a.mean)
+            hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, true>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, false>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s,
+                               a);
     }
     {
         TraceScope ts(RSE_K_COMBINE, s);
@@ -981,16 +1026,15 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
                                              (n_ids + PAIRS_BLOCK * PAIRS_U * 4 - 1) / (PAIRS_BLOCK * PAIRS_U * 4));
         hipLaunchKernelGGL(k_pairs, dim3(fill_blocks(pairs_units, 1, PAIRS_GRID)), dim3(PAIRS_BLOCK), 0, s,
                            d_row_off,
-                           d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.k0, w.v0, w.ctr,
+                           d_bag_offsets, n_bags, n_ids, batch, n_tables, capacity, invalid, w.p0, w.ctr,
                            &blocks->header()->status, sp, sp_plan.passes, sp_plan.width);
         bool alt = false;
-        const int rc = radix_sort_pairs(w.k0, w.v0, w.k1, w.v1, n_ids, bits, w.sort_ws, &alt, s);
+        const int rc = radix_sort_pairs(w.p0, w.p1, n_ids, bits, w.sort_ws, &alt, s);
         if (rc) return rc;
         plan.sorted_in_alt = alt ? 1 : 0;
         // the segment index needs only the sorted pairs
         BwdArgs ia = {};
-        ia.keys = alt ? w.k1 : w.k0;
-        ia.vals = alt ? w.v1 : w.v0;
+        ia.pairs = alt ? w.p1 : w.p0;
         ia.n = n_ids;
         ia.invalid = invalid;
         ia.ctr = w.ctr;
@@ -1033,8 +1077,7 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
 
     BwdArgs a;
     a.rv = blocks->view();
-    a.keys = plan->sorted_in_alt ? w.k1 : w.k0;
-    a.vals = plan->sorted_in_alt ? w.v1 : w.v0;
+    a.pairs = plan->sorted_in_alt ? w.p1 : w.p0;
     a.bag_off = d_bag_offsets;
     a.grad = d_grad;
     a.batch = batch;
@@ -1058,8 +1101,8 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
     a.op.b2 = opt->beta2;
     a.op.omb1 = 1.0 - opt->beta1;
     a.op.omb2 = 1.0 - opt->beta2;
-    a.op.bc1 = opt->kind == RSE_ADAM ? 1.0 - std::pow(opt->beta1, (double)opt->step) : 1.0;
-    a.op.bc2 = opt->kind == RSE_ADAM ? 1.0 - std::pow(opt->beta2, (double)opt->step) : 1.0;
+    a.op.inv_bc1 = opt->kind == RSE_ADAM ? 1.0 / (1.0 - std::pow(opt->beta1, (double)opt->step)) : 1.0;
+    a.op.sq_inv_bc2 = opt->kind == RSE_ADAM ? std::sqrt(1.0 / (1.0 - std::pow(opt->beta2, (double)opt->step))) : 1.0;
     return dispatch(a, blocks->dim, blocks->w_dtype == RSE_BF16, opt->kind, n_ids, s);
 }
 

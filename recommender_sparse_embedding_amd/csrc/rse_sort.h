@@ -42,12 +42,12 @@ SortPrep sort_prep(void* ws, int64_t n);
 // callers check this before enqueueing anything).
 bool sort_supported(int64_t n, int bits);
 
-// Sorts (k0, v0) by the low `bits` bits, stably, ping-ponging through
-// (k1, v1); the result ends in (k1, v1) if *result_in_alt.  Requires the
-// digit totals of every pass to be in prep.totals (summed over its copies)
-// and the rest of prep to be zero (the caller's pair kernel does both).
-int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n, int bits,
-                     void* ws, bool* result_in_alt, hipStream_t s);
+// Sorts the (key, value) pairs p0 (x = key, y = value) by the low `bits`
+// bits of the key, stably, ping-ponging through p1; the result ends in p1 if
+// *result_in_alt.  Requires the digit totals of every pass to be in
+// prep.totals (summed over its copies) and the rest of prep to be zero (the
+// caller's pair kernel does both).
+int radix_sort_pairs(uint2* p0, uint2* p1, int64_t n, int bits, void* ws, bool* result_in_alt, hipStream_t s);
 
 // Device helper for the pair kernel: adds key's digits of every pass to
 // block-local histograms (LDS, [SORT_MAX_PASSES][SORT_MAX_BINS]).

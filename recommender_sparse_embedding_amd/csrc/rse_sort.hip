@@ -3,9 +3,11 @@
 // duplicate gradients are merged without floating-point atomics; here by
 // sorting lookups by row and reducing each run).
 //
-// One kernel per digit pass (digits of up to 9 bits, so 26-bit row keys take
-// three passes); the digit histograms of every pass are computed beforehand
-// by the pair-building kernel.  A pass runs a bounded number of blocks; each
+// Pairs are stored interleaved, one 8-byte (key, value) word each, so the
+// scattered runs a pass writes are twice as long in bytes as with separate
+// key and value arrays.  One kernel per digit pass (digits of up to 9 bits,
+// so 26-bit row keys take three passes); the digit histograms of every pass
+// are computed beforehand by the pair-building kernel.  A pass runs a bounded number of blocks; each
 // repeatedly:
 //   1. takes the next tile (4096 pairs) from an atomic counter, so every tile
 //      it may wait on belongs to a block that is already running;
@@ -74,8 +76,7 @@ __device__ void block_scan_bins(const uint32_t* in, uint32_t* out, int bins, uin
     __syncthreads();
 }
 
-__global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const uint32_t* vals_in,
-                                                uint32_t* keys_out, uint32_t* vals_out, int64_t n, int shift,
+__global__ __launch_bounds__(SB) void k_onesweep(const uint2* pairs_in, uint2* pairs_out, int64_t n, int shift,
                                                 int width, const uint32_t* totals, uint32_t* state,
                                                 uint32_t* tile_ctr, uint32_t* error, uint32_t n_tiles) {
     latency_bound_priority();
@@ -122,8 +123,9 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
     for (int k = 0; k < ITEMS; ++k) {
         const int64_t i = base + (int64_t)w * PER_WAVE + k * WAVE + lane;
         const bool v = i < n;
-        key[k] = v ? keys_in[i] : 0u;
-        val[k] = v ? vals_in[i] : 0u;
+        const uint2 pr = v ? pairs_in[i] : make_uint2(0u, 0u);
+        key[k] = pr.x;
+        val[k] = pr.y;
     }
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
@@ -224,8 +226,7 @@ __global__ __launch_bounds__(SB) void k_onesweep(const uint32_t* keys_in, const 
         const uint32_t d = (kk >> shift) & dmask;
         const uint32_t o = s_glob[d] + ((uint32_t)x - s_pre[d]);
         if ((int64_t)o < n) {                 // always, when the totals match the keys
-            keys_out[o] = kk;
-            vals_out[o] = s_v[x];
+            pairs_out[o] = make_uint2(kk, s_v[x]);     // one 8-byte store per pair
         } else {
             atomicExch(error, 1u);
         }
@@ -274,8 +275,7 @@ bool sort_supported(int64_t n, int bits) {
            n <= (int64_t)ST_VAL;
 }
 
-int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n, int bits,
-                     void* ws, bool* result_in_alt, hipStream_t s) {
+int radix_sort_pairs(uint2* p0, uint2* p1, int64_t n, int bits, void* ws, bool* result_in_alt, hipStream_t s) {
     if (!sort_supported(n, bits)) return RSE_ERR_UNSUPPORTED;
     const SortPlan plan = sort_plan(bits);
     const int64_t n_tiles = tiles_of(n);
@@ -285,13 +285,11 @@ int radix_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int
         for (int ps = 0; ps < plan.passes; ++ps) {
             const int shift = plan.width * ps;
             const int width = bits - shift < plan.width ? bits - shift : plan.width;
-            uint32_t* ki = alt ? k1 : k0;
-            uint32_t* vi = alt ? v1 : v0;
-            uint32_t* ko = alt ? k0 : k1;
-            uint32_t* vo = alt ? v0 : v1;
+            uint2* pi = alt ? p1 : p0;
+            uint2* po = alt ? p0 : p1;
             TraceScope ts(RSE_K_SORT_SCATTER, s);
             const int64_t grid = n_tiles < SORT_BLOCKS ? n_tiles : SORT_BLOCKS;
-            hipLaunchKernelGGL(k_onesweep, dim3((unsigned)grid), dim3(SB), 0, s, ki, vi, ko, vo, n, shift, width,
+            hipLaunchKernelGGL(k_onesweep, dim3((unsigned)grid), dim3(SB), 0, s, pi, po, n, shift, width,
                                p.totals + ps * SORT_MAX_BINS, p.state + (int64_t)ps * n_tiles * SORT_MAX_BINS,
                                p.tile_ctr + ps, p.error, (uint32_t)n_tiles);
             alt = !alt;

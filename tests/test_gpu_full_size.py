@@ -102,6 +102,11 @@ class Full:
         srt.record(side)
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
         rse.embedding_bag_fwd(self.blk, ro, t_bo, T, B, cfg.pooling, out)
+        # one-hot: the rows the forward read (before the update), [B, T, d]
+        self.rows_read = None
+        if cfg.bag == ("fixed", 1):
+            w, _ = self.blk.read_rows(ro)
+            self.rows_read = w.view(T, B, D).transpose(0, 1).contiguous()
         main.wait_event(srt)
         self.step_no += 1
         nu = torch.zeros(1, dtype=torch.int64, device=dev)
@@ -146,10 +151,14 @@ def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float):
         assert np.array_equal(ro_g, ro_r), f"row offsets, step {s}"
         out_r = orc.fwd(ro_r, bo, cfg.batch, cfg.pooling)
         if cfg.bag == ("fixed", 1):
-            # one-hot: the pooled row is the row itself, exactly
-            assert np.array_equal(out_g.view(np.uint32), out_r.view(np.uint32)), f"one-hot pooled rows, step {s}"
-        else:
-            assert_close(out_g, out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol, f"pooled output, step {s}")
+            # one-hot: the pooled row is the row the forward read, exactly (on
+            # the device: the rows of every lookup, read back, in [B, T, d])
+            assert torch.equal(torch.from_numpy(out_g).to(gpu.dev).view(torch.int32),
+                               gpu.rows_read.view(torch.int32)), f"one-hot pooled rows differ from the rows read, step {s}"
+            gpu.rows_read = None
+            if s == 0:       # rows still hold their exact initial values
+                assert np.array_equal(out_g.view(np.uint32), out_r.view(np.uint32)), f"one-hot pooled rows, step {s}"
+        assert_close(out_g, out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol, f"pooled output, step {s}")
         del out_g, out_r
         offs = np.unique(ro_r[ro_r >= 0])
         prev_w, _ = orc.get_rows(offs)
