@@ -55,12 +55,15 @@ __device__ __forceinline__ void widen_add(double* acc, const u32x4& q) {
 
 
 // Pooled rows are written once and not read again by this kernel: stream
-// them past the caches so hot embedding rows stay resident.
-template <int VEC>
-__device__ __forceinline__ void store_out(float* dst, const double* acc, double scale, bool mean) {
+// them past the caches so hot embedding rows stay resident.  Mean pooling
+// multiplies by 1 / len (one division per bag, within one fp64 rounding of
+// the quotient); an empty bag (len 0) stores its zero sum.
+template <int VEC, bool MEAN>
+__device__ __forceinline__ void store_out(float* dst, const double* acc, int64_t len) {
+    const double inv = MEAN && len > 0 ? 1.0 / (double)len : 1.0;
     float f[VEC];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) f[k] = (float)(mean ? acc[k] / scale : acc[k]);
+    for (int k = 0; k < VEC; ++k) f[k] = (float)(MEAN ? acc[k] * inv : acc[k]);
 #pragma unroll
     for (int k = 0; k < VEC; k += 4) {
         const f32x4 v = {f[k], f[k + 1], f[k + 2], f[k + 3]};
@@ -115,7 +118,7 @@ __device__ __forceinline__ const char* dummy_row(const uint64_t* s_chunks, const
 // and in range; the addresses are shuffled to all lanes and the BPG rows
 // loaded together.  Any other chunk (longer or empty bags, malformed
 // offsets, rows past the capacity) is done bag by bag by chunk_general.
-template <int D, bool BF16>
+template <int D, bool BF16, bool MEAN>
 __device__ __forceinline__ void chunk_general(const FwdArgs& a, const uint64_t* s_chunks, int64_t jb,
                                                         int nb, int li) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -139,11 +142,11 @@ __device__ __forceinline__ void chunk_general(const FwdArgs& a, const uint64_t* 
         }
         const int64_t t = (int64_t)((uint64_t)j / (uint64_t)a.batch);
         const int64_t b = j - t * a.batch;
-        store_out<VEC>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, (double)(e0 - s0), a.mean && e0 > s0);
+        store_out<VEC, MEAN>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, e0 - s0);
     }
 }
 
-template <int D, bool BF16, int BPG, bool LDS_TAB>
+template <int D, bool BF16, bool MEAN, int BPG, bool LDS_TAB>
 __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_onehot(FwdArgs a) {
     const uint64_t not_simple = (__ballot(li < BPG && !(one && in_range)) >> gbase) & gmask;
     const uint32_t vbits = (uint32_t)((__ballot(li < BPG && valid) >> gbase) & ((1ull << BPG) - 1));
     if (not_simple != 0 || nb != BPG) {
-        chunk_general<D, BF16>(a, s_chunks, jb, nb, li);
+        chunk_general<D, BF16, MEAN>(a, s_chunks, jb, nb, li);
         return;
     }
     u32x4 q[BPG];
@@ -231,7 +234,7 @@ struct BagOffs4 {
     }
 };
 
-template <int D, bool BF16, int BPG, int UNROLL>
+template <int D, bool BF16, bool MEAN, int BPG, int UNROLL>
 __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
     do {                                                                             \
         const int64_t len = bag_end - bag_start;                                     \
         float* dst = a.out + ((int64_t)b * a.n_tables + t) * D + li * VEC;          \
-        store_out<VEC>(dst, acc, (double)len, a.mean && len > 0);                    \
+        store_out<VEC, MEAN>(dst, acc, len);                                         \
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;                                  \
         if (++b == (uint32_t)a.batch) {                                              \
             b = 0;                                                                   \
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_groups(FwdArgs a) {
 // The wave's groups split one bag's lookups round-robin (the next step's row
 // offsets requested while the current rows are in flight) and combine with
 // xor-shuffles in a fixed tree.
-template <int D, bool BF16, int UNROLL>
+template <int D, bool BF16, bool MEAN, int UNROLL>
 __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, GROUPS = G::GROUPS;
@@ -398,8 +401,7 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
             const int64_t t = (int64_t)((uint64_t)j / (uint64_t)a.batch);
             const int64_t b = j - t * a.batch;
             const int64_t len = e - s;
-            store_out<VEC>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, (double)len,
-                           a.mean && len > 0);
+            store_out<VEC, MEAN>(a.out + (b * a.n_tables + t) * D + li * VEC, acc, len);
         }
     }
 }
@@ -408,15 +410,15 @@ __global__ __launch_bounds__(FWD_BLOCK) void k_fwd_wave(FwdArgs a) {
 #define RSE_FWD_ONEHOT_BPG 8
 #endif
 
-template <int D, bool BF16>
-int launch_fwd(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
+template <int D, bool BF16, bool MEAN>
+int launch_fwd_p(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
     using G = Geo<D, BF16>;
     TraceScope ts(RSE_K_FWD, s);
     const double avg = a.n_bags > 0 ? (double)n_ids / (double)a.n_bags : 0.0;
     constexpr int WAVES = FWD_BLOCK / WAVE;
     if (avg >= 2.0 * G::GROUPS && G::GROUPS > 1) {
         const int blocks = fill_blocks(a.n_bags, WAVES, 256 * 32);
-        hipLaunchKernelGGL((k_fwd_wave<D, BF16, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
+        hipLaunchKernelGGL((k_fwd_wave<D, BF16, MEAN, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
     } else if (avg <= 1.5 && n_ids > 0 && a.capacity > 0) {
         // one-hot: one chunk of BPG bags per group, all its rows in flight
         constexpr int BPG = G::LPR < RSE_FWD_ONEHOT_BPG ? G::LPR : RSE_FWD_ONEHOT_BPG;
@@ -425,17 +427,22 @@ int launch_fwd(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
         const int64_t blocks = (chunks + per_block - 1) / per_block;
         if (blocks > 0x7FFFFFFFll) return RSE_ERR_INVALID_ARG;
         if (a.rv.n_chunks <= LDS_CHUNKS)
-            hipLaunchKernelGGL((k_fwd_onehot<D, BF16, BPG, true>), dim3((unsigned)blocks), dim3(FWD_BLOCK), 0, s, a);
+            hipLaunchKernelGGL((k_fwd_onehot<D, BF16, MEAN, BPG, true>), dim3((unsigned)blocks), dim3(FWD_BLOCK), 0, s, a);
         else
-            hipLaunchKernelGGL((k_fwd_onehot<D, BF16, BPG, false>), dim3((unsigned)blocks), dim3(FWD_BLOCK), 0, s,
+            hipLaunchKernelGGL((k_fwd_onehot<D, BF16, MEAN, BPG, false>), dim3((unsigned)blocks), dim3(FWD_BLOCK), 0, s,
                                a);
     } else {
         constexpr int BPG = 4;
         const int64_t groups = (a.n_bags + BPG - 1) / BPG;
         const int blocks = fill_blocks(groups, WAVES * G::GROUPS, 256 * 32);
-        hipLaunchKernelGGL((k_fwd_groups<D, BF16, BPG, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
+        hipLaunchKernelGGL((k_fwd_groups<D, BF16, MEAN, BPG, 4>), dim3(blocks), dim3(FWD_BLOCK), 0, s, a);
     }
     return launch_status();
+}
+
+template <int D, bool BF16>
+int launch_fwd(const FwdArgs& a, int64_t n_ids, hipStream_t s) {
+    return a.mean ? launch_fwd_p<D, BF16, true>(a, n_ids, s) : launch_fwd_p<D, BF16, false>(a, n_ids, s);
 }
 
 }  // namespace
