@@ -150,6 +150,22 @@ int rse_blocks_status(rse_blocks* blocks, int64_t* rows_used_out, int32_t* statu
 int rse_blocks_read_rows(const rse_blocks* blocks, const int64_t* d_offs, int64_t n,
                          float* d_w_out, float* d_state_out, void* stream);
 
+/*
+ * Restoring saved rows ("RecIS：阿里开源推荐系统统一训练框架", "Saver": the
+ * sparse parameters and their optimizer state are exported and imported).
+ * rse_blocks_write_rows is the inverse of rse_blocks_read_rows: row
+ * d_offs[i] receives weights d_w[i, :] (fp32; bf16 storage rounds to nearest
+ * even, which is exact for values read from bf16 rows) and state
+ * d_state[i, :] (k * dim floats, NULL for SGD).  Offsets outside the
+ * capacity set the sticky status RSE_ERR_BAD_INPUT and are skipped.  The row
+ * counter is not changed; rse_blocks_set_rows_used sets it (0 <= rows_used
+ * <= capacity, else RSE_ERR_INVALID_ARG), so that keys inserted later get
+ * the rows after the restored ones.
+ */
+int rse_blocks_write_rows(rse_blocks* blocks, const int64_t* d_offs, int64_t n, const float* d_w,
+                          const float* d_state, void* stream);
+int rse_blocks_set_rows_used(rse_blocks* blocks, int64_t rows_used, void* stream);
+
 /* ------------------------------------------------------------- IDMap --- */
 /*
  * IDMap ("RecIS", "Embedding Engine"): an open-addressing hash map from a
@@ -241,6 +257,19 @@ int rse_blocks_clear_status(rse_blocks* blocks, void* stream);
  * table index is 0. */
 int rse_idmap_export(rse_idmap* map, int64_t* d_keys_out, int32_t* d_table_out,
                      int64_t* d_off_out, int64_t capacity, int64_t* d_count_out, void* stream);
+
+/*
+ * Insert saved entries (the inverse of rse_idmap_export, "RecIS", "Saver"):
+ * key d_keys[i] of table d_tables[i] (0 for a merged map, whose keys are
+ * already (t << 56) | id) maps to row d_offs[i].  The keys must not be in
+ * the map yet.  A table index or offset out of range, or a duplicate key,
+ * sets the sticky status RSE_ERR_BAD_INPUT; entries that would take a
+ * table past its max_load set RSE_ERR_IDMAP_FULL and nothing is inserted.
+ * After a duplicate the map's contents are unspecified (recreate it).
+ * The blocks' rows are not touched: restore them with rse_blocks_write_rows.
+ */
+int rse_idmap_import(rse_idmap* map, const int64_t* d_keys, const int32_t* d_tables, const int64_t* d_offs,
+                     int64_t n, void* stream);
 
 /* ------------------------------------------------- pooled forward ----- */
 /*

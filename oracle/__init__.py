@@ -89,6 +89,8 @@ def _load():
     lib.orc_touched.argtypes = [P, P, P]
     lib.orc_last_grad.restype = ctypes.c_int
     lib.orc_last_grad.argtypes = [P, i64, P]
+    lib.orc_import.restype = ctypes.c_int
+    lib.orc_import.argtypes = [P, P, P, P, P, P, i64, i64, i64]
     lib.orc_init_value.restype = f64
     lib.orc_init_value.argtypes = [u64, i32, i32, u64, i32]
     lib.orc_splitmix64_mix.restype = u64
@@ -202,6 +204,28 @@ class OracleTable:
         tabs = np.empty(n, np.int32)
         self._lib.orc_map_dump(self._h, _p(keys), _p(tabs))
         return keys, tabs
+
+    def export_state(self):
+        """(keys, map index, offsets, weights [n, dim], state [n, k*dim], step)
+        of every row, in offset order."""
+        keys, tabs = self.map_dump()
+        offs = np.arange(self.n_rows, dtype=np.int64)
+        w, st = self.get_rows(offs)
+        return keys, tabs, offs, w, st, self.step
+
+    def import_state(self, keys, tables, offs, w, state, step):
+        """Replace the table's maps, rows and step by a saved state (the
+        inverse of export_state; every row 0..n-1 listed once)."""
+        keys = _c(keys, np.int64)
+        tabs = _c(tables, np.int32)
+        offs = _c(offs, np.int64)
+        w = _c(w, np.float32)
+        st = _c(state, np.float32) if self.state_per_elem else None
+        n = keys.shape[0]
+        rc = self._lib.orc_import(self._h, _p(keys), _p(tabs), _p(offs), _p(w), _p(st) if st is not None else None,
+                                  n, n, int(step))
+        if rc != 0:
+            raise ValueError("oracle import_state: bad state")
 
     def touched(self):
         n = int(self._lib.orc_touched(self._h, None, None))

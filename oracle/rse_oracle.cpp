@@ -361,6 +361,40 @@ int orc_last_grad(void* h, int64_t off, double* g_out) {
     return 0;
 }
 
+// Restore a saved state ("RecIS：阿里开源推荐系统统一训练框架", "Saver"): the
+// table's maps, rows and step counter are replaced by n entries (key, map
+// index, offset) with their weights [n, dim] (exact in the storage type) and
+// state [n, k * dim], and the row counter set to n_rows.  Offsets must be
+// distinct and below n_rows; every row below n_rows must be listed.
+// Returns 0, or -1 on a bad argument.
+int orc_import(void* h, const int64_t* keys, const int32_t* tables, const int64_t* offs, const float* w,
+               const float* state, int64_t n, int64_t n_rows, int64_t step) {
+    Table* T = (Table*)h;
+    const int d = T->dim, k = T->state_per_elem();
+    if (n != n_rows || n < 0) return -1;
+    for (auto& m : T->maps) m.clear();
+    T->rows.clear();
+    T->last_grad.clear();
+    T->last_count.clear();
+    T->row_key.assign(n_rows, 0);
+    T->row_table.assign(n_rows, -1);
+    for (int64_t i = 0; i < n; ++i) {
+        if (offs[i] < 0 || offs[i] >= n_rows || tables[i] < 0 || tables[i] >= (int32_t)T->maps.size()) return -1;
+        if (T->row_table[offs[i]] != -1) return -1;
+        if (!T->maps[tables[i]].emplace(keys[i], offs[i]).second) return -1;
+        T->row_key[offs[i]] = keys[i];
+        T->row_table[offs[i]] = tables[i];
+        Row r;
+        r.w.resize(d);
+        for (int c = 0; c < d; ++c) r.w[c] = (double)w[i * d + c];
+        r.state.assign(state ? state + i * k * d : nullptr, state ? state + (i + 1) * k * d : nullptr);
+        T->rows[offs[i]] = r;
+    }
+    T->n_rows = n_rows;
+    T->step = step;
+    return 0;
+}
+
 double orc_init_value(uint64_t key, int32_t table, int32_t c, uint64_t seed, int32_t wdtype) {
     return init_value(key, table, c, seed, wdtype);
 }

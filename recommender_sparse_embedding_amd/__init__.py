@@ -90,6 +90,7 @@ class EmbeddingBlocks:
     def __init__(self, dim: int, w_dtype: int = F32, optim: int = SGD, rows_per_chunk_log2: int = 20,
                  max_chunks: int = 1024, seed: int = 0, device="cuda", stream=None):
         self.dim, self.w_dtype, self.optim = dim, w_dtype, optim
+        self.rows_per_chunk_log2, self.max_chunks, self.seed = rows_per_chunk_log2, max_chunks, seed
         self.rows_per_chunk = 1 << rows_per_chunk_log2
         self.row_bytes = row_bytes(dim, w_dtype, optim)
         self.device = torch.device(device)
@@ -133,6 +134,25 @@ class EmbeddingBlocks:
     def clear_status(self, stream=None):
         check(lib.rse_blocks_clear_status(self.handle, _stream(stream)), "rse_blocks_clear_status")
 
+    def write_rows(self, offs: torch.Tensor, w: torch.Tensor, state: torch.Tensor | None = None, stream=None):
+        """Inverse of read_rows: rows `offs` (int64 CUDA) get weights w [n, dim]
+        (fp32) and state [n, k*dim] (fp32; None for SGD)."""
+        _need(offs, torch.int64, "offs")
+        _need(w, torch.float32, "w")
+        n = offs.numel()
+        if w.numel() != n * self.dim:
+            raise ValueError("w must hold n * dim floats")
+        k = self.state_per_elem
+        if k:
+            _need(state, torch.float32, "state")
+            if state.numel() != n * k * self.dim:
+                raise ValueError("state must hold n * k * dim floats")
+        check(lib.rse_blocks_write_rows(self.handle, _ptr(offs), n, _ptr(w), _ptr(state) if k else None,
+                                        _stream(stream)), "rse_blocks_write_rows")
+
+    def set_rows_used(self, rows_used: int, stream=None):
+        check(lib.rse_blocks_set_rows_used(self.handle, int(rows_used), _stream(stream)), "rse_blocks_set_rows_used")
+
     def read_rows(self, offs: torch.Tensor, stream=None):
         """Weights (widened to fp32) and state of rows `offs` (int64 CUDA)."""
         _need(offs, torch.int64, "offs")
@@ -159,6 +179,7 @@ class IdMap:
     def __init__(self, slots_per_table, max_load: float = 0.7, merged: bool = False,
                  hash_seed: int = 0, device="cuda", stream=None):
         slots = [int(s) for s in slots_per_table]
+        self.slots_per_table, self.max_load, self.hash_seed = slots, float(max_load), int(hash_seed)
         self.n_tables = len(slots)
         self.merged = bool(merged)
         self.device = torch.device(device)
@@ -189,6 +210,17 @@ class IdMap:
 
     def clear_status(self, stream=None):
         check(lib.rse_idmap_clear_status(self.handle, _stream(stream)), "rse_idmap_clear_status")
+
+    def import_entries(self, keys: torch.Tensor, tables: torch.Tensor, offs: torch.Tensor, stream=None):
+        """Insert saved (key, table, offset) entries (int64 / int32 / int64 CUDA)."""
+        _need(keys, torch.int64, "keys")
+        _need(tables, torch.int32, "tables")
+        _need(offs, torch.int64, "offs")
+        n = keys.numel()
+        if tables.numel() != n or offs.numel() != n:
+            raise ValueError("keys, tables and offs must have the same length")
+        check(lib.rse_idmap_import(self.handle, _ptr(keys), _ptr(tables), _ptr(offs), n, _stream(stream)),
+              "rse_idmap_import")
 
     def export(self, capacity: int, stream=None):
         """Live entries (keys int64, table int32, offsets int64), any order."""
@@ -349,5 +381,7 @@ __all__ = [
     "RseError", "blocks_grow", "idmap_find_or_insert", "idmap_find_or_insert_noalloc", "embedding_bag_fwd", "embedding_bag_bwd_update",
     "embedding_bag_bwd_prepare", "embedding_bag_bwd_apply",
     "bwd_workspace", "row_bytes", "status_str", "lib", "trace_start", "trace_stop", "K_PROBE", "K_FWD",
-    "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE",
+    "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE", "save", "load",
 ]
+
+from .saver import load, save  # noqa: E402  (the Saver uses the classes above)

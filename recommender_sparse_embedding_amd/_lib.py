@@ -60,6 +60,9 @@ SIGNATURES = {
     "rse_idmap_workspace_size": ([_I64, _PSZ], ctypes.c_int),
     "idmap_find_or_insert": ([_P, _P, _P, _I64, _P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "idmap_find_or_insert_noalloc": ([_P, _P, _P, _I64, _P, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "rse_idmap_import": ([_P, _P, _P, _P, _I64, _P], ctypes.c_int),
+    "rse_blocks_write_rows": ([_P, _P, _I64, _P, _P, _P], ctypes.c_int),
+    "rse_blocks_set_rows_used": ([_P, _I64, _P], ctypes.c_int),
     "rse_idmap_status": ([_P, _PI32, _PI64, _P], ctypes.c_int),
     "rse_idmap_clear_status": ([_P, _P], ctypes.c_int),
     "rse_idmap_export": ([_P, _P, _P, _P, _I64, _P, _P], ctypes.c_int),

@@ -52,6 +52,37 @@ __global__ void k_read_rows(RowsView rv, const int64_t* offs, int64_t n, int dim
     }
 }
 
+// Inverse of k_read_rows: weights from fp32 (bf16 storage rounds to nearest
+// even, exact for values read from bf16 rows), state copied.  Offsets outside
+// the capacity are reported and skipped.
+template <bool BF16>
+__global__ void k_write_rows(RowsView rv, int64_t capacity, const int64_t* offs, int64_t n, int dim, int k_state,
+                             const float* w_in, const float* st_in, int32_t* status) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t per_row = (int64_t)dim * (1 + k_state);
+    for (int64_t e = tid; e < n * per_row; e += stride) {
+        const int64_t q = e / per_row;
+        const int64_t c = e - q * per_row;
+        const int64_t r = offs[q];
+        if (r < 0 || r >= capacity) {
+            if (c == 0) atomicCAS(status, 0, (int32_t)RSE_ERR_BAD_INPUT);
+            continue;
+        }
+        char* row = rv.row(r);
+        if (c < dim) {
+            const float v = w_in[q * dim + c];
+            if (BF16) ((RSE_GLOBAL uint16_t*)row)[c] = f64_to_bf16_rne((double)v);
+            else ((RSE_GLOBAL float*)row)[c] = v;
+        } else if (st_in) {
+            const int64_t w_bytes = (int64_t)dim * (BF16 ? 2 : 4);
+            ((RSE_GLOBAL float*)(row + w_bytes))[c - dim] = st_in[q * (per_row - dim) + (c - dim)];
+        }
+    }
+}
+
+__global__ void k_set_rows_used(BlocksHeader* h, int64_t rows) { h->rows_used = rows; }
+
 }  // namespace
 
 extern "C" {
@@ -166,6 +197,29 @@ int rse_blocks_read_rows(const rse_blocks* b, const int64_t* d_offs, int64_t n, 
     else
         hipLaunchKernelGGL(k_read_rows<false>, grid, dim3(256), 0, as_stream(stream), b->view(), d_offs,
                            n, b->dim, k, d_w_out, k ? d_state_out : nullptr);
+    return launch_status();
+}
+
+int rse_blocks_write_rows(rse_blocks* b, const int64_t* d_offs, int64_t n, const float* d_w,
+                          const float* d_state, void* stream) {
+    if (!b || n < 0 || (n > 0 && (!d_offs || !d_w))) return RSE_ERR_INVALID_ARG;
+    const int k = b->state_per_elem();
+    if (n > 0 && k > 0 && !d_state) return RSE_ERR_INVALID_ARG;
+    if (n == 0) return RSE_OK;
+    const int64_t work = n * b->dim * (1 + k);
+    const dim3 grid(fill_blocks(work, 256, 4096));
+    if (b->w_dtype == RSE_BF16)
+        hipLaunchKernelGGL(k_write_rows<true>, grid, dim3(256), 0, as_stream(stream), b->view(), b->capacity(),
+                           d_offs, n, b->dim, k, d_w, k ? d_state : nullptr, &b->header()->status);
+    else
+        hipLaunchKernelGGL(k_write_rows<false>, grid, dim3(256), 0, as_stream(stream), b->view(), b->capacity(),
+                           d_offs, n, b->dim, k, d_w, k ? d_state : nullptr, &b->header()->status);
+    return launch_status();
+}
+
+int rse_blocks_set_rows_used(rse_blocks* b, int64_t rows_used, void* stream) {
+    if (!b || rows_used < 0 || rows_used > b->capacity()) return RSE_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(k_set_rows_used, dim3(1), dim3(1), 0, as_stream(stream), b->header(), rows_used);
     return launch_status();
 }
 

@@ -708,6 +708,86 @@ __global__ void k_export(const Slot* slots, const TableDir* dir, int32_t n_regio
 
 __global__ void k_zero_u64(unsigned long long* p) { *p = 0; }
 
+// ------------------------------------------------------------ import -----
+// Entries (key, region, offset) of a saved map, in three kernels: count the
+// entries per region (and reject a bad region or offset), decide whether
+// every region stays within its load limit, then insert (one thread per
+// entry, probing from its bucket and claiming an empty slot by CAS).  The
+// set of entries decides the map's contents; the slot each key lands in may
+// depend on timing, which nothing observes.
+__global__ void k_import_reset(TableDir* dir, int32_t n_regions, MapHeader* h) {
+    for (int r = threadIdx.x; r < n_regions; r += blockDim.x) dir[r].new_keys = 0;
+    if (threadIdx.x == 0) h->pad[0] = 0;
+}
+
+__global__ void k_import_count(TableDir* dir, int32_t n_regions, const int32_t* tabs, const int64_t* offs,
+                               int64_t n, MapHeader* h) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t r = tabs[i];
+        if (r < 0 || r >= n_regions || offs[i] < 0 || (uint64_t)offs[i] >= PENDING_BASE) {
+            atomicCAS(&h->status, 0, (int32_t)RSE_ERR_BAD_INPUT);
+            continue;
+        }
+        atomicAdd((unsigned long long*)&dir[r].new_keys, 1ull);
+    }
+}
+
+__global__ void k_import_decide(TableDir* dir, int32_t n_regions, MapHeader* h) {
+    __shared__ int s_fail;
+    if (threadIdx.x == 0) s_fail = h->status;
+    __syncthreads();
+    for (int r = threadIdx.x; r < n_regions; r += blockDim.x)
+        if (dir[r].n_keys + dir[r].new_keys > dir[r].max_keys) atomicCAS(&s_fail, 0, (int)RSE_ERR_IDMAP_FULL);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (s_fail) atomicCAS(&h->status, 0, s_fail);
+        h->pad[0] = s_fail ? 0 : 1;        // go flag for k_import_insert
+    }
+    __syncthreads();
+    if (!s_fail)
+        for (int r = threadIdx.x; r < n_regions; r += blockDim.x) dir[r].n_keys += dir[r].new_keys;
+}
+
+__global__ void k_import_insert(Slot* slots, TableDir* dir, const int64_t* keys, const int32_t* tabs,
+                                const int64_t* offs, int64_t n, MapHeader* h) {
+    if (h->pad[0] != 1) return;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t key = (uint64_t)keys[i];
+        const TableDir d = dir[tabs[i]];
+        const uint64_t off = (uint64_t)offs[i];
+        if (key == EMPTY_KEY) {
+            const unsigned long long old = atomicCAS((unsigned long long*)&dir[tabs[i]].side_val,
+                                                     (unsigned long long)EMPTY_VAL, (unsigned long long)off);
+            if (old != EMPTY_VAL) atomicCAS(&h->status, 0, (int32_t)RSE_ERR_BAD_INPUT);   // duplicate key
+            continue;
+        }
+        int64_t b = reduce_range(fmix64(key ^ d.salt), d.n_buckets);
+        bool done = false;
+        for (int64_t probes = 0; probes < d.n_buckets && !done; ++probes) {
+            const int64_t base = d.slot_base + b * BUCKET;
+            for (int q = 0; q < BUCKET && !done; ++q) {
+                const uint64_t k = slots[base + q].key;
+                if (k == key) {                       // duplicate key
+                    atomicCAS(&h->status, 0, (int32_t)RSE_ERR_BAD_INPUT);
+                    done = true;
+                } else if (k == EMPTY_KEY) {
+                    const unsigned long long old = atomicCAS((unsigned long long*)&slots[base + q].key,
+                                                             (unsigned long long)EMPTY_KEY, (unsigned long long)key);
+                    if (old == EMPTY_KEY) {
+                        slots[base + q].val = off;
+                        done = true;
+                    } else if (old == key) {
+                        atomicCAS(&h->status, 0, (int32_t)RSE_ERR_BAD_INPUT);
+                        done = true;
+                    }
+                }
+            }
+            b = (b + 1 == d.n_buckets) ? 0 : b + 1;
+        }
+        if (!done) atomicCAS(&h->status, 0, (int32_t)RSE_ERR_IDMAP_FULL);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -966,6 +1046,22 @@ int idmap_find_or_insert_noalloc(rse_idmap* map, rse_blocks* blocks, const int64
     // every call; everything else is written before it is read
     return find_or_insert_impl(map, blocks, d_ids, n_ids, d_bounds, stride, n_tables, insert_missing,
                                d_row_off_out, d_n_new_out, ws, NOALLOC_SCRATCH_BYTES, stream);
+}
+
+int rse_idmap_import(rse_idmap* map, const int64_t* d_keys, const int32_t* d_tables, const int64_t* d_offs,
+                     int64_t n, void* stream) {
+    if (!map || n < 0) return RSE_ERR_INVALID_ARG;
+    if (n > 0 && (!d_keys || !d_tables || !d_offs)) return RSE_ERR_INVALID_ARG;
+    if (n == 0) return RSE_OK;
+    hipStream_t s = as_stream(stream);
+    hipLaunchKernelGGL(k_import_reset, dim3(1), dim3(256), 0, s, map->d_dir(), map->n_tables, map->header());
+    const dim3 grid(fill_blocks(n, 256, 8192));
+    hipLaunchKernelGGL(k_import_count, grid, dim3(256), 0, s, map->d_dir(), map->n_tables, d_tables, d_offs, n,
+                       map->header());
+    hipLaunchKernelGGL(k_import_decide, dim3(1), dim3(256), 0, s, map->d_dir(), map->n_tables, map->header());
+    hipLaunchKernelGGL(k_import_insert, grid, dim3(256), 0, s, map->d_slots(), map->d_dir(), d_keys, d_tables,
+                       d_offs, n, map->header());
+    return launch_status();
 }
 
 int rse_idmap_status(rse_idmap* map, int32_t* status_out, int64_t* n_keys_out, void* stream) {

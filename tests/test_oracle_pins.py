@@ -434,3 +434,62 @@ def test_bf16_rounding_matches_torch_and_avoids_double_rounding(oracle_mod):
     t = 1.0 + 2.0**-8 + 2.0**-40
     assert oracle_mod.round_bf16_bits(t) == 0x3F81
     assert torch.tensor(np.float32(t)).to(torch.bfloat16).view(torch.int16).item() == 0x3F80
+
+
+# ------------------------------------------------------------- saver ----
+def test_resume_from_exported_state_equals_uninterrupted_run(oracle_mod):
+    """"RecIS", "Saver": exporting the sparse state (keys, offsets, rows,
+    optimizer state, step) after some steps and importing it into a fresh
+    table must continue exactly as the uninterrupted run: same offsets for
+    old and new keys, same pooled outputs, same rows bit for bit.  Covers
+    Adam (step-dependent bias correction), mean pooling and fresh ids, and a
+    merged bf16 Adagrad table."""
+    import synth
+
+    for cfg in (synth.config(3, n_tables=2, batch=64, cardinality=("fixed", 500), fresh_frac=0.05),
+                synth.config(5, n_tables=3, batch=16, cardinality=("fixed", 300))):
+        wl = synth.Workload(cfg)
+
+        def table():
+            return oracle_mod.OracleTable(cfg.dim, cfg.wdtype, cfg.optim, cfg.n_tables, cfg.merged, seed=cfg.seed,
+                                          lr=cfg.lr, eps=cfg.eps, beta1=cfg.beta1, beta2=cfg.beta2)
+
+        a = table()
+        for ids, bounds in wl.prepopulation():
+            a.find_or_insert(ids, bounds, 1)
+
+        def step(t, s):
+            ids, bo = wl.batch_inputs(s)
+            ro, nn = t.find_or_insert(ids, bo, cfg.batch)
+            out = t.fwd(ro, bo, cfg.batch, cfg.pooling)
+            U = t.bwd_update(ro, bo, cfg.batch, wl.grad(s), cfg.pooling)
+            return ro, nn, out, U
+
+        for s in range(2):
+            step(a, s)
+        b = table()
+        b.import_state(*a.export_state())
+        assert b.step == a.step == 2 and b.n_rows == a.n_rows
+        for s in range(2, 4):
+            ra, rb = step(a, s), step(b, s)
+            assert np.array_equal(ra[0], rb[0]) and ra[1] == rb[1] and ra[3] == rb[3]
+            assert np.array_equal(ra[2].view(np.uint32), rb[2].view(np.uint32))
+        ka, ta, oa, wa, sa, _ = a.export_state()
+        kb, tb, ob, wb, sb, _ = b.export_state()
+        assert np.array_equal(ka, kb) and np.array_equal(ta, tb)
+        assert np.array_equal(wa.view(np.uint32), wb.view(np.uint32)) and np.array_equal(sa.view(np.uint32),
+                                                                                       sb.view(np.uint32))
+
+
+def test_import_state_rejects_inconsistent_states(oracle_mod):
+    t = oracle_mod.OracleTable(4, optim=oracle_mod.OPT_SGD)
+    w = np.zeros((2, 4), np.float32)
+    st = np.zeros((2, 0), np.float32)
+    with pytest.raises(ValueError):          # the same key twice
+        t.import_state(np.array([7, 7]), np.array([0, 0], np.int32), np.array([0, 1]), w, st, 0)
+    with pytest.raises(ValueError):          # row 1 listed twice, row 0 missing
+        t.import_state(np.array([7, 8]), np.array([0, 0], np.int32), np.array([1, 1]), w, st, 0)
+    t.import_state(np.array([7, 8]), np.array([0, 0], np.int32), np.array([1, 0]), w, st, 3)
+    assert t.n_rows == 2 and t.step == 3
+    ro, nn = t.find_or_insert(np.array([8, 7, 9]), [0, 3])
+    assert ro.tolist() == [0, 1, 2] and nn == 1
