@@ -449,12 +449,53 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     }
     if phase:
         res["overlap_phase_ms"] = phase
+    if full_schedules:
+        res["interaction"] = bench_interaction(rse, out, steps)
     # release the workload's device memory before the next one
     del batches, find_ws, ws2, out, idm, blk
     gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def bench_interaction(rse, pooled, steps):
+    """The DLRM dot interaction on the workload's pooled output [B, T, d]
+    (plus a dense vector [B, d]): forward and backward, timed with HIP events
+    on the stream they run on, with their algorithmic bytes (every input read
+    once, every output written once) and fp64 multiply-adds."""
+    import torch
+
+    B, T, D = pooled.shape
+    F, P = T + 1, (T + 1) * T // 2
+    dense = torch.randn((B, D), device=pooled.device)
+    dout = torch.randn((B, D + P), device=pooled.device)
+    out = torch.empty((B, D + P), device=pooled.device)
+    for _ in range(2):
+        rse.dlrm_interaction_fwd(dense, pooled, out)
+        rse.dlrm_interaction_bwd(dense, pooled, dout)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        rse.dlrm_interaction_fwd(dense, pooled, out)
+    ev[1].record(stream)
+    for _ in range(steps):
+        rse.dlrm_interaction_bwd(dense, pooled, dout)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    t_f = ev[0].elapsed_time(ev[1]) / steps
+    t_b = ev[1].elapsed_time(ev[2]) / steps
+    fwd_bytes = B * F * D * 4 + B * (D + P) * 4
+    bwd_bytes = B * F * D * 4 + B * (D + P) * 4 + B * F * D * 4
+    return {"shape": f"batch {B}, {T} tables + dense, dim {D}: out [B, {D + P}]",
+            "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+            "fwd_gbs": round(fwd_bytes / (t_f * 1e-3) / 1e9, 1), "bwd_gbs": round(bwd_bytes / (t_b * 1e-3) / 1e9, 1),
+            "fwd_frac_of_hbm_peak": round(fwd_bytes / (t_f * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bwd_frac_of_hbm_peak": round(bwd_bytes / (t_b * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "fwd_fp64_tflops": round(2 * B * P * D / (t_f * 1e-3) / 1e12, 2),
+            "bwd_fp64_tflops": round(2 * B * F * F * D / (t_b * 1e-3) / 1e12, 2)}
 
 
 # ------------------------------------------------------- CPU baseline ------

@@ -360,8 +360,45 @@ def embedding_bag_bwd_apply(blocks: EmbeddingBlocks, plan, bag_offsets: torch.Te
                                       ws.numel(), _stream(stream)), "embedding_bag_bwd_apply")
 
 
+# ------------------------------------------------- DLRM dot interaction --
+def dlrm_interaction_fwd(dense: torch.Tensor, pooled: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """dense [B, d], pooled [B, T, d] fp32 CUDA -> [B, d + (T+1)T/2]: the dense
+    vector, then the dot products of every pair of (dense, table 0..T-1) in
+    row-major upper-triangle order."""
+    B, T, d = pooled.shape
+    if dense.shape != (B, d):
+        raise ValueError("dense must be [B, d] for pooled [B, T, d]")
+    P = (T + 1) * T // 2
+    if out is None:
+        out = torch.empty((B, d + P), dtype=torch.float32, device=pooled.device)
+    if out.numel() != B * (d + P):
+        raise ValueError("out must hold B * (d + (T+1)T/2) floats")
+    _need(dense, torch.float32, "dense")
+    _need(pooled, torch.float32, "pooled")
+    _need(out, torch.float32, "out")
+    check(lib.dlrm_interaction_fwd(_ptr(dense), _ptr(pooled), B, T, d, _ptr(out), _stream(stream)),
+          "dlrm_interaction_fwd")
+    return out
+
+
+def dlrm_interaction_bwd(dense: torch.Tensor, pooled: torch.Tensor, dout: torch.Tensor, stream=None):
+    """Gradients (ddense [B, d], dpooled [B, T, d]) of dlrm_interaction_fwd for
+    the upstream gradient dout [B, d + (T+1)T/2]."""
+    B, T, d = pooled.shape
+    if dense.shape != (B, d) or dout.numel() != B * (d + (T + 1) * T // 2):
+        raise ValueError("shapes of dense / dout do not match pooled [B, T, d]")
+    _need(dense, torch.float32, "dense")
+    _need(pooled, torch.float32, "pooled")
+    _need(dout, torch.float32, "dout")
+    ddense = torch.empty_like(dense)
+    dpooled = torch.empty_like(pooled)
+    check(lib.dlrm_interaction_bwd(_ptr(dense), _ptr(pooled), _ptr(dout), B, T, d, _ptr(ddense), _ptr(dpooled),
+                                   _stream(stream)), "dlrm_interaction_bwd")
+    return ddense, dpooled
+
+
 # ----------------------------------------------------------------- trace --
-K_PROBE, K_FWD, K_SORT_SCATTER, K_SEG_UPDATE, K_COMBINE = 1, 2, 3, 4, 5
+K_PROBE, K_FWD, K_SORT_SCATTER, K_SEG_UPDATE, K_COMBINE, K_INTERACT = 1, 2, 3, 4, 5, 6
 
 
 def trace_start(kernel: int):
@@ -381,7 +418,8 @@ __all__ = [
     "RseError", "blocks_grow", "idmap_find_or_insert", "idmap_find_or_insert_noalloc", "embedding_bag_fwd", "embedding_bag_bwd_update",
     "embedding_bag_bwd_prepare", "embedding_bag_bwd_apply",
     "bwd_workspace", "row_bytes", "status_str", "lib", "trace_start", "trace_stop", "K_PROBE", "K_FWD",
-    "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE", "save", "load",
+    "K_SORT_SCATTER", "K_SEG_UPDATE", "K_COMBINE", "K_INTERACT", "save", "load", "dlrm_interaction_fwd",
+    "dlrm_interaction_bwd",
 ]
 
 from .saver import load, save  # noqa: E402  (the Saver uses the classes above)

@@ -74,6 +74,8 @@ SIGNATURES = {
                                   ctypes.c_int),
     "embedding_bag_bwd_apply": ([_P, ctypes.POINTER(RseBwdPlan), _P, _I32, _I64, _I32, _P,
                                  ctypes.POINTER(RseOptim), _P, _P, _SZ, _P], ctypes.c_int),
+    "dlrm_interaction_fwd": ([_P, _P, _I64, _I32, _I32, _P, _P], ctypes.c_int),
+    "dlrm_interaction_bwd": ([_P, _P, _P, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "rse_trace_start": ([_I32], ctypes.c_int),
     "rse_trace_stop": ([_PI64, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
 }

@@ -50,7 +50,7 @@ void trace_mark(int kernel, hipStream_t s, bool after) {
 extern "C" {
 
 int rse_trace_start(int32_t kernel) {
-    if (kernel < RSE_K_PROBE || kernel > RSE_K_COMBINE) return RSE_ERR_INVALID_ARG;
+    if (kernel < RSE_K_PROBE || kernel > RSE_K_INTERACT) return RSE_ERR_INVALID_ARG;
     Trace& t = trace();
     std::lock_guard<std::mutex> lk(t.mu);
     if (t.ev.empty()) {

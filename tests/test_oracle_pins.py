@@ -493,3 +493,109 @@ def test_import_state_rejects_inconsistent_states(oracle_mod):
     assert t.n_rows == 2 and t.step == 3
     ro, nn = t.find_or_insert(np.array([8, 7, 9]), [0, 3])
     assert ro.tolist() == [0, 1, 2] and nn == 1
+
+
+# ------------------------------------------------------ dot interaction ----
+def _interaction():
+    from oracle import interaction
+    return interaction
+
+
+def test_interaction_shapes_from_the_page():
+    """Batch 4, d 4, three fields: pooled [4,3,4] plus the dense vector give
+    6 pairs ([4,6]) and [4,10] after the concatenation."""
+    g = _golden("dlrm_shapes.txt")
+    B, d, F = (int(g[k][0]) for k in ("batch", "dim", "fields"))
+    rng = np.random.default_rng(1)
+    dense = rng.standard_normal((B, d))
+    pooled = rng.standard_normal((B, F, d))
+    out, _ = _interaction().interaction_fwd(dense, pooled)
+    assert list(out.shape) == eval(g["concat"][0])
+    assert out.shape[1] - d == eval(g["upper_triangle"][0])[1]
+    assert np.array_equal(out[:, :d], dense)
+
+
+def test_interaction_pairs_are_the_dots_listed():
+    """Every pair of the stacked vectors (dense first, then the fields in
+    table order) is one dot product; pair (0, t+1) is dense . field t."""
+    rng = np.random.default_rng(2)
+    B, T, d = 3, 5, 7
+    dense = rng.standard_normal((B, d))
+    pooled = rng.standard_normal((B, T, d))
+    out, _ = _interaction().interaction_fwd(dense, pooled)
+    vecs = [dense] + [pooled[:, t, :] for t in range(T)]
+    p = d
+    for i in range(T + 1):
+        for j in range(i + 1, T + 1):
+            for b in range(B):
+                assert abs(out[b, p] - sum(vecs[i][b, k] * vecs[j][b, k] for k in range(d))) < 1e-12
+            p += 1
+    assert p == d + (T + 1) * T // 2
+
+
+def test_interaction_backward_matches_torch_autograd():
+    """The oracle's backward against torch autograd (float64) of the same
+    forward built from torch ops (bmm, triu_indices, cat)."""
+    rng = np.random.default_rng(3)
+    B, T, d = 4, 6, 8
+    dense = torch.tensor(rng.standard_normal((B, d)), requires_grad=True)
+    pooled = torch.tensor(rng.standard_normal((B, T, d)), requires_grad=True)
+    X = torch.cat([dense[:, None, :], pooled], dim=1)
+    Z = torch.bmm(X, X.transpose(1, 2).contiguous())
+    iu = torch.triu_indices(T + 1, T + 1, offset=1)
+    out = torch.cat([dense, Z[:, iu[0], iu[1]]], dim=1)
+    dout = torch.tensor(rng.standard_normal(tuple(out.shape)))
+    out.backward(dout)
+    dd, dp, _, _ = _interaction().interaction_bwd(dense.detach().numpy(), pooled.detach().numpy(), dout.numpy())
+    o, _ = _interaction().interaction_fwd(dense.detach().numpy(), pooled.detach().numpy())
+    assert np.allclose(o, out.detach().numpy(), rtol=1e-13, atol=1e-13)
+    assert np.allclose(dd, dense.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dp, pooled.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_interaction_backward_matches_finite_differences():
+    rng = np.random.default_rng(4)
+    B, T, d = 2, 3, 4
+    dense = rng.standard_normal((B, d))
+    pooled = rng.standard_normal((B, T, d))
+    inter = _interaction()
+    out, _ = inter.interaction_fwd(dense, pooled)
+    dout = rng.standard_normal(out.shape)
+    dd, dp, _, _ = inter.interaction_bwd(dense, pooled, dout)
+    h = 1e-6
+
+    def loss(de, po):
+        return float((inter.interaction_fwd(de, po)[0] * dout).sum())
+
+    for b in range(B):
+        for k in range(d):
+            e = np.zeros_like(dense)
+            e[b, k] = h
+            assert abs((loss(dense + e, pooled) - loss(dense - e, pooled)) / (2 * h) - dd[b, k]) < 1e-6
+            for t in range(T):
+                e = np.zeros_like(pooled)
+                e[b, t, k] = h
+                assert abs((loss(dense, pooled + e) - loss(dense, pooled - e)) / (2 * h) - dp[b, t, k]) < 1e-6
+
+
+def test_interaction_field_permutation_permutes_pairs():
+    """Swapping two fields swaps the pairs that involve them; pairs of the
+    other vectors are unchanged."""
+    rng = np.random.default_rng(5)
+    B, T, d = 2, 4, 3
+    dense = rng.standard_normal((B, d))
+    pooled = rng.standard_normal((B, T, d))
+    inter = _interaction()
+    a, _ = inter.interaction_fwd(dense, pooled)
+    sw = pooled[:, [0, 2, 1, 3], :]
+    b_, _ = inter.interaction_fwd(dense, sw)
+    F = T + 1
+
+    def p(i, j):
+        i, j = min(i, j), max(i, j)
+        return d + i * F - i * (i + 1) // 2 + (j - i - 1)
+
+    perm = {0: 0, 1: 1, 2: 3, 3: 2, 4: 4}          # vector index after the swap of fields 1 and 2
+    for i in range(F):
+        for j in range(i + 1, F):
+            assert np.allclose(a[:, p(i, j)], b_[:, p(perm[i], perm[j])])
