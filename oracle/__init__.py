@@ -17,6 +17,10 @@ Semantics followed (by page and section of the source pages):
   variable-length bags.
 * "DLRM — Meta 把工业推荐模型拆成 4 个标准积木", "踩过的坑" 4: sparse optimizer
   updates only the rows seen in the batch.
+* "RecIS：阿里开源推荐系统统一训练框架", "代码架构": a hook on the hash table
+  for feature admission and eviction.  The pages give no policy; the ones
+  defined here (count-min admission threshold, eviction by last-seen clock,
+  recycled rows handed out in ascending order) are stated in rse_oracle.cpp.
 """
 
 from __future__ import annotations
@@ -91,6 +95,27 @@ def _load():
     lib.orc_last_grad.argtypes = [P, i64, P]
     lib.orc_import.restype = ctypes.c_int
     lib.orc_import.argtypes = [P, P, P, P, P, P, i64, i64, i64]
+    u32 = ctypes.c_uint32
+    lib.orc_set_tracking.restype = ctypes.c_int
+    lib.orc_set_tracking.argtypes = [P, i32]
+    lib.orc_set_clock.restype = ctypes.c_int
+    lib.orc_set_clock.argtypes = [P, u32]
+    lib.orc_set_admission.restype = ctypes.c_int
+    lib.orc_set_admission.argtypes = [P, i32, i64, u32, u64]
+    lib.orc_set_recycling.restype = ctypes.c_int
+    lib.orc_set_recycling.argtypes = [P, i32]
+    lib.orc_rehash.restype = i64
+    lib.orc_rehash.argtypes = [P, u32]
+    lib.orc_entries.restype = i64
+    lib.orc_entries.argtypes = [P, P, P, P]
+    lib.orc_sketch.restype = i64
+    lib.orc_sketch.argtypes = [P, P]
+    lib.orc_estimate.restype = u32
+    lib.orc_estimate.argtypes = [P, i64, i32]
+    lib.orc_last_seen.restype = ctypes.c_int
+    lib.orc_last_seen.argtypes = [P, P]
+    lib.orc_free_list.restype = i64
+    lib.orc_free_list.argtypes = [P, P, P]
     lib.orc_init_value.restype = f64
     lib.orc_init_value.argtypes = [u64, i32, i32, u64, i32]
     lib.orc_splitmix64_mix.restype = u64
@@ -239,3 +264,59 @@ class OracleTable:
         if self._lib.orc_last_grad(self._h, int(off), _p(g)) != 0:
             raise KeyError(off)
         return g
+
+    # -------------------------------------- admission, age and eviction --
+    def set_tracking(self, on=True):
+        """Lookups stamp their rows with the clock; all stamps restart at 0."""
+        self._lib.orc_set_tracking(self._h, int(bool(on)))
+
+    def set_clock(self, clock: int):
+        self._lib.orc_set_clock(self._h, int(clock))
+
+    def set_admission(self, threshold: int, width: int = 0, depth: int = 0, seed: int = 0):
+        """Count-min admission with a fresh sketch; threshold <= 1 turns it off."""
+        if self._lib.orc_set_admission(self._h, int(depth), int(width), int(threshold),
+                                       ctypes.c_uint64(seed & (2**64 - 1))) != 0:
+            raise ValueError("oracle set_admission: bad sketch shape")
+
+    def set_recycling(self, on=True):
+        self._lib.orc_set_recycling(self._h, int(bool(on)))
+
+    def rehash(self, min_clock: int = 0) -> int:
+        """Evict keys last seen before min_clock (with tracking on) and, with
+        recycling on, rebuild the free list. Returns the number of keys kept."""
+        return int(self._lib.orc_rehash(self._h, int(min_clock)))
+
+    def entries(self):
+        """Live (key, map index, offset) entries, sorted by offset."""
+        n = int(self._lib.orc_entries(self._h, None, None, None))
+        keys = np.empty(n, np.int64)
+        tabs = np.empty(n, np.int32)
+        offs = np.empty(n, np.int64)
+        self._lib.orc_entries(self._h, _p(keys), _p(tabs), _p(offs))
+        o = np.argsort(offs, kind="stable")
+        return keys[o], tabs[o], offs[o]
+
+    def sketch(self):
+        n = int(self._lib.orc_sketch(self._h, None))
+        out = np.empty(n, np.uint32)
+        if n:
+            self._lib.orc_sketch(self._h, _p(out))
+        return out
+
+    def estimate(self, key: int, table: int = 0) -> int:
+        return int(self._lib.orc_estimate(self._h, int(key), int(table)))
+
+    def last_seen(self):
+        out = np.empty(self.n_rows, np.uint32)
+        if out.size:
+            self._lib.orc_last_seen(self._h, _p(out))
+        return out
+
+    def free_list(self):
+        """(rows not yet handed out, in order; number already handed out)."""
+        n = int(self._lib.orc_free_list(self._h, None, None))
+        out = np.empty(n, np.int64)
+        done = np.zeros(1, np.int64)
+        self._lib.orc_free_list(self._h, _p(out) if n else None, _p(done))
+        return out, int(done[0])

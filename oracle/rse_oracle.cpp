@@ -40,7 +40,29 @@
 //  * mean pooling divides by the bag length; an empty bag pools to zero and
 //    has no gradient; a missing key (offset -1) contributes nothing;
 //  * bf16 storage rounds the final double value to nearest, ties to even.
+//
+// Feature admission and eviction ("RecIS：阿里开源推荐系统统一训练框架",
+// "代码架构": a hook on the hash table for feature admission and eviction;
+// the policies themselves are not given, so these are definitions here):
+//  * admission (off unless a threshold above 1 is set): a count-min sketch of
+//    `depth` rows of `width` uint32 counters counts every lookup of a key that
+//    is absent from the map when the call starts (all lookups of the call are
+//    counted before any is inserted); an absent key is inserted only if its
+//    estimate -- the minimum of its counters after the call's counts -- is at
+//    least the threshold; otherwise its lookups get offset -1.  Counter j of a
+//    key is fmix64(key ^ map_index * golden ^ salt_j) reduced to [0, width)
+//    by a 64x64 multiply-high (murmur3 fmix64; salt_j = the (j+1)-th
+//    SplitMix64 output of the sketch seed);
+//  * age: with tracking on, every lookup that resolves to a row stamps the
+//    row with the current clock (a caller-set integer, typically the step);
+//  * eviction (rehash with a minimum clock): keys whose row's stamp is below
+//    the minimum leave the map; every other key keeps its offset;
+//  * recycling (when on): the rehash lists every row below the row counter
+//    that no remaining key references, ascending; new keys take rows from
+//    that list in order before new rows are appended.  A reused row starts
+//    over from its new key's initial value and zero optimizer state.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -64,6 +86,16 @@ uint64_t splitmix64_mix(uint64_t z) {
 }
 
 const uint64_t GOLDEN = 0x9E3779B97F4A7C15ull;  // SplitMix64 increment
+
+// MurmurHash3's 64-bit finaliser (Appleby, public domain).
+uint64_t fmix64(uint64_t k) {
+    k ^= k >> 33;
+    k *= 0xFF51AFD7ED558CCDull;
+    k ^= k >> 33;
+    k *= 0xC4CEB9FE1A85EC53ull;
+    k ^= k >> 33;
+    return k;
+}
 const double INIT_SCALE = 1.0 / 16.0;           // sigma = 2^-4
 
 // Value of column c of a freshly inserted row (exact in the storage type).
@@ -141,6 +173,49 @@ struct Table {
     std::map<int64_t, std::vector<double>> last_grad;
     std::map<int64_t, int64_t> last_count;
 
+    // Admission, age and recycling (definitions in the file header).
+    bool track = false;
+    uint32_t clock = 0;
+    std::vector<uint32_t> last_seen;   // per row
+    uint32_t admit_min = 0;
+    int32_t sk_depth = 0;
+    int64_t sk_width = 0;
+    std::vector<uint64_t> sk_salt;
+    std::vector<uint32_t> sketch;      // [depth][width]
+    bool recycle = false;
+    std::vector<int64_t> free_rows;    // ascending, from the last rehash
+    size_t free_next = 0;
+
+    bool admission_on() const { return admit_min > 1 && sk_width > 0; }
+
+    int64_t sketch_cell(uint64_t key, int32_t m, int j) const {
+        const uint64_t h = fmix64(key ^ ((uint64_t)(uint32_t)m * GOLDEN) ^ sk_salt[j]);
+        return (int64_t)(((unsigned __int128)h * (uint64_t)sk_width) >> 64);
+    }
+
+    uint32_t estimate(uint64_t key, int32_t m) const {
+        uint32_t e = UINT32_MAX;
+        for (int j = 0; j < sk_depth; ++j) e = std::min(e, sketch[(size_t)j * sk_width + sketch_cell(key, m, j)]);
+        return e;
+    }
+
+    // Row for a new key: the next listed free row, else a new one.
+    int64_t new_row(int64_t key, int32_t m) {
+        int64_t off;
+        if (recycle && free_next < free_rows.size()) {
+            off = free_rows[free_next++];
+            row_key[off] = key;
+            row_table[off] = m;
+            rows.erase(off);
+        } else {
+            off = n_rows++;
+            row_key.push_back(key);
+            row_table.push_back(m);
+            last_seen.push_back(0);
+        }
+        return off;
+    }
+
     int state_per_elem() const {
         return optim == OPT_SGD ? 0 : (optim == OPT_ADAGRAD ? 1 : 2);
     }
@@ -189,7 +264,9 @@ int orc_find_or_insert(void* h, const int64_t* ids, int64_t n_ids, const int64_t
     if (bounds[0] != 0 || bounds[(int64_t)n_tables * stride] != n_ids) return -1;
     for (int32_t t = 0; t < n_tables; ++t)
         if (bounds[(int64_t)(t + 1) * stride] < bounds[(int64_t)t * stride]) return -1;
-    int64_t n_new = 0;
+    // keys and map indices of every lookup (and the merged-mode id check)
+    std::vector<int64_t> keys(n_ids);
+    std::vector<int32_t> mi(n_ids);
     for (int32_t t = 0; t < n_tables; ++t) {
         for (int64_t i = bounds[(int64_t)t * stride]; i < bounds[(int64_t)(t + 1) * stride]; ++i) {
             int64_t key = ids[i];
@@ -199,21 +276,33 @@ int orc_find_or_insert(void* h, const int64_t* ids, int64_t n_ids, const int64_t
                 key = (int64_t)(((uint64_t)t << 56) | (uint64_t)key);
                 m = 0;
             }
-            auto& map = T->maps[m];
-            auto it = map.find(key);
-            if (it != map.end()) {
-                row_off_out[i] = it->second;
-            } else if (insert_missing) {
-                int64_t off = T->n_rows++;
-                map.emplace(key, off);
-                T->row_key.push_back(key);
-                T->row_table.push_back(m);
-                row_off_out[i] = off;
-                ++n_new;
-            } else {
-                row_off_out[i] = -1;
-            }
+            keys[i] = key;
+            mi[i] = m;
         }
+    }
+    // admission: count every lookup of a key absent at the start of the call
+    const bool admit = insert_missing && T->admission_on();
+    if (admit) {
+        for (int64_t i = 0; i < n_ids; ++i) {
+            if (T->maps[mi[i]].count(keys[i])) continue;
+            for (int j = 0; j < T->sk_depth; ++j)
+                T->sketch[(size_t)j * T->sk_width + T->sketch_cell((uint64_t)keys[i], mi[i], j)] += 1u;
+        }
+    }
+    int64_t n_new = 0;
+    for (int64_t i = 0; i < n_ids; ++i) {
+        auto& map = T->maps[mi[i]];
+        auto it = map.find(keys[i]);
+        int64_t off = -1;
+        if (it != map.end()) {
+            off = it->second;
+        } else if (insert_missing && (!admit || T->estimate((uint64_t)keys[i], mi[i]) >= T->admit_min)) {
+            off = T->new_row(keys[i], mi[i]);
+            map.emplace(keys[i], off);
+            ++n_new;
+        }
+        row_off_out[i] = off;
+        if (off >= 0 && T->track) T->last_seen[off] = T->clock;
     }
     *n_new_out = n_new;
     return 0;
@@ -392,7 +481,122 @@ int orc_import(void* h, const int64_t* keys, const int32_t* tables, const int64_
     }
     T->n_rows = n_rows;
     T->step = step;
+    T->last_seen.assign(n_rows, 0);
+    T->free_rows.clear();
+    T->free_next = 0;
     return 0;
+}
+
+// ------------------------------------------- admission, age, eviction ----
+// Tracking on: lookups stamp their rows with the clock (stamps start at 0).
+int orc_set_tracking(void* h, int32_t on) {
+    Table* T = (Table*)h;
+    T->track = on != 0;
+    std::fill(T->last_seen.begin(), T->last_seen.end(), 0u);
+    return 0;
+}
+
+int orc_set_clock(void* h, uint32_t clock) {
+    ((Table*)h)->clock = clock;
+    return 0;
+}
+
+// Admission with a fresh (zero) sketch; threshold <= 1 turns it off.
+int orc_set_admission(void* h, int32_t depth, int64_t width, uint32_t threshold, uint64_t seed) {
+    Table* T = (Table*)h;
+    if (threshold > 1 && (depth < 1 || depth > 8 || width < 1)) return -1;
+    T->admit_min = threshold;
+    T->sk_depth = threshold > 1 ? depth : 0;
+    T->sk_width = threshold > 1 ? width : 0;
+    T->sk_salt.clear();
+    for (int j = 0; j < T->sk_depth; ++j) T->sk_salt.push_back(splitmix64_mix(seed + (uint64_t)(j + 1) * GOLDEN));
+    T->sketch.assign((size_t)T->sk_depth * (size_t)T->sk_width, 0u);
+    return 0;
+}
+
+// Recycling on or off; either way the free list starts empty.
+int orc_set_recycling(void* h, int32_t on) {
+    Table* T = (Table*)h;
+    T->recycle = on != 0;
+    T->free_rows.clear();
+    T->free_next = 0;
+    return 0;
+}
+
+// Rehash: keys whose row was last seen before min_clock leave the map (only
+// with tracking on); with recycling on, the free list becomes every row
+// below the row counter that no remaining key references, ascending.
+// Returns the number of keys kept.
+int64_t orc_rehash(void* h, uint32_t min_clock) {
+    Table* T = (Table*)h;
+    std::vector<char> referenced((size_t)T->n_rows, 0);
+    int64_t kept = 0;
+    for (auto& map : T->maps) {
+        for (auto it = map.begin(); it != map.end();) {
+            const int64_t off = it->second;
+            if (!T->track || T->last_seen[off] >= min_clock) {
+                referenced[off] = 1;
+                ++kept;
+                ++it;
+            } else {
+                it = map.erase(it);
+            }
+        }
+    }
+    if (T->recycle) {
+        T->free_rows.clear();
+        T->free_next = 0;
+        for (int64_t o = 0; o < T->n_rows; ++o)
+            if (!referenced[o]) T->free_rows.push_back(o);
+    }
+    return kept;
+}
+
+// Live entries (key, map index, offset) in no particular order; returns n.
+int64_t orc_entries(void* h, int64_t* keys_out, int32_t* tabs_out, int64_t* offs_out) {
+    Table* T = (Table*)h;
+    int64_t q = 0;
+    for (size_t m = 0; m < T->maps.size(); ++m) {
+        for (auto& kv : T->maps[m]) {
+            if (keys_out) {
+                keys_out[q] = kv.first;
+                tabs_out[q] = (int32_t)m;
+                offs_out[q] = kv.second;
+            }
+            ++q;
+        }
+    }
+    return q;
+}
+
+// Sketch counters [depth * width]; returns depth * width.
+int64_t orc_sketch(void* h, uint32_t* out) {
+    Table* T = (Table*)h;
+    if (out) std::copy(T->sketch.begin(), T->sketch.end(), out);
+    return (int64_t)T->sketch.size();
+}
+
+uint32_t orc_estimate(void* h, int64_t key, int32_t m) {
+    Table* T = (Table*)h;
+    return T->admission_on() ? T->estimate((uint64_t)key, m) : 0u;
+}
+
+// Row stamps [n_rows].
+int orc_last_seen(void* h, uint32_t* out) {
+    Table* T = (Table*)h;
+    std::copy(T->last_seen.begin(), T->last_seen.end(), out);
+    return 0;
+}
+
+// Free list: the rows not yet handed out, in order; returns their number
+// (out may be null) and the number already handed out.
+int64_t orc_free_list(void* h, int64_t* out, int64_t* handed_out) {
+    Table* T = (Table*)h;
+    const int64_t n = (int64_t)(T->free_rows.size() - T->free_next);
+    if (out)
+        for (int64_t q = 0; q < n; ++q) out[q] = T->free_rows[T->free_next + q];
+    if (handed_out) *handed_out = (int64_t)T->free_next;
+    return n;
 }
 
 double orc_init_value(uint64_t key, int32_t table, int32_t c, uint64_t seed, int32_t wdtype) {
