@@ -271,6 +271,70 @@ int rse_idmap_export(rse_idmap* map, int64_t* d_keys_out, int32_t* d_table_out,
 int rse_idmap_import(rse_idmap* map, const int64_t* d_keys, const int32_t* d_tables, const int64_t* d_offs,
                      int64_t n, void* stream);
 
+/* ----------------------------------- admission, eviction, resize ----- */
+/*
+ * The hook on the hash table for feature admission and eviction ("RecIS：
+ * 阿里开源推荐系统统一训练框架", "代码架构").  The pages name the hook but
+ * give no policy; the policies here are definitions:
+ *
+ * Age.  rse_idmap_set_stamps attaches one uint32 stamp per row (caller
+ * memory, n_stamps >= the blocks' capacity at every find call, else that
+ * call returns RSE_ERR_INVALID_ARG; the caller zeroes it).  While attached,
+ * every lookup of idmap_find_or_insert that resolves to a row writes the
+ * map's clock (rse_idmap_set_clock, host-side, no launch) into the row's
+ * stamp.  NULL / 0 detaches.  A call that fails may already have stamped
+ * the rows it found.
+ *
+ * Admission.  rse_idmap_set_admission attaches a count-min sketch of
+ * `depth` (1..8) rows of `width` uint32 counters (caller memory, depth *
+ * width entries; the call zeroes it on `stream`) and a threshold.  With
+ * insert_missing, every lookup of a key absent from the map when the call
+ * starts adds 1 to the key's counter in each row (counter j of key k in
+ * region r: fmix64(k ^ r * 0x9E3779B97F4A7C15 ^ salt_j) reduced to
+ * [0, width) by a 64x64 multiply-high, salt_j the (j+1)-th SplitMix64
+ * output of `seed`); then an absent key is inserted iff the minimum of its
+ * counters is >= threshold, else its lookups get -1.  All lookups of a key
+ * in a call get the same answer.  Counters never decay (they wrap after
+ * 2^32 counts).  threshold <= 1 turns admission off (d_sketch may be NULL).
+ * A call that fails (capacity) takes its counts back; a call with a bad id
+ * counts nothing.
+ *
+ * Eviction and resize.  rse_idmap_rehash clears `dst` (a map with the same
+ * number of tables and the same merged flag as `src`, in memory that does
+ * not overlap it; any size) and copies every key of `src` into it with the
+ * same offset, except, when `src` has stamps attached, keys whose row's
+ * stamp is below min_clock (those are evicted).  With min_clock 0 or no
+ * stamps it is a plain resize.  If a table's kept keys exceed dst's
+ * max_load, dst's sticky status becomes RSE_ERR_IDMAP_FULL, dst stays empty
+ * and nothing else changes.  Otherwise, if the blocks have a free list
+ * (rse_blocks_set_free_list, capacity >= the blocks' capacity, else
+ * RSE_ERR_INVALID_ARG), it is rebuilt: every row below rows_used that no
+ * kept key references, ascending; idmap_find_or_insert then gives new keys
+ * (ranked by first sight) the listed rows in order before it takes rows
+ * past rows_used, and initialises them like new rows.  Without a free list
+ * evicted rows are not reused.  `src` is not modified; dst takes over
+ * src's stamps, clock and admission settings (host side).  Workspace: at
+ * least rse_idmap_rehash_workspace_size bytes (a bit per row of the blocks'
+ * capacity); stream-ordered, no synchronisation.  A row offset in `src` at
+ * or beyond the blocks' capacity fails the call with RSE_ERR_BAD_INPUT in
+ * dst's status.
+ */
+int rse_idmap_set_stamps(rse_idmap* map, uint32_t* d_stamps, int64_t n_stamps);
+int rse_idmap_set_clock(rse_idmap* map, uint32_t clock);
+int rse_idmap_set_admission(rse_idmap* map, uint32_t* d_sketch, int32_t depth, int64_t width,
+                            uint32_t threshold, uint64_t seed, void* stream);
+int rse_idmap_rehash_workspace_size(const rse_blocks* blocks, size_t* bytes_out);
+int rse_idmap_rehash(rse_idmap* dst, rse_idmap* src, rse_blocks* blocks, uint32_t min_clock, void* d_ws,
+                     size_t ws_bytes, void* stream);
+
+/* Attach a free list of rows (caller memory, `capacity` uint32 entries;
+ * NULL / 0 detaches).  Either way the list is emptied (on `stream`); a later
+ * rse_idmap_rehash fills it. */
+int rse_blocks_set_free_list(rse_blocks* blocks, uint32_t* d_free, int64_t capacity, void* stream);
+/* Entries of the free list handed out so far and entries left (those are
+ * d_free[head .. head + count)).  Synchronises `stream`. */
+int rse_blocks_free_status(rse_blocks* blocks, int64_t* head_out, int64_t* count_out, void* stream);
+
 /* ------------------------------------------------- pooled forward ----- */
 /*
  * out[b, t, :] = sum over the rows of bag j = t*batch + b ("DLRM ... 2.1":

@@ -153,6 +153,31 @@ class EmbeddingBlocks:
     def set_rows_used(self, rows_used: int, stream=None):
         check(lib.rse_blocks_set_rows_used(self.handle, int(rows_used), _stream(stream)), "rse_blocks_set_rows_used")
 
+    def enable_free_list(self, capacity: int | None = None, stream=None):
+        """Attach an (empty) free list of recycled rows for `capacity` rows
+        (default: the current capacity); a map rehash fills it."""
+        cap = self.capacity if capacity is None else int(capacity)
+        self.free_rows = torch.zeros(max(cap, 1), dtype=torch.int32, device=self.device)   # uint32 entries
+        check(lib.rse_blocks_set_free_list(self.handle, _ptr(self.free_rows), cap, _stream(stream)),
+              "rse_blocks_set_free_list")
+        return self
+
+    def disable_free_list(self, stream=None):
+        check(lib.rse_blocks_set_free_list(self.handle, None, 0, _stream(stream)), "rse_blocks_set_free_list")
+        self.free_rows = None
+
+    def free_list(self, stream=None):
+        """(rows already handed out, rows left as an int64 tensor, in order);
+        synchronises the stream."""
+        head, count = ctypes.c_int64(), ctypes.c_int64()
+        check(lib.rse_blocks_free_status(self.handle, ctypes.byref(head), ctypes.byref(count), _stream(stream)),
+              "rse_blocks_free_status")
+        rows = getattr(self, "free_rows", None)
+        if rows is None or count.value == 0:
+            return head.value, torch.zeros(0, dtype=torch.int64, device=self.device)
+        left = rows[head.value:head.value + count.value].to(torch.int64) & 0xFFFFFFFF
+        return head.value, left
+
     def read_rows(self, offs: torch.Tensor, stream=None):
         """Weights (widened to fp32) and state of rows `offs` (int64 CUDA)."""
         _need(offs, torch.int64, "offs")
@@ -221,6 +246,75 @@ class IdMap:
             raise ValueError("keys, tables and offs must have the same length")
         check(lib.rse_idmap_import(self.handle, _ptr(keys), _ptr(tables), _ptr(offs), n, _stream(stream)),
               "rse_idmap_import")
+
+    # ---------------------------------- admission, age, eviction, resize --
+    def track_age(self, n_rows: int, stream=None):
+        """Attach zeroed per-row stamps for rows [0, n_rows); lookups write the
+        clock into them (n_rows must cover the blocks' capacity)."""
+        self.stamps = torch.zeros(max(int(n_rows), 1), dtype=torch.int32, device=self.device)   # uint32
+        check(lib.rse_idmap_set_stamps(self.handle, _ptr(self.stamps), int(n_rows)), "rse_idmap_set_stamps")
+        return self
+
+    def set_clock(self, clock: int):
+        check(lib.rse_idmap_set_clock(self.handle, int(clock) & 0xFFFFFFFF), "rse_idmap_set_clock")
+
+    def enable_admission(self, threshold: int, width: int, depth: int = 4, seed: int = 0, stream=None):
+        """Count-min admission: an absent key is inserted once its estimated
+        count of absent lookups reaches `threshold` (<= 1 turns it off)."""
+        if threshold <= 1:
+            self.sketch = None
+            check(lib.rse_idmap_set_admission(self.handle, None, 0, 0, int(threshold), 0, _stream(stream)),
+                  "rse_idmap_set_admission")
+            return self
+        self.sketch = torch.empty(int(depth) * int(width), dtype=torch.int32, device=self.device)   # uint32
+        self.sketch_shape = (int(depth), int(width))
+        check(lib.rse_idmap_set_admission(self.handle, _ptr(self.sketch), int(depth), int(width), int(threshold),
+                                          int(seed) & (2**64 - 1), _stream(stream)), "rse_idmap_set_admission")
+        return self
+
+    def rehash_into(self, dst: "IdMap", blocks: EmbeddingBlocks, min_clock: int = 0, stream=None):
+        """Copy this map's keys into `dst` (same tables, any size), evicting
+        keys last seen before min_clock when stamps are attached; rebuilds
+        the blocks' free list if one is attached.  Stream-ordered: read
+        dst.status() for the outcome."""
+        sz = ctypes.c_size_t()
+        check(lib.rse_idmap_rehash_workspace_size(blocks.handle, ctypes.byref(sz)), "rse_idmap_rehash_workspace_size")
+        ws = _bytes(sz.value, self.device)
+        check(lib.rse_idmap_rehash(dst.handle, self.handle, blocks.handle, int(min_clock) & 0xFFFFFFFF, _ptr(ws),
+                                   sz.value, _stream(stream)), "rse_idmap_rehash")
+        dst._ws_keep = ws            # the stream may still be reading it
+        for name in ("stamps", "sketch", "sketch_shape"):
+            if hasattr(self, name):
+                setattr(dst, name, getattr(self, name))
+
+    def _replace_with(self, other: "IdMap"):
+        """Take over other's library object and memory (other gets ours)."""
+        self._finalizer.detach()
+        other._finalizer.detach()
+        self.handle, other.handle = other.handle, self.handle
+        self.mem, other.mem = other.mem, self.mem
+        self.slots_per_table, other.slots_per_table = other.slots_per_table, self.slots_per_table
+        self._finalizer = weakref.finalize(self, lib.rse_idmap_destroy, self.handle)
+        other._finalizer = weakref.finalize(other, lib.rse_idmap_destroy, other.handle)
+
+    def _rebuild(self, slots_per_table, blocks, min_clock, stream):
+        dst = IdMap(slots_per_table, self.max_load, self.merged, self.hash_seed, self.device, stream)
+        self.rehash_into(dst, blocks, min_clock, stream)
+        st, _ = dst.status(stream)
+        if st != 0:
+            raise RseError("rse_idmap_rehash", st)
+        self._replace_with(dst)
+        return self
+
+    def evict(self, blocks: EmbeddingBlocks, min_clock: int, stream=None):
+        """Drop keys last seen before min_clock (rows go to the free list, if
+        any); the map keeps its size.  Synchronises the stream."""
+        return self._rebuild(self.slots_per_table, blocks, min_clock, stream)
+
+    def resize(self, slots_per_table, blocks: EmbeddingBlocks, stream=None):
+        """Rehash every key into new slot regions of the given sizes (offsets
+        unchanged).  Synchronises the stream."""
+        return self._rebuild([int(x) for x in slots_per_table], blocks, 0, stream)
 
     def export(self, capacity: int, stream=None):
         """Live entries (keys int64, table int32, offsets int64), any order."""

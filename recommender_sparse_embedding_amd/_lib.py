@@ -63,6 +63,13 @@ SIGNATURES = {
     "rse_idmap_import": ([_P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "rse_blocks_write_rows": ([_P, _P, _I64, _P, _P, _P], ctypes.c_int),
     "rse_blocks_set_rows_used": ([_P, _I64, _P], ctypes.c_int),
+    "rse_idmap_set_stamps": ([_P, _P, _I64], ctypes.c_int),
+    "rse_idmap_set_clock": ([_P, ctypes.c_uint32], ctypes.c_int),
+    "rse_idmap_set_admission": ([_P, _P, _I32, _I64, ctypes.c_uint32, _U64, _P], ctypes.c_int),
+    "rse_idmap_rehash_workspace_size": ([_P, _PSZ], ctypes.c_int),
+    "rse_idmap_rehash": ([_P, _P, _P, ctypes.c_uint32, _P, _SZ, _P], ctypes.c_int),
+    "rse_blocks_set_free_list": ([_P, _P, _I64, _P], ctypes.c_int),
+    "rse_blocks_free_status": ([_P, _PI64, _PI64, _P], ctypes.c_int),
     "rse_idmap_status": ([_P, _PI32, _PI64, _P], ctypes.c_int),
     "rse_idmap_clear_status": ([_P, _P], ctypes.c_int),
     "rse_idmap_export": ([_P, _P, _P, _P, _I64, _P, _P], ctypes.c_int),

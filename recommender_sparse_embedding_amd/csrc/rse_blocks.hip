@@ -20,6 +20,8 @@ __global__ void k_blocks_clear(BlocksHeader* h, uint64_t* chunks, int32_t max_ch
     if (tid == 0) {
         h->rows_used = 0;
         h->status = 0;
+        h->free_head = 0;
+        h->free_count = 0;
     }
     for (int i = tid; i < max_chunks; i += gridDim.x * blockDim.x) chunks[i] = 0;
 }
@@ -82,6 +84,11 @@ __global__ void k_write_rows(RowsView rv, int64_t capacity, const int64_t* offs,
 }
 
 __global__ void k_set_rows_used(BlocksHeader* h, int64_t rows) { h->rows_used = rows; }
+
+__global__ void k_reset_free_list(BlocksHeader* h) {
+    h->free_head = 0;
+    h->free_count = 0;
+}
 
 }  // namespace
 
@@ -241,5 +248,24 @@ const char* rse_status_str(int status) {
 }
 
 int rse_version(void) { return 100; }
+
+int rse_blocks_set_free_list(rse_blocks* blocks, uint32_t* d_free, int64_t capacity, void* stream) {
+    if (!blocks || capacity < 0 || (capacity > 0 && !d_free)) return RSE_ERR_INVALID_ARG;
+    blocks->d_free = capacity > 0 ? d_free : nullptr;
+    blocks->free_cap = capacity > 0 ? capacity : 0;
+    hipLaunchKernelGGL(k_reset_free_list, dim3(1), dim3(1), 0, as_stream(stream), blocks->header());
+    return launch_status();
+}
+
+int rse_blocks_free_status(rse_blocks* blocks, int64_t* head_out, int64_t* count_out, void* stream) {
+    if (!blocks) return RSE_ERR_INVALID_ARG;
+    BlocksHeader h;
+    if (hipMemcpyAsync(&h, blocks->header(), sizeof(h), hipMemcpyDeviceToHost, as_stream(stream)) != hipSuccess)
+        return RSE_ERR_HIP;
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return RSE_ERR_HIP;
+    if (head_out) *head_out = h.free_head;
+    if (count_out) *count_out = h.free_count;
+    return RSE_OK;
+}
 
 }  // extern "C"

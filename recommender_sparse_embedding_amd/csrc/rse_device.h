@@ -50,7 +50,9 @@ struct BlocksHeader {
     int64_t rows_used;
     int32_t status;
     int32_t pad0;
-    int64_t pad[30];
+    int64_t free_head;    // free-list entries already handed out
+    int64_t free_count;   // free-list entries left, from free_head on
+    int64_t pad[28];
 };
 static_assert(sizeof(BlocksHeader) == 256, "BlocksHeader size");
 

@@ -21,6 +21,8 @@ struct rse_blocks {
     uint64_t seed;
     char* d_meta;           // BlocksHeader followed by the chunk table
     std::vector<uint64_t> chunks;   // host copy of the chunk table
+    uint32_t* d_free = nullptr;     // free list of rows (caller memory), or null
+    int64_t free_cap = 0;
 
     rse::BlocksHeader* header() const { return reinterpret_cast<rse::BlocksHeader*>(d_meta); }
     uint64_t* chunk_table() const {
@@ -46,6 +48,19 @@ struct rse_idmap {
     double max_load;
     char* d_mem;            // MapHeader, TableDir[n_tables], slots
     std::vector<rse::TableDir> dir;   // host copy of the static directory
+    // age tracking: one stamp per row (caller memory), written with `clock`
+    uint32_t* d_stamps = nullptr;
+    int64_t n_stamps = 0;
+    uint32_t clock = 0;
+    // admission: count-min sketch [depth][width] (caller memory)
+    uint32_t* d_sketch = nullptr;
+    int32_t sk_depth = 0;
+    int64_t sk_width = 0;
+    uint32_t admit_min = 0;
+    uint64_t sk_salt[8] = {};
+
+    size_t mem_bytes() const;
+    bool admission_on() const { return d_sketch && admit_min > 1 && sk_width > 0; }
 
     rse::MapHeader* header() const { return reinterpret_cast<rse::MapHeader*>(d_mem); }
     rse::TableDir* d_dir() const {

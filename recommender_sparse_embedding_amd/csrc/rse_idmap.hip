@@ -35,6 +35,11 @@ rse::Slot* rse_idmap::d_slots() const {
         d_mem + align_up(sizeof(MapHeader) + (size_t)n_tables * sizeof(TableDir), 256));
 }
 
+size_t rse_idmap::mem_bytes() const {
+    return align_up(sizeof(MapHeader) + (size_t)n_tables * sizeof(TableDir), 256) +
+           (size_t)total_slots * sizeof(Slot);
+}
+
 namespace {
 
 constexpr int PROBE_BLOCK = 256;
@@ -45,12 +50,19 @@ constexpr uint32_t SIDE_MARK = 0xFFFFFFFFu;   // slot index meaning "side slot"
 struct Ws {
     unsigned long long* ctr;   // [0] misses [1] overflow [2] bad input [3] ok
                                // [4] rows_used before [5] new keys [6] status code
+                               // [7] free-list head before [8] rows taken from it
+                               // [9] admission candidates [10] admitted lookups
     uint32_t* miss_list;       // lookup indices that missed (any order)
     uint32_t* slot_of;         // per lookup: claimed slot (SIDE_MARK for the side slot)
     uint32_t* flag;            // per lookup: 0 hit, 1 pending, 2 first sight
     uint32_t* tile_sum;        // per scan tile
     uint64_t* new_key;         // per new row (by rank): key
     uint32_t* new_tab;         // per new row: table index used by the init
+    // Admission lists, in memory that k_rank_commit fills only later: the
+    // candidates (lookups of absent keys) over new_key, the admitted ones
+    // over new_tab.
+    uint32_t* cand;
+    uint32_t* admitted;
 };
 
 Ws carve(void* base, int64_t n_ids, size_t* total) {
@@ -65,6 +77,8 @@ Ws carve(void* base, int64_t n_ids, size_t* total) {
     w.tile_sum = c.take<uint32_t>(tiles + 1);
     w.new_key = c.take<uint64_t>(n);
     w.new_tab = c.take<uint32_t>(n);
+    w.cand = reinterpret_cast<uint32_t*>(w.new_key);
+    w.admitted = w.new_tab;
     if (total) *total = c.size();
     return w;
 }
@@ -79,10 +93,31 @@ struct ProbeArgs {
     int32_t n_tables;       // logical tables of the call
     int32_t merged;
     int32_t insert;
-    int32_t pad;
+    int32_t collect;        // list absent lookups as admission candidates
     int64_t* row_off;
+    const uint32_t* list;   // probe only these lookups (with *list_n), or null: all
+    const unsigned long long* list_n;
+    uint32_t* stamps;       // per-row last-seen clock, or null
+    int64_t n_stamps;
+    uint32_t clock;
+    int32_t pad2;
     Ws ws;
 };
+
+// Appends `value` for every lane with `me` set, one atomic per wave.
+__device__ __forceinline__ void wave_append(bool me, uint32_t value, unsigned long long* counter, uint32_t* list) {
+    const unsigned long long mm = __ballot(me);
+    if (!mm) return;
+    const int leader = __ffsll((long long)mm) - 1;
+    unsigned long long pos0 = 0;
+    if (lane_id() == leader) pos0 = atomicAdd(counter, (unsigned long long)__popcll(mm));
+    pos0 = __shfl(pos0, leader, WAVE);
+    if (me) list[pos0 + __popcll(mm & ((1ull << lane_id()) - 1))] = value;
+}
+
+__device__ __forceinline__ void stamp_row(uint32_t* stamps, int64_t n_stamps, uint32_t clock, uint64_t off) {
+    if (stamps && off < (uint64_t)n_stamps) stamps[off] = clock;
+}
 
 // -------------------------------------------------------------- reset ----
 __global__ void k_reset(Ws ws, TableDir* dir, int32_t n_regions, int64_t n_tiles) {
@@ -241,15 +276,17 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
     const int gshift = g * 8;
     const int64_t wave_global = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t n_items = a.list ? (int64_t)*a.list_n : a.n_ids;
 
-    for (int64_t base = wave_global * WAVE; base < a.n_ids; base += n_waves * WAVE) {
-        // (1) lanes past the end repeat the last lookup's reads, so that every
+    for (int64_t base = wave_global * WAVE; base < n_items; base += n_waves * WAVE) {
+        // (1) lanes past the end repeat the last item's reads, so that every
         // load is issued unconditionally
-        const int64_t i = base + lane;
-        const bool active = i < a.n_ids;
-        const int64_t ic = active ? i : a.n_ids - 1;
-        const int t = table_of(sb, a.n_tables, ic);
-        uint64_t key = (uint64_t)a.ids[ic];
+        const int64_t q = base + lane;
+        const bool active = q < n_items;
+        const int64_t qc = active ? q : n_items - 1;
+        const int64_t i = a.list ? (int64_t)a.list[qc] : qc;    // lookup index
+        const int t = table_of(sb, a.n_tables, i);
+        uint64_t key = (uint64_t)a.ids[i];
         int region = t;
         uint64_t res = RES_SLOW;
         if (a.merged) {
@@ -295,7 +332,9 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
             a.row_off[i] = res < PENDING_BASE ? (int64_t)res : -1;
             a.ws.flag[i] = 0;
             if (res == RES_BAD) a.ws.ctr[2] = 1;
+            if (res < PENDING_BASE) stamp_row(a.stamps, a.n_stamps, a.clock, res);
         }
+        if (a.collect) wave_append(res == RES_ABSENT, (uint32_t)i, &a.ws.ctr[9], a.ws.cand);
 
         // (3) the full probe for the rest: group g takes the g-th lowest
         uint64_t slow = __ballot(res == RES_SLOW);
@@ -307,7 +346,7 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
             for (int k = 0; k < 8; ++k) slow &= slow - 1;
             const uint64_t key_r = shfl_idx(key, src);
             const int region_r = shfl_idx(region, src);
-            const int64_t ir = base + src;
+            const int64_t ir = shfl_idx(i, src);
             int kind = 2;
             uint64_t val = 0;
             uint32_t slot_idx = 0;
@@ -322,10 +361,12 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
                     pos0 = atomicAdd(&a.ws.ctr[0], (unsigned long long)__popcll(mm));
                 pos0 = __shfl(pos0, __ffsll((long long)mm) - 1, WAVE);
             }
+            if (a.collect) wave_append(leader && kind == 2, (uint32_t)ir, &a.ws.ctr[9], a.ws.cand);
             if (leader) {
                 if (kind == 0) {
                     a.row_off[ir] = (int64_t)val;
                     a.ws.flag[ir] = 0;
+                    stamp_row(a.stamps, a.n_stamps, a.clock, val);
                 } else if (kind == 1) {
                     const unsigned long long below = mm & ((1ull << lane) - 1);
                     a.ws.miss_list[pos0 + __popcll(below)] = (uint32_t)ir;
@@ -411,6 +452,90 @@ __global__ void k_mark(MarkArgs a) {
         if (s_new[r]) atomicAdd((unsigned long long*)&a.dir[r].new_keys, (unsigned long long)s_new[r]);
 }
 
+// ---------------------------------------------------------- admission --
+// Count-min sketch of the lookups of absent keys.  Counter j of a key in
+// region r is fmix64(key ^ r * gamma ^ salt_j) reduced to [0, width); the
+// estimate is the minimum over the rows.  Increments are integer atomics, so
+// the counters after a call do not depend on thread timing.
+struct AdmitArgs {
+    const int64_t* ids;
+    const int64_t* bounds;
+    int64_t stride;
+    int32_t n_tables;
+    int32_t merged;
+    uint32_t* sketch;
+    int64_t width;
+    int32_t depth;
+    uint32_t threshold;
+    uint64_t salt[8];
+    Ws ws;
+};
+
+__device__ __forceinline__ int64_t sketch_cell(uint64_t key, uint32_t region, uint64_t salt, int64_t width) {
+    return reduce_range(fmix64(key ^ ((uint64_t)region * SM64_GAMMA) ^ salt), width);
+}
+
+// Key and region of candidate lookup i.
+__device__ __forceinline__ void cand_key(const AdmitArgs& a, const int64_t* sb, uint32_t i, uint64_t& key,
+                                         uint32_t& region) {
+    const int t = table_of(sb, a.n_tables, i);
+    key = (uint64_t)a.ids[i];
+    region = (uint32_t)t;
+    if (a.merged) {
+        key |= (uint64_t)t << 56;
+        region = 0;
+    }
+}
+
+// Counts the candidates (undo 0), or takes the counts back (undo 1, after
+// k_decide, for a call that does not commit).  Nothing is counted for a call
+// with a bad id.
+__global__ void k_admit_count(AdmitArgs a, int32_t undo) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const unsigned long long n = a.ws.ctr[9];
+    if (n == 0 || a.ws.ctr[2] != 0) return;
+    if (undo && a.ws.ctr[3] != 0) return;
+    for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    __syncthreads();
+    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n;
+         q += (unsigned long long)gridDim.x * blockDim.x) {
+        uint64_t key;
+        uint32_t region;
+        cand_key(a, sb, a.ws.cand[q], key, region);
+        for (int j = 0; j < a.depth; ++j) {
+            uint32_t* c = a.sketch + (int64_t)j * a.width + sketch_cell(key, region, a.salt[j], a.width);
+            if (undo) atomicSub(c, 1u);
+            else atomicAdd(c, 1u);
+        }
+    }
+}
+
+// Lists the candidates whose estimate reaches the threshold.
+__global__ void k_admit_pick(AdmitArgs a) {
+    __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    const unsigned long long n = a.ws.ctr[9];
+    if (n == 0 || a.ws.ctr[2] != 0) return;
+    for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    __syncthreads();
+    for (unsigned long long q0 = (unsigned long long)blockIdx.x * blockDim.x; q0 < n;
+         q0 += (unsigned long long)gridDim.x * blockDim.x) {
+        const unsigned long long q = q0 + threadIdx.x;
+        bool pick = false;
+        uint32_t i = 0;
+        if (q < n) {
+            i = a.ws.cand[q];
+            uint64_t key;
+            uint32_t region;
+            cand_key(a, sb, i, key, region);
+            uint32_t est = 0xFFFFFFFFu;
+            for (int j = 0; j < a.depth; ++j)
+                est = min(est, a.sketch[(int64_t)j * a.width + sketch_cell(key, region, a.salt[j], a.width)]);
+            pick = est >= a.threshold;
+        }
+        wave_append(pick, i, &a.ws.ctr[10], a.ws.admitted);
+    }
+}
+
 constexpr int DECIDE_BLOCK = 256;   // small, so that it finds room beside other streams' kernels
 
 // Block-wide exclusive scan of DECIDE_BLOCK values (one per thread); returns
@@ -484,13 +609,21 @@ __global__ __launch_bounds__(DECIDE_BLOCK) void k_decide(DecideArgs a) {
         int fail = 0;
         if (a.ws.ctr[2]) fail = RSE_ERR_BAD_INPUT;
         else if (a.ws.ctr[1] || s_fail) fail = RSE_ERR_IDMAP_FULL;
+        // new keys take listed free rows first, then rows past rows_used
         const int64_t used = a.bh->rows_used;
-        if (!fail && used + (int64_t)total > a.capacity) fail = RSE_ERR_NEED_GROW;
+        const int64_t head = a.bh->free_head;
+        const int64_t take = min((int64_t)total, a.bh->free_count);
+        const int64_t tail = (int64_t)total - take;
+        if (!fail && used + tail > a.capacity) fail = RSE_ERR_NEED_GROW;
         a.ws.ctr[4] = (unsigned long long)used;
         a.ws.ctr[5] = total;
+        a.ws.ctr[7] = (unsigned long long)head;
+        a.ws.ctr[8] = (unsigned long long)take;
         if (!fail) {
             a.ws.ctr[3] = 1;
-            a.bh->rows_used = used + (int64_t)total;
+            a.bh->rows_used = used + tail;
+            a.bh->free_head = head + take;
+            a.bh->free_count -= take;
             *a.n_new_out = (int64_t)total;
         } else {
             a.ws.ctr[3] = 0;
@@ -518,8 +651,15 @@ struct CommitArgs {
     int32_t n_tables;
     int32_t pad;
     int64_t n;
+    const uint32_t* free_list;
     Ws ws;
 };
+
+// Row of the new key ranked rk: listed free rows first, then rows_used on.
+__device__ __forceinline__ uint64_t new_row_of(const Ws& ws, const uint32_t* free_list, uint64_t rk) {
+    const uint64_t take = ws.ctr[8];
+    return rk < take ? (uint64_t)free_list[ws.ctr[7] + rk] : ws.ctr[4] + (rk - take);
+}
 
 // One block per tile of SCAN_TILE lookups (16 per thread).  If the call
 // commits, the tile's first sights get their ranks (the tile's prefix from
@@ -532,7 +672,6 @@ __global__ __launch_bounds__(256) void k_rank_commit(CommitArgs a) {
     if (a.ws.ctr[0] == 0) return;
     for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
     const bool ok = a.ws.ctr[3] != 0;
-    const uint64_t used = a.ws.ctr[4];
     const int64_t i0 = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * 16;
     uint32_t f[16];
     uint32_t c = 0;
@@ -563,7 +702,7 @@ __global__ __launch_bounds__(256) void k_rank_commit(CommitArgs a) {
         const int t = table_of(sb, a.n_tables, i);
         const int region = a.merged ? 0 : t;
         if (ok) {
-            const uint64_t off = used + rk;
+            const uint64_t off = new_row_of(a.ws, a.free_list, rk);
             uint64_t key = (uint64_t)a.ids[i];
             if (a.merged) key = ((uint64_t)t << 56) | key;
             if (s == SIDE_MARK) a.dir[region].side_val = off;
@@ -594,13 +733,19 @@ struct FinishArgs {
     uint64_t seed;
     int32_t dim;
     int32_t pad;
+    const uint32_t* free_list;
+    uint32_t* stamps;
+    int64_t n_stamps;
+    uint32_t clock;
+    int32_t pad2;
     Ws ws;
 };
 
 // One grid-stride range over two kinds of items: first every pending lookup
-// (it reads its key's final offset, or -1 if the call did not commit), then
-// every 16 bytes of the new rows (weights from the key hash, state zero;
-// rows are consecutive so the writes are contiguous).
+// (it reads its key's final offset, or -1 if the call did not commit, and
+// stamps the row), then every 16 bytes of the new rows (weights from the key
+// hash, state zero; recycled rows come from the ascending free list and the
+// rest are consecutive, so the writes are mostly contiguous).
 template <bool BF16>
 __global__ void k_finish(FinishArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
@@ -610,7 +755,6 @@ __global__ void k_finish(FinishArgs a) {
     __syncthreads();
     const bool ok = a.ws.ctr[3] != 0;
     const uint64_t n_new = ok ? a.ws.ctr[5] : 0;
-    const uint64_t used = a.ws.ctr[4];
     const int64_t q_per_row = a.row_bytes / 16;
     const int64_t w_q = (int64_t)a.dim * (BF16 ? 2 : 4) / 16;   // 16-byte units of weights
     const int per_q = BF16 ? 8 : 4;
@@ -628,6 +772,7 @@ __global__ void k_finish(FinishArgs a) {
                 } else {
                     v = (int64_t)a.slots[s].val;
                 }
+                stamp_row(a.stamps, a.n_stamps, a.clock, (uint64_t)v);
             }
             a.row_off[i] = v;
             continue;
@@ -635,7 +780,7 @@ __global__ void k_finish(FinishArgs a) {
         const uint64_t ee = e - n_miss;
         const uint64_t r = ee / (uint64_t)q_per_row;
         const int64_t qi = (int64_t)(ee - r * (uint64_t)q_per_row);
-        char* row = a.rv.row((int64_t)(used + r));
+        char* row = a.rv.row((int64_t)new_row_of(a.ws, a.free_list, r));
         u32x4 out = u32x4{0u, 0u, 0u, 0u};
         if (qi < w_q) {
             const uint64_t key = a.ws.new_key[r];
@@ -677,6 +822,11 @@ __global__ void k_clear_header(MapHeader* h, int32_t n_tables, int32_t merged) {
 }
 
 __global__ void k_clear_status(MapHeader* h) { h->status = 0; }
+
+__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
 
 // ------------------------------------------------------------ export -----
 __global__ void k_export(const Slot* slots, const TableDir* dir, int32_t n_regions, int64_t total_slots,
@@ -785,6 +935,244 @@ __global__ void k_import_insert(Slot* slots, TableDir* dir, const int64_t* keys,
             b = (b + 1 == d.n_buckets) ? 0 : b + 1;
         }
         if (!done) atomicCAS(&h->status, 0, (int32_t)RSE_ERR_IDMAP_FULL);
+    }
+}
+
+// ------------------------------------------------------------ rehash -----
+// Copies the keys of one map into another (cleared) map with the same
+// regions, keeping their offsets, and drops the keys whose row was last seen
+// before a minimum clock.  With a free list attached to the blocks, the
+// free list is then rebuilt as every row below rows_used that no kept key
+// references, ascending.  Kernels: clear the destination and a row bitmap;
+// count kept keys per region and mark their rows; decide (every region
+// within its load limit); insert; then count, scan and write the free rows.
+// A failed decision leaves the source, the blocks and the free list as they
+// were.
+constexpr int FL_BLOCK = 256;            // one 32-row bitmap word per thread
+constexpr int64_t FL_TILE_ROWS = FL_BLOCK * 32;
+
+struct RehashWs {
+    unsigned long long* ctr;   // [0] go flag
+    uint32_t* bitmap;          // one bit per row: referenced by a kept key
+    uint32_t* tile_sum;        // free rows per tile of FL_TILE_ROWS rows, then their scan
+};
+
+RehashWs carve_rehash(void* base, int64_t rows, size_t* total) {
+    Carver c(base);
+    RehashWs w;
+    const int64_t words = (rows + 31) / 32;
+    const int64_t tiles = (rows + FL_TILE_ROWS - 1) / FL_TILE_ROWS;
+    w.ctr = c.take<unsigned long long>(16);
+    w.bitmap = c.take<uint32_t>((size_t)(words > 0 ? words : 1));
+    w.tile_sum = c.take<uint32_t>((size_t)tiles + 1);
+    if (total) *total = c.size();
+    return w;
+}
+
+struct RehashArgs {
+    const Slot* src_slots;
+    const TableDir* src_dir;
+    int64_t src_total;
+    int32_t n_regions;
+    int32_t use_stamps;
+    Slot* dst_slots;
+    TableDir* dst_dir;
+    MapHeader* dh;
+    const uint32_t* stamps;
+    int64_t n_stamps;
+    uint32_t min_clock;
+    int32_t pad;
+    int64_t bitmap_rows;
+    RehashWs ws;
+};
+
+__device__ __forceinline__ bool rh_keep(const RehashArgs& a, uint64_t off) {
+    return !a.use_stamps || off >= (uint64_t)a.n_stamps || a.stamps[off] >= a.min_clock;
+}
+
+__global__ void k_rh_reset(RehashArgs a, int64_t n_words) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t w = tid; w < n_words; w += (int64_t)gridDim.x * blockDim.x) a.ws.bitmap[w] = 0;
+    for (int64_t r = tid; r < a.n_regions; r += (int64_t)gridDim.x * blockDim.x) {
+        a.dst_dir[r].n_keys = 0;
+        a.dst_dir[r].side_val = EMPTY_VAL;
+        a.dst_dir[r].new_keys = 0;
+    }
+    if (tid == 0) {
+        a.dh->status = 0;
+        a.ws.ctr[0] = 0;
+    }
+}
+
+// One thread per source slot (the side slots after them).  `kept` decides
+// what a slot holds: a committed key whose row passes rh_keep.
+__device__ __forceinline__ bool rh_slot(const RehashArgs& a, int64_t s, uint64_t& key, uint64_t& off, int& region) {
+    if (s < a.src_total) {
+        const Slot sl = a.src_slots[s];
+        if (sl.key == EMPTY_KEY || sl.val >= PENDING_BASE) return false;
+        key = sl.key;
+        off = sl.val;
+        region = region_of_slot(a.src_dir, a.n_regions, (uint32_t)s);
+    } else {
+        region = (int)(s - a.src_total);
+        off = a.src_dir[region].side_val;
+        if (off >= PENDING_BASE) return false;
+        key = EMPTY_KEY;
+    }
+    return rh_keep(a, off);
+}
+
+__global__ void k_rh_count(RehashArgs a) {
+    __shared__ uint32_t s_cnt[RSE_MAX_TABLES];
+    for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) s_cnt[r] = 0;
+    __syncthreads();
+    const int64_t n = a.src_total + a.n_regions;
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
+        uint64_t key, off;
+        int region;
+        if (!rh_slot(a, s, key, off, region)) continue;
+        if (off >= (uint64_t)a.bitmap_rows) {           // an offset past the blocks' capacity
+            atomicCAS(&a.dh->status, 0, (int32_t)RSE_ERR_BAD_INPUT);
+            continue;
+        }
+        atomicAdd(&s_cnt[region], 1u);
+        atomicOr(&a.ws.bitmap[off >> 5], 1u << (off & 31));
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x)
+        if (s_cnt[r]) atomicAdd((unsigned long long*)&a.dst_dir[r].new_keys, (unsigned long long)s_cnt[r]);
+}
+
+__global__ void k_rh_decide(RehashArgs a) {
+    __shared__ int s_fail;
+    if (threadIdx.x == 0) s_fail = a.dh->status;
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x)
+        if (a.dst_dir[r].new_keys > a.dst_dir[r].max_keys) atomicCAS(&s_fail, 0, (int)RSE_ERR_IDMAP_FULL);
+    __syncthreads();
+    if (!s_fail)
+        for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) a.dst_dir[r].n_keys = a.dst_dir[r].new_keys;
+    if (threadIdx.x == 0) {
+        if (s_fail) atomicCAS(&a.dh->status, 0, s_fail);
+        a.ws.ctr[0] = s_fail ? 0 : 1;
+    }
+}
+
+// Keys are distinct per region in the source, so an insert only has to find
+// an empty slot along its chain.
+__global__ void k_rh_insert(RehashArgs a) {
+    if (a.ws.ctr[0] != 1) return;
+    const int64_t n = a.src_total + a.n_regions;
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
+        uint64_t key, off;
+        int region;
+        if (!rh_slot(a, s, key, off, region)) continue;
+        if (key == EMPTY_KEY) {
+            a.dst_dir[region].side_val = off;
+            continue;
+        }
+        const TableDir d = a.dst_dir[region];
+        int64_t b = reduce_range(fmix64(key ^ d.salt), d.n_buckets);
+        bool done = false;
+        for (int64_t probes = 0; probes < d.n_buckets && !done; ++probes) {
+            const int64_t base = d.slot_base + b * BUCKET;
+            for (int q = 0; q < BUCKET && !done; ++q) {
+                if (a.dst_slots[base + q].key != EMPTY_KEY) continue;
+                const unsigned long long old = atomicCAS((unsigned long long*)&a.dst_slots[base + q].key,
+                                                         (unsigned long long)EMPTY_KEY, (unsigned long long)key);
+                if (old == EMPTY_KEY) {
+                    a.dst_slots[base + q].val = off;
+                    done = true;
+                }
+            }
+            b = (b + 1 == d.n_buckets) ? 0 : b + 1;
+        }
+        if (!done) atomicCAS(&a.dh->status, 0, (int32_t)RSE_ERR_IDMAP_FULL);
+    }
+}
+
+struct FreeArgs {
+    const uint32_t* bitmap;
+    BlocksHeader* bh;
+    uint32_t* free_list;
+    uint32_t* tile_sum;
+    int64_t n_tiles;
+    const unsigned long long* go;
+};
+
+// Free rows among the 32 of bitmap word w (rows below rows_used only).
+__device__ __forceinline__ uint32_t free_bits(const FreeArgs& a, int64_t w, int64_t rows) {
+    const int64_t r0 = w * 32;
+    if (r0 >= rows) return 0u;
+    const uint32_t valid = rows - r0 >= 32 ? 0xFFFFFFFFu : ((1u << (rows - r0)) - 1u);
+    return ~a.bitmap[w] & valid;
+}
+
+// Block-wide exclusive scan of FL_BLOCK values; returns the total.
+__device__ uint32_t fl_block_scan(uint32_t v, uint32_t* excl) {
+    __shared__ uint32_t wsum[FL_BLOCK / WAVE];
+    const int lane = lane_id();
+    const int w = threadIdx.x / WAVE;
+    uint32_t x = v;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = 0, total = 0;
+    for (int k = 0; k < FL_BLOCK / WAVE; ++k) {
+        if (k < w) pre += wsum[k];
+        total += wsum[k];
+    }
+    __syncthreads();
+    *excl = pre + x - v;
+    return total;
+}
+
+__global__ __launch_bounds__(FL_BLOCK) void k_fl_count(FreeArgs a) {
+    if (*a.go != 1) return;
+    const int64_t rows = a.bh->rows_used;
+    const int64_t w = (int64_t)blockIdx.x * FL_BLOCK + threadIdx.x;
+    uint32_t ex;
+    const uint32_t t = fl_block_scan((uint32_t)__popc(free_bits(a, w, rows)), &ex);
+    if (threadIdx.x == 0) a.tile_sum[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(FL_BLOCK) void k_fl_scan(FreeArgs a) {
+    __shared__ uint32_t s_carry;
+    if (*a.go != 1) return;
+    if (threadIdx.x == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < a.n_tiles; base += FL_BLOCK) {
+        const int64_t k = base + threadIdx.x;
+        const uint32_t v = k < a.n_tiles ? a.tile_sum[k] : 0;
+        uint32_t ex;
+        const uint32_t t = fl_block_scan(v, &ex);
+        const uint32_t carry = s_carry;
+        if (k < a.n_tiles) a.tile_sum[k] = carry + ex;
+        __syncthreads();
+        if (threadIdx.x == 0) s_carry = carry + t;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        a.bh->free_head = 0;
+        a.bh->free_count = s_carry;
+    }
+}
+
+__global__ __launch_bounds__(FL_BLOCK) void k_fl_write(FreeArgs a) {
+    if (*a.go != 1) return;
+    const int64_t rows = a.bh->rows_used;
+    const int64_t w = (int64_t)blockIdx.x * FL_BLOCK + threadIdx.x;
+    uint32_t bits = free_bits(a, w, rows);
+    uint32_t ex;
+    fl_block_scan((uint32_t)__popc(bits), &ex);
+    uint64_t pos = (uint64_t)a.tile_sum[blockIdx.x] + ex;
+    while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        a.free_list[pos++] = (uint32_t)(w * 32 + b);
     }
 }
 
@@ -902,6 +1290,8 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     size_t need = 0;
     Ws ws = carve(d_ws, n_ids, &need);
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
+    // every row a lookup can resolve to must have a stamp
+    if (map->d_stamps && map->n_stamps < blocks->capacity()) return RSE_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
 
     const int64_t n_tiles = (n_ids + SCAN_TILE - 1) / SCAN_TILE;
@@ -916,9 +1306,19 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     pa.stride = stride;
     pa.n_tables = n_tables;
     pa.merged = map->merged;
-    pa.insert = insert_missing ? 1 : 0;
-    pa.pad = 0;
+    // With admission the probe runs twice: first without inserting, listing
+    // the lookups of absent keys; then, after the sketch has counted them,
+    // with inserting, over the admitted ones only.
+    const bool admit = insert_missing && map->admission_on();
+    pa.insert = insert_missing && !admit ? 1 : 0;
+    pa.collect = admit ? 1 : 0;
     pa.row_off = d_row_off_out;
+    pa.list = nullptr;
+    pa.list_n = nullptr;
+    pa.stamps = map->d_stamps;
+    pa.n_stamps = map->n_stamps;
+    pa.clock = map->clock;
+    pa.pad2 = 0;
     pa.ws = ws;
     // 64 lookups per wave per iteration; enough waves to fill 256 CUs
     const int probe_blocks = fill_blocks((n_ids + WAVE - 1) / WAVE, PROBE_BLOCK / 64, 256 * 16);
@@ -928,6 +1328,28 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     }
 
     const int miss_blocks = fill_blocks(n_ids, 256, 2048);
+    AdmitArgs aa;
+    if (admit) {
+        aa.ids = d_ids;
+        aa.bounds = d_bounds;
+        aa.stride = stride;
+        aa.n_tables = n_tables;
+        aa.merged = map->merged;
+        aa.sketch = map->d_sketch;
+        aa.width = map->sk_width;
+        aa.depth = map->sk_depth;
+        aa.threshold = map->admit_min;
+        for (int j = 0; j < 8; ++j) aa.salt[j] = map->sk_salt[j];
+        aa.ws = ws;
+        hipLaunchKernelGGL(k_admit_count, dim3(miss_blocks), dim3(256), 0, s, aa, 0);
+        hipLaunchKernelGGL(k_admit_pick, dim3(miss_blocks), dim3(256), 0, s, aa);
+        ProbeArgs pb = pa;
+        pb.insert = 1;
+        pb.collect = 0;
+        pb.list = ws.admitted;
+        pb.list_n = &ws.ctr[10];
+        hipLaunchKernelGGL(k_probe, dim3(probe_blocks), dim3(PROBE_BLOCK), 0, s, pb);
+    }
     MarkArgs ma;
     ma.slots = pa.slots;
     ma.dir = pa.dir;
@@ -953,6 +1375,7 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     da.n_tiles = n_tiles;
     da.ws = ws;
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(DECIDE_BLOCK), 0, s, da);
+    if (admit) hipLaunchKernelGGL(k_admit_count, dim3(miss_blocks), dim3(256), 0, s, aa, 1);
 
     CommitArgs ca;
     ca.slots = pa.slots;
@@ -965,6 +1388,7 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     ca.n_tables = n_tables;
     ca.pad = 0;
     ca.n = n_ids;
+    ca.free_list = blocks->d_free;
     ca.ws = ws;
     hipLaunchKernelGGL(k_rank_commit, tiles_grid, dim3(256), 0, s, ca);
 
@@ -981,6 +1405,11 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     fa.seed = blocks->seed;
     fa.dim = blocks->dim;
     fa.pad = 0;
+    fa.free_list = blocks->d_free;
+    fa.stamps = map->d_stamps;
+    fa.n_stamps = map->n_stamps;
+    fa.clock = map->clock;
+    fa.pad2 = 0;
     fa.ws = ws;
     const int64_t finish_work = n_ids * (1 + blocks->row_bytes / 16);
     const dim3 finish_grid(fill_blocks(finish_work, 256, 8192));
@@ -1097,6 +1526,119 @@ int rse_idmap_export(rse_idmap* map, int64_t* d_keys_out, int32_t* d_table_out, 
     hipLaunchKernelGGL(k_export, dim3(fill_blocks(map->total_slots, 256, 8192)), dim3(256), 0, s,
                        map->d_slots(), map->d_dir(), map->n_tables, map->total_slots, d_keys_out,
                        d_table_out, d_off_out, capacity, cnt);
+    return launch_status();
+}
+
+// ------------------------------------------- admission, age, eviction --
+int rse_idmap_set_stamps(rse_idmap* map, uint32_t* d_stamps, int64_t n_stamps) {
+    if (!map || n_stamps < 0 || (n_stamps > 0 && !d_stamps)) return RSE_ERR_INVALID_ARG;
+    map->d_stamps = n_stamps > 0 ? d_stamps : nullptr;
+    map->n_stamps = n_stamps > 0 ? n_stamps : 0;
+    return RSE_OK;
+}
+
+int rse_idmap_set_clock(rse_idmap* map, uint32_t clock) {
+    if (!map) return RSE_ERR_INVALID_ARG;
+    map->clock = clock;
+    return RSE_OK;
+}
+
+int rse_idmap_set_admission(rse_idmap* map, uint32_t* d_sketch, int32_t depth, int64_t width, uint32_t threshold,
+                            uint64_t seed, void* stream) {
+    if (!map) return RSE_ERR_INVALID_ARG;
+    if (threshold <= 1) {
+        map->d_sketch = nullptr;
+        map->sk_depth = 0;
+        map->sk_width = 0;
+        map->admit_min = threshold;
+        return RSE_OK;
+    }
+    if (!d_sketch || depth < 1 || depth > 8 || width < 1) return RSE_ERR_INVALID_ARG;
+    map->d_sketch = d_sketch;
+    map->sk_depth = depth;
+    map->sk_width = width;
+    map->admit_min = threshold;
+    // row salts: successive SplitMix64 outputs of the seed
+    uint64_t sm = seed;
+    for (int j = 0; j < 8; ++j) {
+        sm += SM64_GAMMA;
+        uint64_t z = sm;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        map->sk_salt[j] = j < depth ? z ^ (z >> 31) : 0;
+    }
+    const int64_t n = (int64_t)depth * width;
+    hipLaunchKernelGGL(k_fill_u32, dim3(fill_blocks(n, 256, 4096)), dim3(256), 0, as_stream(stream), d_sketch, n,
+                       0u);
+    return launch_status();
+}
+
+int rse_idmap_rehash_workspace_size(const rse_blocks* blocks, size_t* bytes_out) {
+    if (!blocks || !bytes_out) return RSE_ERR_INVALID_ARG;
+    carve_rehash(nullptr, blocks->capacity(), bytes_out);
+    return RSE_OK;
+}
+
+int rse_idmap_rehash(rse_idmap* dst, rse_idmap* src, rse_blocks* blocks, uint32_t min_clock, void* d_ws,
+                     size_t ws_bytes, void* stream) {
+    if (!dst || !src || !blocks || !d_ws || dst == src) return RSE_ERR_INVALID_ARG;
+    if (dst->n_tables != src->n_tables || dst->merged != src->merged) return RSE_ERR_INVALID_ARG;
+    const char* d0 = dst->d_mem;
+    const char* s0 = src->d_mem;
+    if (d0 < s0 + src->mem_bytes() && s0 < d0 + dst->mem_bytes()) return RSE_ERR_INVALID_ARG;
+    const int64_t cap = blocks->capacity();
+    if (src->d_stamps && src->n_stamps < cap) return RSE_ERR_INVALID_ARG;
+    if (blocks->d_free && blocks->free_cap < cap) return RSE_ERR_INVALID_ARG;
+    size_t need = 0;
+    RehashWs ws = carve_rehash(d_ws, cap, &need);
+    if (ws_bytes < need) return RSE_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+
+    RehashArgs a;
+    a.src_slots = src->d_slots();
+    a.src_dir = src->d_dir();
+    a.src_total = src->total_slots;
+    a.n_regions = src->n_tables;
+    a.use_stamps = src->d_stamps ? 1 : 0;
+    a.dst_slots = dst->d_slots();
+    a.dst_dir = dst->d_dir();
+    a.dh = dst->header();
+    a.stamps = src->d_stamps;
+    a.n_stamps = src->n_stamps;
+    a.min_clock = min_clock;
+    a.pad = 0;
+    a.bitmap_rows = cap;
+    a.ws = ws;
+    const int64_t n_words = (cap + 31) / 32;
+    hipLaunchKernelGGL(k_clear_slots, dim3(fill_blocks(dst->total_slots, 256, 8192)), dim3(256), 0, s,
+                       dst->d_slots(), dst->total_slots);
+    hipLaunchKernelGGL(k_rh_reset, dim3(fill_blocks(n_words > src->n_tables ? n_words : src->n_tables, 256, 4096)),
+                       dim3(256), 0, s, a, n_words);
+    const dim3 grid(fill_blocks(src->total_slots + src->n_tables, 256, 8192));
+    hipLaunchKernelGGL(k_rh_count, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rh_decide, dim3(1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rh_insert, grid, dim3(256), 0, s, a);
+    if (blocks->d_free && cap > 0) {
+        FreeArgs f;
+        f.bitmap = ws.bitmap;
+        f.bh = blocks->header();
+        f.free_list = blocks->d_free;
+        f.tile_sum = ws.tile_sum;
+        f.n_tiles = (cap + FL_TILE_ROWS - 1) / FL_TILE_ROWS;
+        f.go = ws.ctr;
+        hipLaunchKernelGGL(k_fl_count, dim3((unsigned)f.n_tiles), dim3(FL_BLOCK), 0, s, f);
+        hipLaunchKernelGGL(k_fl_scan, dim3(1), dim3(FL_BLOCK), 0, s, f);
+        hipLaunchKernelGGL(k_fl_write, dim3((unsigned)f.n_tiles), dim3(FL_BLOCK), 0, s, f);
+    }
+    // the destination takes over the source's policies
+    dst->d_stamps = src->d_stamps;
+    dst->n_stamps = src->n_stamps;
+    dst->clock = src->clock;
+    dst->d_sketch = src->d_sketch;
+    dst->sk_depth = src->sk_depth;
+    dst->sk_width = src->sk_width;
+    dst->admit_min = src->admit_min;
+    for (int j = 0; j < 8; ++j) dst->sk_salt[j] = src->sk_salt[j];
     return launch_status();
 }
 
