@@ -451,12 +451,118 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
         res["overlap_phase_ms"] = phase
     if full_schedules:
         res["interaction"] = bench_interaction(rse, out, steps)
+        res["feature_transform"] = bench_features(rse, T, B, dev, steps)
+    res["rehash"] = bench_rehash(rse, idm, blk, lambda: find(batch_at(cursor[0])), dev)
     # release the workload's device memory before the next one
     del batches, find_ws, ws2, out, idm, blk
     gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def bench_features(rse, T, B, dev, steps):
+    """The fused feature transform at the workload's shape (T tables x B
+    lookups): tables cycle through hash-then-mod of int64 ids, bucketize of
+    float64 values over 1000 boundaries, mod of raw ids and a hashed float,
+    all in one launch; average of `steps` launches timed with events on the
+    stream the kernel runs on.  Algorithmic bytes per launch: 8 B raw value
+    read and 8 B id written per lookup."""
+    import torch
+
+    rng = np.random.default_rng(7)
+    progs, cols = [], []
+    for t in range(T):
+        k = t % 4
+        if k == 0:
+            progs.append((rse.FT_INT64, [(rse.FT_HASH, 1000 + t), (rse.FT_MOD, 1 << 24)]))
+            cols.append(rng.integers(-(2**63), 2**63 - 1, B, dtype=np.int64))
+        elif k == 1:
+            progs.append((rse.FT_FLOAT64, [(rse.FT_BUCKETIZE, np.sort(rng.standard_normal(1000) * 3))]))
+            cols.append((rng.standard_normal(B) * 3).view(np.int64))
+        elif k == 2:
+            progs.append((rse.FT_INT64, [(rse.FT_MOD, 1_000_003)]))
+            cols.append(rng.integers(-(2**62), 2**62, B, dtype=np.int64))
+        else:
+            progs.append((rse.FT_FLOAT64, [(rse.FT_HASH, 5), (rse.FT_MOD, 1 << 20)]))
+            cols.append(rng.standard_normal(B).view(np.int64))
+    ft = rse.FeatureTransform(progs, device=dev)
+    raw = torch.from_numpy(np.concatenate(cols)).to(dev)
+    bounds = torch.arange(0, (T + 1) * B, B, dtype=torch.int64, device=dev)
+    ids = torch.empty_like(raw)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        rse.feature_transform(ft, raw, bounds, out=ids)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        rse.feature_transform(ft, raw, bounds, out=ids)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert ft.status() == 0
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = T * B * 16
+    n_ops = sum(len(ops) for _, ops in progs)
+    return {"lookups": T * B, "tables": T, "operations": n_ops, "launches": 1, "ms": round(ms, 4),
+            "ids_per_s": round(T * B / (ms * 1e-3), 1), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def bench_rehash(rse, idm, blk, find_next, dev):
+    """The map's rehash at the workload's full size, into a second region of
+    the same size: a resize (every key copied) and an eviction (age tracking
+    on, one batch found at clock 1; the rehash with minimum clock 1 keeps that
+    batch's keys, drops the rest and rebuilds the free list).  Each is the
+    average of 3 launches after one warm-up launch, timed with events on the
+    stream the kernels run on.  Algorithmic bytes: source slots read and
+    destination slots cleared (16 B each), kept keys written (16 B), one bit
+    per row of bitmap cleared and read twice, plus for the eviction one
+    4-byte stamp per live key and one 4-byte free-list entry per freed row."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    S = sum(-(-s // 8) * 8 for s in idm.slots_per_table) + idm.n_tables
+    cap = blk.capacity
+    live = sum(idm.status()[1])
+    dst = rse.IdMap(idm.slots_per_table, idm.max_load, idm.merged, idm.hash_seed + 1, dev)
+
+    def run(min_clock, reps=3):
+        idm.rehash_into(dst, blk, min_clock)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            idm.rehash_into(dst, blk, min_clock)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        st, kept = dst.status()
+        assert st == 0, st
+        return e0.elapsed_time(e1) / reps, sum(kept)
+
+    ms_r, kept_r = run(0)
+    assert kept_r == live
+    bytes_r = 16 * (2 * S + live) + 3 * cap // 8
+    idm.track_age(cap)
+    blk.enable_free_list()
+    idm.set_clock(1)
+    find_next()
+    ms_e, kept_e = run(1)
+    head, free = blk.free_list()
+    n_free = int(free.numel())
+    bytes_e = 16 * (2 * S + kept_e) + 4 * live + 3 * cap // 8 + 4 * n_free
+    out = {"slots": S, "live_keys": live, "rows_capacity": cap,
+           "resize_ms": round(ms_r, 4), "resize_gbs": round(bytes_r / (ms_r * 1e-3) / 1e9, 1),
+           "resize_frac_of_peak": round(bytes_r / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "evict_ms": round(ms_e, 4), "evict_kept_keys": kept_e, "evict_freed_rows": n_free,
+           "evict_gbs": round(bytes_e / (ms_e * 1e-3) / 1e9, 1),
+           "evict_frac_of_peak": round(bytes_e / (ms_e * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "resize_algorithmic_bytes": int(bytes_r), "evict_algorithmic_bytes": int(bytes_e)}
+    log(f"  rehash: resize {ms_r:.3f} ms ({out['resize_gbs']} GB/s), evict {ms_e:.3f} ms "
+        f"({out['evict_gbs']} GB/s), kept {kept_e} of {live}, freed {n_free}")
+    del dst
+    return out
 
 
 def bench_interaction(rse, pooled, steps):

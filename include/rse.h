@@ -315,15 +315,15 @@ int rse_idmap_import(rse_idmap* map, const int64_t* d_keys, const int32_t* d_tab
  * evicted rows are not reused.  `src` is not modified; dst takes over
  * src's stamps, clock and admission settings (host side).  Workspace: at
  * least rse_idmap_rehash_workspace_size bytes (a bit per row of the blocks'
- * capacity); stream-ordered, no synchronisation.  A row offset in `src` at
- * or beyond the blocks' capacity fails the call with RSE_ERR_BAD_INPUT in
- * dst's status.
+ * capacity and per slot of src); stream-ordered, no synchronisation.  A
+ * row offset in `src` at or beyond the blocks' capacity fails the call with
+ * RSE_ERR_BAD_INPUT in dst's status.
  */
 int rse_idmap_set_stamps(rse_idmap* map, uint32_t* d_stamps, int64_t n_stamps);
 int rse_idmap_set_clock(rse_idmap* map, uint32_t clock);
 int rse_idmap_set_admission(rse_idmap* map, uint32_t* d_sketch, int32_t depth, int64_t width,
                             uint32_t threshold, uint64_t seed, void* stream);
-int rse_idmap_rehash_workspace_size(const rse_blocks* blocks, size_t* bytes_out);
+int rse_idmap_rehash_workspace_size(const rse_idmap* src, const rse_blocks* blocks, size_t* bytes_out);
 int rse_idmap_rehash(rse_idmap* dst, rse_idmap* src, rse_blocks* blocks, uint32_t min_clock, void* d_ws,
                      size_t ws_bytes, void* stream);
 
@@ -334,6 +334,59 @@ int rse_blocks_set_free_list(rse_blocks* blocks, uint32_t* d_free, int64_t capac
 /* Entries of the free list handed out so far and entries left (those are
  * d_free[head .. head + count)).  Synchronises `stream`. */
 int rse_blocks_free_status(rse_blocks* blocks, int64_t* head_out, int64_t* count_out, void* stream);
+
+/* ------------------------------------------- fused feature transforms -- */
+/*
+ * Raw feature values -> int64 ids for every table in one launch ("RecIS：
+ * 阿里开源推荐系统统一训练框架", "Feature Engine": Hash, Mod and Bucketize,
+ * small operations merged into one GPU kernel launch).  The pages name the
+ * operations only; definitions:
+ *
+ * Lookup i of table t (bounds[t*stride] <= i < bounds[(t+1)*stride], the
+ * ids' table-major layout) holds one 64-bit raw value; table t's program
+ * says whether that is an int64 (RSE_FT_INT64) or the bits of a float64
+ * (RSE_FT_FLOAT64) and applies up to RSE_FT_MAX_OPS operations in order:
+ *   RSE_FT_HASH, arg = seed (bits): XXH64 (xxHash64 of the value's 8
+ *     little-endian bytes with that seed); the digest read as int64;
+ *   RSE_FT_MOD, arg = m > 0: floor modulo of the value as a signed int64,
+ *     a result in [0, m);
+ *   RSE_FT_BUCKETIZE, arg = index of the table's first boundary in the
+ *     boundary array, n_boundaries = their number (ascending, no NaN):
+ *     the number of boundaries <= x for the float64 x (NaN: all of them);
+ *   RSE_FT_IDENTITY: nothing.
+ * An integer program may use Hash and Mod; a float program must start with
+ * Bucketize or Hash; the value after the last operation is the id.
+ *
+ * rse_features_create validates the programs and boundaries on the host
+ * (RSE_ERR_INVALID_ARG if any breaks these rules) and copies them into
+ * caller device memory of rse_features_mem_size bytes (256-byte aligned);
+ * it synchronises `stream`.  feature_transform writes ids[0..n) (it may
+ * write in place over the raw array); malformed bounds (bounds[0] != 0,
+ * bounds[n_tables*stride] != n, a decreasing pair) set the sticky status
+ * RSE_ERR_BAD_INPUT (rse_features_status, synchronising) and write nothing.
+ */
+#define RSE_FT_MAX_OPS 4
+enum { RSE_FT_INT64 = 0, RSE_FT_FLOAT64 = 1 };
+enum { RSE_FT_IDENTITY = 0, RSE_FT_HASH = 1, RSE_FT_MOD = 2, RSE_FT_BUCKETIZE = 3 };
+typedef struct rse_feature_op {
+    int32_t kind;
+    int32_t n_boundaries;   /* RSE_FT_BUCKETIZE */
+    int64_t arg;
+} rse_feature_op;
+typedef struct rse_feature_program {
+    int32_t input;          /* RSE_FT_INT64 | RSE_FT_FLOAT64 */
+    int32_t n_ops;
+    rse_feature_op ops[RSE_FT_MAX_OPS];
+} rse_feature_program;
+typedef struct rse_features rse_features;
+
+int rse_features_mem_size(int32_t n_tables, int64_t n_boundaries, size_t* bytes_out);
+int rse_features_create(rse_features** out, void* d_mem, size_t mem_bytes, const rse_feature_program* programs,
+                        int32_t n_tables, const double* boundaries, int64_t n_boundaries, void* stream);
+int rse_features_destroy(rse_features* features);
+int feature_transform(const rse_features* features, const int64_t* d_raw, int64_t n, const int64_t* d_bounds,
+                      int64_t stride, int64_t* d_ids_out, void* stream);
+int rse_features_status(rse_features* features, int32_t* status_out, void* stream);
 
 /* ------------------------------------------------- pooled forward ----- */
 /*

@@ -278,7 +278,8 @@ class IdMap:
         the blocks' free list if one is attached.  Stream-ordered: read
         dst.status() for the outcome."""
         sz = ctypes.c_size_t()
-        check(lib.rse_idmap_rehash_workspace_size(blocks.handle, ctypes.byref(sz)), "rse_idmap_rehash_workspace_size")
+        check(lib.rse_idmap_rehash_workspace_size(self.handle, blocks.handle, ctypes.byref(sz)),
+              "rse_idmap_rehash_workspace_size")
         ws = _bytes(sz.value, self.device)
         check(lib.rse_idmap_rehash(dst.handle, self.handle, blocks.handle, int(min_clock) & 0xFFFFFFFF, _ptr(ws),
                                    sz.value, _stream(stream)), "rse_idmap_rehash")
@@ -455,6 +456,76 @@ def embedding_bag_bwd_apply(blocks: EmbeddingBlocks, plan, bag_offsets: torch.Te
 
 
 # ------------------------------------------------- DLRM dot interaction --
+# ------------------------------------------------------ feature transforms --
+FT_INT64, FT_FLOAT64 = 0, 1
+FT_IDENTITY, FT_HASH, FT_MOD, FT_BUCKETIZE = 0, 1, 2, 3
+
+
+class FeatureTransform:
+    """Per-table programs of Hash / Mod / Bucketize, applied to every table's
+    raw values in one launch.  `programs`: one (input_kind, ops) per table,
+    ops a list of (FT_HASH, seed) | (FT_MOD, m) | (FT_BUCKETIZE, boundaries)."""
+
+    def __init__(self, programs, device="cuda", stream=None):
+        import numpy as np
+
+        self.device = torch.device(device)
+        n = len(programs)
+        progs = (_lib.RseFeatureProgram * n)()
+        bnd = []
+        for t, (kind, ops) in enumerate(programs):
+            if len(ops) > 4:
+                raise ValueError(f"table {t}: at most 4 operations")
+            progs[t].input = int(kind)
+            progs[t].n_ops = len(ops)
+            for k, (op, arg) in enumerate(ops):
+                progs[t].ops[k].kind = int(op)
+                if op == FT_BUCKETIZE:
+                    b = np.asarray(arg, np.float64).ravel()
+                    progs[t].ops[k].arg = len(bnd)
+                    progs[t].ops[k].n_boundaries = b.size
+                    bnd.extend(b.tolist())
+                elif op == FT_HASH:
+                    seed = int(arg) & (2**64 - 1)
+                    progs[t].ops[k].arg = seed - 2**64 if seed >= 2**63 else seed
+                else:
+                    progs[t].ops[k].arg = int(arg)
+        self.n_tables = n
+        b_arr = (ctypes.c_double * max(len(bnd), 1))(*bnd)
+        sz = ctypes.c_size_t()
+        check(lib.rse_features_mem_size(n, len(bnd), ctypes.byref(sz)), "rse_features_mem_size")
+        self.mem = _bytes(sz.value, self.device)
+        h = ctypes.c_void_p()
+        check(lib.rse_features_create(ctypes.byref(h), _ptr(self.mem), sz.value, progs, n, b_arr, len(bnd),
+                                      _stream(stream)), "rse_features_create")
+        self.handle = h
+        self._finalizer = weakref.finalize(self, lib.rse_features_destroy, h)
+
+    def status(self, stream=None) -> int:
+        st = ctypes.c_int32()
+        check(lib.rse_features_status(self.handle, ctypes.byref(st), _stream(stream)), "rse_features_status")
+        return st.value
+
+
+def feature_transform(ft: FeatureTransform, raw: torch.Tensor, bounds: torch.Tensor, stride: int = 1,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """ids (int64) of every lookup from its raw 64-bit value (int64 tensor;
+    float64 features passed as their bits, e.g. x.view(torch.int64))."""
+    _need(raw, torch.int64, "raw")
+    _need(bounds, torch.int64, "bounds")
+    n = raw.numel()
+    if bounds.numel() < ft.n_tables * stride + 1:
+        raise ValueError("bounds must hold n_tables * stride + 1 entries")
+    if out is None:
+        out = torch.empty_like(raw)
+    _need(out, torch.int64, "out")
+    if out.numel() != n:
+        raise ValueError("out must have one id per raw value")
+    check(lib.feature_transform(ft.handle, _ptr(raw), n, _ptr(bounds), int(stride), _ptr(out), _stream(stream)),
+          "feature_transform")
+    return out
+
+
 def dlrm_interaction_fwd(dense: torch.Tensor, pooled: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     """dense [B, d], pooled [B, T, d] fp32 CUDA -> [B, d + (T+1)T/2]: the dense
     vector, then the dot products of every pair of (dense, table 0..T-1) in

@@ -23,6 +23,14 @@ class RseError(RuntimeError):
         self.code = code
 
 
+class RseFeatureOp(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("n_boundaries", ctypes.c_int32), ("arg", ctypes.c_int64)]
+
+
+class RseFeatureProgram(ctypes.Structure):
+    _fields_ = [("input", ctypes.c_int32), ("n_ops", ctypes.c_int32), ("ops", RseFeatureOp * 4)]
+
+
 class RseBwdPlan(ctypes.Structure):
     _fields_ = [("n_ids", ctypes.c_int64), ("n_bags", ctypes.c_int64), ("invalid", ctypes.c_uint32),
                 ("key_bits", ctypes.c_int32), ("sorted_in_alt", ctypes.c_int32), ("dim", ctypes.c_int32)]
@@ -66,10 +74,16 @@ SIGNATURES = {
     "rse_idmap_set_stamps": ([_P, _P, _I64], ctypes.c_int),
     "rse_idmap_set_clock": ([_P, ctypes.c_uint32], ctypes.c_int),
     "rse_idmap_set_admission": ([_P, _P, _I32, _I64, ctypes.c_uint32, _U64, _P], ctypes.c_int),
-    "rse_idmap_rehash_workspace_size": ([_P, _PSZ], ctypes.c_int),
+    "rse_idmap_rehash_workspace_size": ([_P, _P, _PSZ], ctypes.c_int),
     "rse_idmap_rehash": ([_P, _P, _P, ctypes.c_uint32, _P, _SZ, _P], ctypes.c_int),
     "rse_blocks_set_free_list": ([_P, _P, _I64, _P], ctypes.c_int),
     "rse_blocks_free_status": ([_P, _PI64, _PI64, _P], ctypes.c_int),
+    "rse_features_mem_size": ([_I32, _I64, _PSZ], ctypes.c_int),
+    "rse_features_create": ([ctypes.POINTER(_P), _P, _SZ, ctypes.POINTER(RseFeatureProgram), _I32, _P, _I64, _P],
+                            ctypes.c_int),
+    "rse_features_destroy": ([_P], ctypes.c_int),
+    "feature_transform": ([_P, _P, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "rse_features_status": ([_P, _PI32, _P], ctypes.c_int),
     "rse_idmap_status": ([_P, _PI32, _PI64, _P], ctypes.c_int),
     "rse_idmap_clear_status": ([_P, _P], ctypes.c_int),
     "rse_idmap_export": ([_P, _P, _P, _P, _I64, _P, _P], ctypes.c_int),

@@ -22,6 +22,7 @@
 // keys one by one in lookup order, and independent of thread timing.  Only
 // integer atomics are used.  Kernels after the probe exit at once when the
 // batch has no miss.
+#include <algorithm>
 #include <mutex>
 #include <new>
 
@@ -955,9 +956,10 @@ struct RehashWs {
     unsigned long long* ctr;   // [0] go flag
     uint32_t* bitmap;          // one bit per row: referenced by a kept key
     uint32_t* tile_sum;        // free rows per tile of FL_TILE_ROWS rows, then their scan
+    uint32_t* keep;            // one bit per source slot (then side slot): kept
 };
 
-RehashWs carve_rehash(void* base, int64_t rows, size_t* total) {
+RehashWs carve_rehash(void* base, int64_t rows, int64_t src_slots, size_t* total) {
     Carver c(base);
     RehashWs w;
     const int64_t words = (rows + 31) / 32;
@@ -965,6 +967,7 @@ RehashWs carve_rehash(void* base, int64_t rows, size_t* total) {
     w.ctr = c.take<unsigned long long>(16);
     w.bitmap = c.take<uint32_t>((size_t)(words > 0 ? words : 1));
     w.tile_sum = c.take<uint32_t>((size_t)tiles + 1);
+    w.keep = c.take<uint32_t>((size_t)(src_slots + 31) / 32 + 1);
     if (total) *total = c.size();
     return w;
 }
@@ -990,9 +993,26 @@ __device__ __forceinline__ bool rh_keep(const RehashArgs& a, uint64_t off) {
     return !a.use_stamps || off >= (uint64_t)a.n_stamps || a.stamps[off] >= a.min_clock;
 }
 
-__global__ void k_rh_reset(RehashArgs a, int64_t n_words) {
+// Region bases in LDS, for region_of_slot without global loads.
+__device__ __forceinline__ void stage_region_bases(uint64_t* s_base, const TableDir* dir, int n_regions) {
+    for (int r = threadIdx.x; r < n_regions; r += blockDim.x) s_base[r] = (uint64_t)dir[r].slot_base;
+    __syncthreads();
+}
+
+__device__ __forceinline__ int region_of_slot_lds(const uint64_t* s_base, int n_regions, uint64_t s) {
+    int lo = 0, hi = n_regions;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_base[mid] <= s) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__global__ void k_rh_reset(RehashArgs a, int64_t n_words, int64_t n_keep_words) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (int64_t w = tid; w < n_words; w += (int64_t)gridDim.x * blockDim.x) a.ws.bitmap[w] = 0;
+    for (int64_t w = tid; w < n_keep_words; w += (int64_t)gridDim.x * blockDim.x) a.ws.keep[w] = 0;
     for (int64_t r = tid; r < a.n_regions; r += (int64_t)gridDim.x * blockDim.x) {
         a.dst_dir[r].n_keys = 0;
         a.dst_dir[r].side_val = EMPTY_VAL;
@@ -1004,39 +1024,45 @@ __global__ void k_rh_reset(RehashArgs a, int64_t n_words) {
     }
 }
 
-// One thread per source slot (the side slots after them).  `kept` decides
-// what a slot holds: a committed key whose row passes rh_keep.
-__device__ __forceinline__ bool rh_slot(const RehashArgs& a, int64_t s, uint64_t& key, uint64_t& off, int& region) {
+// One thread per source slot (the side slots after them): a committed
+// key, its offset and region, or false for an empty slot.
+__device__ __forceinline__ bool rh_slot(const RehashArgs& a, const uint64_t* s_base, int64_t s, uint64_t& key,
+                                        uint64_t& off, int& region) {
     if (s < a.src_total) {
         const Slot sl = a.src_slots[s];
         if (sl.key == EMPTY_KEY || sl.val >= PENDING_BASE) return false;
         key = sl.key;
         off = sl.val;
-        region = region_of_slot(a.src_dir, a.n_regions, (uint32_t)s);
+        region = region_of_slot_lds(s_base, a.n_regions, (uint64_t)s);
     } else {
         region = (int)(s - a.src_total);
         off = a.src_dir[region].side_val;
         if (off >= PENDING_BASE) return false;
         key = EMPTY_KEY;
     }
-    return rh_keep(a, off);
+    return true;
 }
 
+// Decides which keys stay (their stamps are read here only: the decision is
+// kept as one bit per source slot), counts them per region and marks their
+// rows.
 __global__ void k_rh_count(RehashArgs a) {
     __shared__ uint32_t s_cnt[RSE_MAX_TABLES];
+    __shared__ uint64_t s_base[RSE_MAX_TABLES];
     for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) s_cnt[r] = 0;
-    __syncthreads();
+    stage_region_bases(s_base, a.src_dir, a.n_regions);
     const int64_t n = a.src_total + a.n_regions;
     for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
         uint64_t key, off;
         int region;
-        if (!rh_slot(a, s, key, off, region)) continue;
+        if (!rh_slot(a, s_base, s, key, off, region) || !rh_keep(a, off)) continue;
         if (off >= (uint64_t)a.bitmap_rows) {           // an offset past the blocks' capacity
             atomicCAS(&a.dh->status, 0, (int32_t)RSE_ERR_BAD_INPUT);
             continue;
         }
         atomicAdd(&s_cnt[region], 1u);
         atomicOr(&a.ws.bitmap[off >> 5], 1u << (off & 31));
+        if (a.use_stamps) atomicOr(&a.ws.keep[s >> 5], 1u << (s & 31));
     }
     __syncthreads();
     for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x)
@@ -1061,12 +1087,15 @@ __global__ void k_rh_decide(RehashArgs a) {
 // Keys are distinct per region in the source, so an insert only has to find
 // an empty slot along its chain.
 __global__ void k_rh_insert(RehashArgs a) {
+    __shared__ uint64_t s_base[RSE_MAX_TABLES];
     if (a.ws.ctr[0] != 1) return;
+    stage_region_bases(s_base, a.src_dir, a.n_regions);
     const int64_t n = a.src_total + a.n_regions;
     for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (int64_t)gridDim.x * blockDim.x) {
+        if (a.use_stamps && !((a.ws.keep[s >> 5] >> (s & 31)) & 1u)) continue;
         uint64_t key, off;
         int region;
-        if (!rh_slot(a, s, key, off, region)) continue;
+        if (!rh_slot(a, s_base, s, key, off, region)) continue;
         if (key == EMPTY_KEY) {
             a.dst_dir[region].side_val = off;
             continue;
@@ -1573,9 +1602,9 @@ int rse_idmap_set_admission(rse_idmap* map, uint32_t* d_sketch, int32_t depth, i
     return launch_status();
 }
 
-int rse_idmap_rehash_workspace_size(const rse_blocks* blocks, size_t* bytes_out) {
-    if (!blocks || !bytes_out) return RSE_ERR_INVALID_ARG;
-    carve_rehash(nullptr, blocks->capacity(), bytes_out);
+int rse_idmap_rehash_workspace_size(const rse_idmap* src, const rse_blocks* blocks, size_t* bytes_out) {
+    if (!src || !blocks || !bytes_out) return RSE_ERR_INVALID_ARG;
+    carve_rehash(nullptr, blocks->capacity(), src->total_slots + src->n_tables, bytes_out);
     return RSE_OK;
 }
 
@@ -1590,7 +1619,8 @@ int rse_idmap_rehash(rse_idmap* dst, rse_idmap* src, rse_blocks* blocks, uint32_
     if (src->d_stamps && src->n_stamps < cap) return RSE_ERR_INVALID_ARG;
     if (blocks->d_free && blocks->free_cap < cap) return RSE_ERR_INVALID_ARG;
     size_t need = 0;
-    RehashWs ws = carve_rehash(d_ws, cap, &need);
+    const int64_t n_src = src->total_slots + src->n_tables;
+    RehashWs ws = carve_rehash(d_ws, cap, n_src, &need);
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
 
@@ -1612,8 +1642,10 @@ int rse_idmap_rehash(rse_idmap* dst, rse_idmap* src, rse_blocks* blocks, uint32_
     const int64_t n_words = (cap + 31) / 32;
     hipLaunchKernelGGL(k_clear_slots, dim3(fill_blocks(dst->total_slots, 256, 8192)), dim3(256), 0, s,
                        dst->d_slots(), dst->total_slots);
-    hipLaunchKernelGGL(k_rh_reset, dim3(fill_blocks(n_words > src->n_tables ? n_words : src->n_tables, 256, 4096)),
-                       dim3(256), 0, s, a, n_words);
+    const int64_t n_keep_words = src->d_stamps ? (n_src + 31) / 32 : 0;
+    const int64_t reset_items = std::max<int64_t>(std::max<int64_t>(n_words, n_keep_words), src->n_tables);
+    hipLaunchKernelGGL(k_rh_reset, dim3(fill_blocks(reset_items, 256, 4096)), dim3(256), 0, s, a, n_words,
+                       n_keep_words);
     const dim3 grid(fill_blocks(src->total_slots + src->n_tables, 256, 8192));
     hipLaunchKernelGGL(k_rh_count, grid, dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_rh_decide, dim3(1), dim3(256), 0, s, a);

@@ -128,3 +128,32 @@ def test_binding_rejects_short_buffers_before_any_call():
     with pytest.raises(ValueError, match="stride"):
         rse.idmap_find_or_insert(None, None, ids, bounds, 0, 2, torch.zeros(10, dtype=torch.int64), n_new)
 
+
+
+def test_feature_programs_validated_on_the_host(lib):
+    """rse_features_create rejects programs that break the transform rules
+    before it touches device memory (the address passed is never used)."""
+    from recommender_sparse_embedding_amd._lib import RseFeatureProgram
+
+    def create(specs, bnd=()):
+        progs = (RseFeatureProgram * len(specs))()
+        for t, (inp, ops) in enumerate(specs):
+            progs[t].input, progs[t].n_ops = inp, len(ops)
+            for k, (kind, arg, nb) in enumerate(ops):
+                progs[t].ops[k].kind, progs[t].ops[k].arg, progs[t].ops[k].n_boundaries = kind, arg, nb
+        b = (ctypes.c_double * max(1, len(bnd)))(*bnd)
+        h = ctypes.c_void_p()
+        return lib.rse_features_create(ctypes.byref(h), ctypes.c_void_p(1 << 20), 1 << 30, progs, len(specs), b,
+                                       len(bnd), None)
+
+    INV = -1
+    F64, I64, HASH, MOD, BUCK = 1, 0, 1, 2, 3
+    assert create([(F64, [])]) == INV                                  # ends as a float
+    assert create([(F64, [(MOD, 3, 0)])]) == INV                       # mod of a float
+    assert create([(I64, [(BUCK, 0, 2)])], (0.0, 1.0)) == INV           # bucketize of an int
+    assert create([(F64, [(BUCK, 0, 2)])], (1.0, 0.0)) == INV           # descending boundaries
+    assert create([(F64, [(BUCK, 1, 2)])], (0.0, 1.0)) == INV           # past the boundary array
+    assert create([(F64, [(BUCK, 0, 2)])], (0.0, float("nan"))) == INV  # NaN boundary
+    assert create([(I64, [(MOD, 0, 0)])]) == INV                       # modulus 0
+    assert create([(I64, [(7, 0, 0)])]) == INV                         # unknown operation
+    assert create([(2, [])]) == INV                                    # unknown input kind
