@@ -513,11 +513,15 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan,
  *     d_ddense [batch, dim] = dout[b, 0:dim] + dx_0,
  *     d_dpooled [batch, n_tables, dim] = dx_{t+1}  (the upstream gradient
  *     embedding_bag_bwd_update takes).
- * Dot products and gradient sums are accumulated in fp64 (products of fp32
- * values are exact) and rounded once to fp32.  All pointers are device
- * pointers; the inputs are not modified.  RSE_ERR_UNSUPPORTED if one sample's
- * vectors and pair matrix, (n_tables + 1) * (dim + 1 + n_tables + 1) floats,
- * exceed 64 KiB.
+ * Precision: with n_tables + 1 <= 32 and dim in {32, 64, 128, 256} the
+ * matrix cores compute the dot products in fp32 over blocks of at most 64
+ * elements, the blocks added in fp64 (|error| <= 65 * 2^-24 * sum_k
+ * |x_ik x_jk|), and the gradients in fp32 (|error| <= 33 * 2^-24 *
+ * sum_j |g_ij x_jk|, plus one rounding for the dense gradient); other
+ * shapes accumulate in fp64 (products of fp32 values are exact) and round
+ * once.  All pointers are device pointers; the inputs are not modified.
+ * RSE_ERR_UNSUPPORTED if one sample's vectors and pair matrix,
+ * (n_tables + 1) * (dim + 1 + n_tables + 1) floats, exceed 64 KiB.
  */
 int dlrm_interaction_fwd(const float* d_dense, const float* d_pooled, int64_t batch, int32_t n_tables,
                          int32_t dim, float* d_out, void* stream);

@@ -11,8 +11,9 @@
 //   backward: with g_ij = dout[b, d + p(i,j)] (and g_ji = g_ij),
 //             dx_i = sum_{j != i} g_ij x_j;  ddense = dout[b, 0:d] + dx_0;
 //             dpooled[b, t, :] = dx_{t+1}
-// Products of fp32 values are exact in fp64 and are accumulated in fp64,
-// rounded once to fp32.
+// Shapes with F <= 32 and d in {32, 64, 128, 256} run on the matrix cores
+// (below); the others on the vector kernels here, whose products of fp32
+// values are exact in fp64 and are accumulated in fp64, rounded once.
 //
 // Both kernels stage a sample's vectors in LDS (fp32, row stride d + 1 so
 // that a column of rows falls in different banks) and work on 4 x 4 register
@@ -21,8 +22,7 @@
 // (interleaved: lane s takes elements s, s + KS, ...) when a sample has few
 // tiles, the KS partial sums added by shuffles; the backward on tiles of
 // (4 vectors x 4 elements K, K + d/4, ...), the symmetric pair matrix G
-// staged in LDS beside X.  Arithmetic intensity is ~6 flop/B (fp64
-// vector ALU ridge ~10 flop/B), so neither uses the matrix cores.
+// staged in LDS beside X.
 #include "rse_host.h"
 
 using namespace rse;
@@ -201,6 +201,169 @@ __global__ __launch_bounds__(IB) void k_dot_bwd(const float* dense, const float*
     }
 }
 
+// ------------------------------------------------ matrix-core path ------
+// For F <= 32 vectors per sample and d a multiple of 32 the interaction is
+// a batch of small dense contractions: the forward's Gram matrix X X^T
+// (F x d by d x F) and the backward's G X (F x F by F x d).  One wave takes
+// one sample at a time: its F vectors are staged in LDS (row stride d + 4,
+// 16-byte aligned), then v_mfma_f32_32x32x2_f32 accumulates 32 x 32 tiles
+// in fp32 (rows and columns past F read as zero).
+//
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l % 32][l / 32] and
+// B[l / 32][l % 32]; accumulator register r of lane l holds
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  In the forward both operands
+// are X (B = X^T holds the same values lane for lane); the two k positions of
+// an instruction are taken from the two halves of the block's k range, so
+// each lane reads 4 consecutive floats of its row per 4 instructions.
+// Precision: fp32 products and sums over blocks of at most 64 elements,
+// the blocks added in fp64: |error| <= 65 * 2^-24 * sum_k |x_ik x_jk| for a
+// dot product (backward: <= 33 * 2^-24 * sum_j |g_ij| |x_jk|, plus one
+// rounding of the dense gradient's sum).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int MF_MAX_F = 32;
+
+__device__ __forceinline__ int mf_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Stages sample b's F vectors into this wave's x (row stride d + 4).
+template <int D>
+__device__ __forceinline__ void mf_stage(float* x, const float* dense, const float* pooled, int64_t b, int T,
+                                         int lane) {
+    constexpr int Q = D / 4, ST = D + 4;
+    const int F = T + 1;
+    const f32x4* drow = reinterpret_cast<const f32x4*>(dense + b * D);
+    const f32x4* prow = reinterpret_cast<const f32x4*>(pooled + b * (int64_t)T * D);
+    for (int q0 = 0; q0 < F * Q; q0 += 4 * WAVE) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * WAVE + lane;
+            const int r = q / Q, c = q % Q;
+            v[u] = q < F * Q ? (r == 0 ? drow[c] : prow[(int64_t)(r - 1) * Q + c]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * WAVE + lane;
+            if (q < F * Q) *reinterpret_cast<f32x4*>(x + (q / Q) * ST + (q % Q) * 4) = v[u];
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_dot_fwd_mfma(const float* dense, const float* pooled, int64_t B, int T,
+                                                      float* out) {
+    extern __shared__ float smem[];
+    constexpr int ST = D + 4, KB = D < 64 ? D : 64, KH = KB / 2;
+    const int F = T + 1;
+    const int64_t P = (int64_t)F * T / 2, ROW = D + P;
+    const int lane = lane_id(), w = threadIdx.x / WAVE, W = blockDim.x / WAVE;
+    float* x = smem + w * F * ST;
+    const int row = lane & 31, half = lane >> 5;
+    for (int64_t base = (int64_t)blockIdx.x * W; base < B; base += (int64_t)gridDim.x * W) {
+        const int64_t b = base + w;
+        const bool live = b < B;
+        if (live) mf_stage<D>(x, dense, pooled, b, T, lane);
+        __syncthreads();
+        if (live) {
+            double acc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0;
+            const float* xr = x + (row < F ? row : 0) * ST + half * KH;
+            for (int kb = 0; kb < D; kb += KB) {
+                f32x16 c = {};
+#pragma unroll
+                for (int s = 0; s < KH; s += 4) {
+                    f32x4 v = *reinterpret_cast<const f32x4*>(xr + kb + s);
+                    if (row >= F) v = f32x4{0.f, 0.f, 0.f, 0.f};
+                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.x, v.x, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.y, v.y, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.z, v.z, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.w, v.w, c, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] += (double)c[r];
+            }
+            float* o = out + b * ROW;
+            for (int c = lane; c < D; c += WAVE) o[c] = x[c];
+            const int j = row;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = mf_row(r, lane);
+                if (i < j && j < F) o[D + pair_index(i, j, F)] = (float)acc[r];
+            }
+        }
+        __syncthreads();                        // x is restaged for the next sample
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_dot_bwd_mfma(const float* dense, const float* pooled, const float* dout,
+                                                      int64_t B, int T, float* ddense, float* dpooled) {
+    extern __shared__ float smem[];
+    constexpr int ST = D + 4, GS = MF_MAX_F + 1;
+    const int F = T + 1;
+    const int64_t P = (int64_t)F * T / 2, ROW = D + P;
+    const int lane = lane_id(), w = threadIdx.x / WAVE, W = blockDim.x / WAVE;
+    float* x = smem + w * (F * ST + MF_MAX_F * GS);
+    float* g = x + F * ST;                      // symmetric pair gradient, 32 x 33, zero outside F x F
+    const int row = lane & 31, half = lane >> 5;
+    for (int64_t base = (int64_t)blockIdx.x * W; base < B; base += (int64_t)gridDim.x * W) {
+        const int64_t b = base + w;
+        const bool live = b < B;
+        if (live) {
+            mf_stage<D>(x, dense, pooled, b, T, lane);
+            for (int e = lane; e < MF_MAX_F * GS; e += WAVE) g[e] = 0.f;
+        }
+        __syncthreads();
+        if (live) {
+            const float* go = dout + b * ROW + D;
+            for (int e = lane; e < F * F; e += WAVE) {
+                const int i = e / F, j = e % F;
+                if (i < j) {
+                    const float v = go[pair_index(i, j, F)];
+                    g[i * GS + j] = v;
+                    g[j * GS + i] = v;
+                }
+            }
+        }
+        __syncthreads();
+        if (live) {
+            const int ksteps = (F + 1) / 2;
+            for (int cb = 0; cb < D; cb += 32) {
+                f32x16 c = {};
+                for (int s = 0; s < ksteps; ++s) {
+                    const int k = 2 * s + half;
+                    const float a = g[row * GS + k];
+                    const float bv = k < F ? x[k * ST + cb + row] : 0.f;
+                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, c, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = mf_row(r, lane);
+                    const int col = cb + row;
+                    if (i >= F) continue;
+                    if (i == 0)
+                        ddense[b * D + col] = (float)((double)c[r] + (double)dout[b * ROW + col]);
+                    else
+                        dpooled[(b * T + (i - 1)) * (int64_t)D + col] = c[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Waves per block of the matrix-core kernels: as many samples as fit 64 KiB
+// of LDS, at most 4.
+int mf_waves(size_t per_wave) {
+    const size_t w = (64 * 1024) / per_wave;
+    return (int)(w < 1 ? 1 : (w > 4 ? 4 : w));
+}
+
+bool mf_ok(int32_t n_tables, int32_t dim) {
+    return n_tables + 1 <= MF_MAX_F && (dim == 32 || dim == 64 || dim == 128 || dim == 256);
+}
+
 int check_shape(int64_t batch, int32_t n_tables, int32_t dim, size_t* lds_fwd, size_t* lds_bwd) {
     if (batch < 0 || n_tables < 1 || dim < 1 || dim > 4096) return RSE_ERR_INVALID_ARG;
     const int64_t F = (int64_t)n_tables + 1;
@@ -224,6 +387,21 @@ int dlrm_interaction_fwd(const float* d_dense, const float* d_pooled, int64_t ba
     if (batch == 0) return RSE_OK;
     if (!d_dense || !d_pooled || !d_out) return RSE_ERR_INVALID_ARG;
     const int F = n_tables + 1, nb = (F + 3) / 4, n_tiles = nb * (nb + 1) / 2;
+    if (mf_ok(n_tables, dim)) {
+        const size_t per_wave = (size_t)F * (dim + 4) * sizeof(float);
+        const int W = mf_waves(per_wave);
+        const dim3 grid(fill_blocks(batch, W, 256 * 8)), block(W * WAVE);
+        const size_t lds = per_wave * W;
+        hipStream_t st = as_stream(stream);
+        TraceScope ts(RSE_K_INTERACT, st);
+        switch (dim) {
+            case 32: hipLaunchKernelGGL(k_dot_fwd_mfma<32>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
+            case 64: hipLaunchKernelGGL(k_dot_fwd_mfma<64>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
+            case 128: hipLaunchKernelGGL(k_dot_fwd_mfma<128>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
+            default: hipLaunchKernelGGL(k_dot_fwd_mfma<256>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
+        }
+        return launch_status();
+    }
     // split d over ks adjacent lanes while the block has idle threads
     int ks = 1;
     while (ks < 64 && n_tiles * ks * 2 <= IB && dim / (ks * 2) >= 4) ks *= 2;
@@ -240,6 +418,21 @@ int dlrm_interaction_bwd(const float* d_dense, const float* d_pooled, const floa
     if (rc) return rc;
     if (batch == 0) return RSE_OK;
     if (!d_dense || !d_pooled || !d_dout || !d_ddense || !d_dpooled) return RSE_ERR_INVALID_ARG;
+    if (mf_ok(n_tables, dim)) {
+        const int F = n_tables + 1;
+        const size_t per_wave = ((size_t)F * (dim + 4) + (size_t)MF_MAX_F * (MF_MAX_F + 1)) * sizeof(float);
+        const int W = mf_waves(per_wave);
+        const dim3 grid(fill_blocks(batch, W, 256 * 8)), block(W * WAVE);
+        const size_t lds = per_wave * W;
+        hipStream_t st = as_stream(stream);
+        switch (dim) {
+            case 32: hipLaunchKernelGGL(k_dot_bwd_mfma<32>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
+            case 64: hipLaunchKernelGGL(k_dot_bwd_mfma<64>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
+            case 128: hipLaunchKernelGGL(k_dot_bwd_mfma<128>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
+            default: hipLaunchKernelGGL(k_dot_bwd_mfma<256>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
+        }
+        return launch_status();
+    }
     hipLaunchKernelGGL(k_dot_bwd, dim3(grid_for(batch)), dim3(IB), lb, as_stream(stream), d_dense, d_pooled, d_dout,
                        batch, (int)n_tables, (int)dim, d_ddense, d_dpooled);
     return launch_status();

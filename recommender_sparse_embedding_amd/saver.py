@@ -14,9 +14,12 @@ row:
 and, as string metadata, what recreates the objects: the blocks' dim, weight
 type, optimizer, chunk size, chunk-table size and init seed, the map's slot
 counts per table, max load, merged flag and hash seed, the row counter, the
-optimizer step and a format tag.  Every step runs in the library (map
-export / import, row read / write); this module only moves tensors between
-the device and the file.
+optimizer step and a format tag.  Rows below the row counter that no key
+references (rows freed by an eviction and not yet reused) are not written:
+the free list they form is, at any time, exactly those rows in ascending
+order, so load(free_list=True) rebuilds it with a rehash.  Every step runs
+in the library (map export / import, row read / write, rehash); this module
+only moves tensors between the device and the file.
 """
 
 from __future__ import annotations
@@ -41,7 +44,7 @@ def save(path: str, idmap, blocks, step: int = 0, extra: dict | None = None, str
         raise RseError("save: objects carry a sticky error status", st or map_st)
     total = int(sum(n_keys))
     keys, tabs, offs, cnt = idmap.export(total, stream)
-    if cnt != total or cnt != rows_used:
+    if cnt != total or cnt > rows_used:
         raise ValueError(f"save: {cnt} map entries, {total} counted keys, {rows_used} rows in use")
     order = torch.argsort(offs)
     keys, tabs, offs = keys[order].contiguous(), tabs[order].contiguous(), offs[order].contiguous()
@@ -61,10 +64,13 @@ def save(path: str, idmap, blocks, step: int = 0, extra: dict | None = None, str
     return meta
 
 
-def load(path: str, device="cuda", extra_rows: int = 0, stream=None):
+def load(path: str, device="cuda", extra_rows: int = 0, free_list: bool = False, stream=None):
     """Recreate (idmap, blocks) from a file written by save(), with room for
-    `extra_rows` more rows.  Returns (idmap, blocks, metadata); metadata
-    ["step"] is the optimizer step to continue from."""
+    `extra_rows` more rows.  free_list=True attaches a free list to the
+    blocks and rebuilds it (the rows below the row counter that no key
+    references, ascending), as the saved run's free list held them.
+    Returns (idmap, blocks, metadata); metadata["step"] is the optimizer
+    step to continue from."""
     from . import EmbeddingBlocks, IdMap, RseError
 
     with safe_open(path, framework="pt") as f:
@@ -89,4 +95,7 @@ def load(path: str, device="cuda", extra_rows: int = 0, stream=None):
     _, st = blk.status(stream)
     if map_st != 0 or st != 0:
         raise RseError("load: restoring the state failed", map_st or st)
+    if free_list:
+        blk.enable_free_list(stream=stream)
+        idm.evict(blk, 0, stream)          # nothing evicted: rebuilds the free list
     return idm, blk, meta

@@ -245,3 +245,41 @@ def test_side_key_eviction_and_admission_undo():
     big = [100 + i for i in range(14) for _ in range(2)]
     call(big, 5, expect_ok=False)
     assert torch.equal(m.sketch, sk_before)
+
+
+def test_save_after_eviction_and_load_with_free_list(tmp_path):
+    """The Saver writes only referenced rows; loading with free_list=True
+    rebuilds the pending free list (the unreferenced rows below the row
+    counter, ascending), and both runs continue with the same offsets and
+    bit-identical rows."""
+    import recommender_sparse_embedding_amd as rse
+
+    cfg = synth.config(1, batch=512)
+    orc, gpu, n_ev, _ = run_stream(cfg, steps=4, admit=None, evict_every=2, window=1)
+    assert n_ev > 0
+    path = str(tmp_path / "evicted.safetensors")
+    rse.save(path, gpu.map, gpu.blocks, step=gpu.step)
+    idm2, blk2, meta = rse.load(path, device="cuda", free_list=True)
+    _, left_a = gpu.blocks.free_list()
+    _, left_b = blk2.free_list()
+    assert torch.equal(left_a, left_b) and left_b.numel() == orc.free_list()[0].size > 0
+    ka = _entries(gpu.map, 1 << 20)
+    kb = _entries(idm2, 1 << 20)
+    assert all(np.array_equal(x, y) for x, y in zip(ka[:3], kb[:3]))
+    wl = synth.Workload(cfg)
+    ids, bo = wl.batch_inputs(10)
+    ro_a, nn_a = gpu.find_or_insert(ids, bo, cfg.batch)
+    t_ids, t_bo = torch.from_numpy(ids).cuda(), torch.from_numpy(bo).cuda()
+    ro_b = torch.empty_like(t_ids)
+    n_new = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rse.idmap_find_or_insert(idm2, blk2, t_ids, t_bo, cfg.batch, cfg.n_tables, ro_b, n_new)
+    assert torch.equal(ro_a, ro_b) and nn_a == int(n_new.item())
+    g = torch.from_numpy(wl.grad(10)).cuda()
+    gpu.bwd(ro_a, bo, g)
+    n_u = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rse.embedding_bag_bwd_update(blk2, ro_b, t_bo, cfg.n_tables, cfg.batch, cfg.pooling, g, gpu.optim,
+                                 meta["step"] + 1, n_u)
+    offs = torch.unique(ro_a[ro_a >= 0])
+    wa, sa = gpu.blocks.read_rows(offs)
+    wb, sb = blk2.read_rows(offs)
+    assert torch.equal(wa.view(torch.int32), wb.view(torch.int32))
