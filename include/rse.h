@@ -513,7 +513,7 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan,
  *     d_ddense [batch, dim] = dout[b, 0:dim] + dx_0,
  *     d_dpooled [batch, n_tables, dim] = dx_{t+1}  (the upstream gradient
  *     embedding_bag_bwd_update takes).
- * Precision: with n_tables + 1 <= 32 and dim in {32, 64, 128, 256} the
+ * Precision: with n_tables + 1 <= 32 and dim in {32, 64, 128} the
  * matrix cores compute the dot products in fp32 over blocks of at most 64
  * elements, the blocks added in fp64 (|error| <= 65 * 2^-24 * sum_k
  * |x_ik x_jk|), and the gradients in fp32 (|error| <= 33 * 2^-24 *

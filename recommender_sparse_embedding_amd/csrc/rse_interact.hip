@@ -11,7 +11,7 @@
 //   backward: with g_ij = dout[b, d + p(i,j)] (and g_ji = g_ij),
 //             dx_i = sum_{j != i} g_ij x_j;  ddense = dout[b, 0:d] + dx_0;
 //             dpooled[b, t, :] = dx_{t+1}
-// Shapes with F <= 32 and d in {32, 64, 128, 256} run on the matrix cores
+// Shapes with F <= 32 and d in {32, 64, 128} run on the matrix cores
 // (below); the others on the vector kernels here, whose products of fp32
 // values are exact in fp64 and are accumulated in fp64, rounded once.
 //
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(IB) void k_dot_bwd(const float* dense, const float*
 }
 
 // ------------------------------------------------ matrix-core path ------
-// For F <= 32 vectors per sample and d a multiple of 32 the interaction is
+// For F <= 32 vectors per sample and d in {32, 64, 128} the interaction is
 // a batch of small dense contractions: the forward's Gram matrix X X^T
 // (F x d by d x F) and the backward's G X (F x F by F x d).  One wave takes
 // one sample at a time: its F vectors are staged in LDS (row stride d + 4,
@@ -221,135 +221,181 @@ __global__ __launch_bounds__(IB) void k_dot_bwd(const float* dense, const float*
 // rounding of the dense gradient's sum).
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+
 constexpr int MF_MAX_F = 32;
 
 __device__ __forceinline__ int mf_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Stages sample b's F vectors into this wave's x (row stride d + 4).
+// Wave-level ordering of a wave's own LDS writes before its other lanes
+// read them (each wave works in its own part of LDS).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Sample b's F vectors as NPF 16-byte pieces per lane (piece q = u * 64 +
+// lane: row q / (D/4), four floats at column 4 (q % (D/4))); rows past F
+// are not loaded.  The loads are issued for the next sample while the
+// current one is computed, then written to LDS (row stride D + 4).
 template <int D>
-__device__ __forceinline__ void mf_stage(float* x, const float* dense, const float* pooled, int64_t b, int T,
-                                         int lane) {
-    constexpr int Q = D / 4, ST = D + 4;
-    const int F = T + 1;
-    const f32x4* drow = reinterpret_cast<const f32x4*>(dense + b * D);
-    const f32x4* prow = reinterpret_cast<const f32x4*>(pooled + b * (int64_t)T * D);
-    for (int q0 = 0; q0 < F * Q; q0 += 4 * WAVE) {
-        f32x4 v[4];
+struct MfVectors {
+    static constexpr int Q = D / 4, ST = D + 4, NPF = (MF_MAX_F * Q + WAVE - 1) / WAVE;
+    f32x4 v[NPF];
+    __device__ __forceinline__ void load(const float* dense, const float* pooled, int64_t b, int T, int lane) {
+        const int F = T + 1;
+        const f32x4* drow = reinterpret_cast<const f32x4*>(dense + b * D);
+        const f32x4* prow = reinterpret_cast<const f32x4*>(pooled + b * (int64_t)T * D);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = q0 + u * WAVE + lane;
+        for (int u = 0; u < NPF; ++u) {
+            const int q = u * WAVE + lane;
             const int r = q / Q, c = q % Q;
-            v[u] = q < F * Q ? (r == 0 ? drow[c] : prow[(int64_t)(r - 1) * Q + c]) : f32x4{0.f, 0.f, 0.f, 0.f};
+            if (q < F * Q) v[u] = r == 0 ? drow[c] : prow[(int64_t)(r - 1) * Q + c];
         }
+    }
+    __device__ __forceinline__ void store(float* x, int T, int lane) const {
+        const int F = T + 1;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = q0 + u * WAVE + lane;
+        for (int u = 0; u < NPF; ++u) {
+            const int q = u * WAVE + lane;
             if (q < F * Q) *reinterpret_cast<f32x4*>(x + (q / Q) * ST + (q % Q) * 4) = v[u];
         }
     }
-}
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void k_dot_fwd_mfma(const float* dense, const float* pooled, int64_t B, int T,
                                                       float* out) {
     extern __shared__ float smem[];
-    constexpr int ST = D + 4, KB = D < 64 ? D : 64, KH = KB / 2;
+    constexpr int ST = D + 4, KB = D < 64 ? D : 64, KH = KB / 2, NB = D / KB;
+    constexpr bool PREFETCH = D <= 128;         // the next sample's vectors in registers
     const int F = T + 1;
     const int64_t P = (int64_t)F * T / 2, ROW = D + P;
     const int lane = lane_id(), w = threadIdx.x / WAVE, W = blockDim.x / WAVE;
     float* x = smem + w * F * ST;
     const int row = lane & 31, half = lane >> 5;
-    for (int64_t base = (int64_t)blockIdx.x * W; base < B; base += (int64_t)gridDim.x * W) {
-        const int64_t b = base + w;
-        const bool live = b < B;
-        if (live) mf_stage<D>(x, dense, pooled, b, T, lane);
-        __syncthreads();
-        if (live) {
-            double acc[16];
+    const int64_t nw = (int64_t)gridDim.x * W;
+    MfVectors<D> pf;
+    int64_t b = (int64_t)blockIdx.x * W + w;
+    if (PREFETCH && b < B) pf.load(dense, pooled, b, T, lane);
+    for (; b < B; b += nw) {
+        if (!PREFETCH) pf.load(dense, pooled, b, T, lane);
+        pf.store(x, T, lane);
+        wave_sync();
+        if (PREFETCH && b + nw < B) pf.load(dense, pooled, b + nw, T, lane);
+        // one fp32 accumulator tile per block of KB elements
+        f32x16 c[NB];
+        const float* xr = x + (row < F ? row : 0) * ST + half * KH;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.0;
-            const float* xr = x + (row < F ? row : 0) * ST + half * KH;
-            for (int kb = 0; kb < D; kb += KB) {
-                f32x16 c = {};
+        for (int nb = 0; nb < NB; ++nb) {
+            c[nb] = f32x16{};
 #pragma unroll
-                for (int s = 0; s < KH; s += 4) {
-                    f32x4 v = *reinterpret_cast<const f32x4*>(xr + kb + s);
-                    if (row >= F) v = f32x4{0.f, 0.f, 0.f, 0.f};
-                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.x, v.x, c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.y, v.y, c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.z, v.z, c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(v.w, v.w, c, 0, 0, 0);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] += (double)c[r];
-            }
-            float* o = out + b * ROW;
-            for (int c = lane; c < D; c += WAVE) o[c] = x[c];
-            const int j = row;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = mf_row(r, lane);
-                if (i < j && j < F) o[D + pair_index(i, j, F)] = (float)acc[r];
+            for (int s = 0; s < KH; s += 4) {
+                f32x4 v = *reinterpret_cast<const f32x4*>(xr + nb * KB + s);
+                if (row >= F) v = f32x4{0.f, 0.f, 0.f, 0.f};
+                c[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.x, v.x, c[nb], 0, 0, 0);
+                c[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.y, v.y, c[nb], 0, 0, 0);
+                c[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.z, v.z, c[nb], 0, 0, 0);
+                c[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.w, v.w, c[nb], 0, 0, 0);
             }
         }
-        __syncthreads();                        // x is restaged for the next sample
+        float* o = out + b * ROW;
+        for (int cc = lane; cc < D; cc += WAVE) o[cc] = x[cc];
+        const int j = row;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = mf_row(r, lane);
+            double v = 0.0;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) v += (double)c[nb][r];
+            if (i < j && j < F) o[D + pair_index(i, j, F)] = (float)v;
+        }
+        wave_sync();                            // x is rewritten for the next sample
     }
 }
 
+// LDS per wave of the backward: X (F rows, stride D + 4), the pair row of
+// the output gradient (P floats) and the symmetric pair matrix G (32 x 33,
+// zero outside F x F and on the diagonal).  The backward is held to two
+// waves per SIMD (256 registers; click-log shape 0.95 -> 0.61 ms: the
+// second wave hides the first one's loads and scattered G reads); the
+// forward gains nothing from that and keeps its registers.
+constexpr int MF_GS = MF_MAX_F + 1;
+constexpr int MF_MAX_P = MF_MAX_F * (MF_MAX_F - 1) / 2;
+
 template <int D>
-__global__ __launch_bounds__(256) void k_dot_bwd_mfma(const float* dense, const float* pooled, const float* dout,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dot_bwd_mfma(const float* dense, const float* pooled, const float* dout,
                                                       int64_t B, int T, float* ddense, float* dpooled) {
     extern __shared__ float smem[];
-    constexpr int ST = D + 4, GS = MF_MAX_F + 1;
+    constexpr int ST = D + 4, NPP = (MF_MAX_P + WAVE - 1) / WAVE;
     const int F = T + 1;
-    const int64_t P = (int64_t)F * T / 2, ROW = D + P;
+    const int P = F * T / 2;
+    const int64_t ROW = D + P;
     const int lane = lane_id(), w = threadIdx.x / WAVE, W = blockDim.x / WAVE;
-    float* x = smem + w * (F * ST + MF_MAX_F * GS);
-    float* g = x + F * ST;                      // symmetric pair gradient, 32 x 33, zero outside F x F
+    float* x = smem + w * (F * ST + MF_MAX_P + MF_MAX_F * MF_GS);
+    float* gp = x + F * ST;                     // the sample's pair gradients, row-major pairs
+    float* g = gp + MF_MAX_P;
     const int row = lane & 31, half = lane >> 5;
-    for (int64_t base = (int64_t)blockIdx.x * W; base < B; base += (int64_t)gridDim.x * W) {
-        const int64_t b = base + w;
-        const bool live = b < B;
-        if (live) {
-            mf_stage<D>(x, dense, pooled, b, T, lane);
-            for (int e = lane; e < MF_MAX_F * GS; e += WAVE) g[e] = 0.f;
-        }
-        __syncthreads();
-        if (live) {
-            const float* go = dout + b * ROW + D;
-            for (int e = lane; e < F * F; e += WAVE) {
-                const int i = e / F, j = e % F;
-                if (i < j) {
-                    const float v = go[pair_index(i, j, F)];
-                    g[i * GS + j] = v;
-                    g[j * GS + i] = v;
-                }
-            }
-        }
-        __syncthreads();
-        if (live) {
-            const int ksteps = (F + 1) / 2;
-            for (int cb = 0; cb < D; cb += 32) {
-                f32x16 c = {};
-                for (int s = 0; s < ksteps; ++s) {
-                    const int k = 2 * s + half;
-                    const float a = g[row * GS + k];
-                    const float bv = k < F ? x[k * ST + cb + row] : 0.f;
-                    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, c, 0, 0, 0);
-                }
+    const int64_t nw = (int64_t)gridDim.x * W;
+    MfVectors<D> pf;
+    float pv[NPP];
+    constexpr bool PREFETCH = D <= 128;
+    int64_t b = (int64_t)blockIdx.x * W + w;
+    auto load_pairs = [&](int64_t bb) {
+        const float* go = dout + bb * ROW + D;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = mf_row(r, lane);
-                    const int col = cb + row;
-                    if (i >= F) continue;
-                    if (i == 0)
-                        ddense[b * D + col] = (float)((double)c[r] + (double)dout[b * ROW + col]);
-                    else
-                        dpooled[(b * T + (i - 1)) * (int64_t)D + col] = c[r];
-                }
+        for (int u = 0; u < NPP; ++u) {
+            const int p = u * WAVE + lane;
+            if (p < P) pv[u] = go[p];
+        }
+    };
+    if (PREFETCH && b < B) {
+        pf.load(dense, pooled, b, T, lane);
+        load_pairs(b);
+    }
+    for (; b < B; b += nw) {
+        if (!PREFETCH) {
+            pf.load(dense, pooled, b, T, lane);
+            load_pairs(b);
+        }
+        pf.store(x, T, lane);
+#pragma unroll
+        for (int u = 0; u < NPP; ++u) {
+            const int p = u * WAVE + lane;
+            if (p < P) gp[p] = pv[u];
+        }
+        wave_sync();
+        for (int e = lane; e < MF_MAX_F * MF_MAX_F; e += WAVE) {
+            const int i = e >> 5, j = e & 31;
+            const int lo = i < j ? i : j, hi = i < j ? j : i;
+            g[i * MF_GS + j] = (hi < F && lo != hi) ? gp[pair_index(lo, hi, F)] : 0.f;
+        }
+        wave_sync();
+        if (PREFETCH && b + nw < B) {
+            pf.load(dense, pooled, b + nw, T, lane);
+            load_pairs(b + nw);
+        }
+        const int ksteps = (F + 1) / 2;
+        for (int cb = 0; cb < D; cb += 32) {
+            f32x16 c = {};
+            for (int s = 0; s < ksteps; ++s) {
+                const int k = 2 * s + half;
+                const float a = g[row * MF_GS + k];
+                const float bv = k < F ? x[k * ST + cb + row] : 0.f;
+                c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, c, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = mf_row(r, lane);
+                const int col = cb + row;
+                if (i >= F) continue;
+                if (i == 0)
+                    ddense[b * D + col] = (float)((double)c[r] + (double)dout[b * ROW + col]);
+                else
+                    dpooled[(b * T + (i - 1)) * (int64_t)D + col] = c[r];
             }
         }
-        __syncthreads();
+        wave_sync();
     }
 }
 
@@ -361,7 +407,7 @@ int mf_waves(size_t per_wave) {
 }
 
 bool mf_ok(int32_t n_tables, int32_t dim) {
-    return n_tables + 1 <= MF_MAX_F && (dim == 32 || dim == 64 || dim == 128 || dim == 256);
+    return n_tables + 1 <= MF_MAX_F && (dim == 32 || dim == 64 || dim == 128);
 }
 
 int check_shape(int64_t batch, int32_t n_tables, int32_t dim, size_t* lds_fwd, size_t* lds_bwd) {
@@ -397,8 +443,7 @@ int dlrm_interaction_fwd(const float* d_dense, const float* d_pooled, int64_t ba
         switch (dim) {
             case 32: hipLaunchKernelGGL(k_dot_fwd_mfma<32>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
             case 64: hipLaunchKernelGGL(k_dot_fwd_mfma<64>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
-            case 128: hipLaunchKernelGGL(k_dot_fwd_mfma<128>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
-            default: hipLaunchKernelGGL(k_dot_fwd_mfma<256>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
+            default: hipLaunchKernelGGL(k_dot_fwd_mfma<128>, grid, block, lds, st, d_dense, d_pooled, batch, (int)n_tables, d_out); break;
         }
         return launch_status();
     }
@@ -420,7 +465,7 @@ int dlrm_interaction_bwd(const float* d_dense, const float* d_pooled, const floa
     if (!d_dense || !d_pooled || !d_dout || !d_ddense || !d_dpooled) return RSE_ERR_INVALID_ARG;
     if (mf_ok(n_tables, dim)) {
         const int F = n_tables + 1;
-        const size_t per_wave = ((size_t)F * (dim + 4) + (size_t)MF_MAX_F * (MF_MAX_F + 1)) * sizeof(float);
+        const size_t per_wave = ((size_t)F * (dim + 4) + MF_MAX_P + (size_t)MF_MAX_F * MF_GS) * sizeof(float);
         const int W = mf_waves(per_wave);
         const dim3 grid(fill_blocks(batch, W, 256 * 8)), block(W * WAVE);
         const size_t lds = per_wave * W;
@@ -428,8 +473,7 @@ int dlrm_interaction_bwd(const float* d_dense, const float* d_pooled, const floa
         switch (dim) {
             case 32: hipLaunchKernelGGL(k_dot_bwd_mfma<32>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
             case 64: hipLaunchKernelGGL(k_dot_bwd_mfma<64>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
-            case 128: hipLaunchKernelGGL(k_dot_bwd_mfma<128>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
-            default: hipLaunchKernelGGL(k_dot_bwd_mfma<256>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
+            default: hipLaunchKernelGGL(k_dot_bwd_mfma<128>, grid, block, lds, st, d_dense, d_pooled, d_dout, batch, (int)n_tables, d_ddense, d_dpooled); break;
         }
         return launch_status();
     }
