@@ -165,7 +165,7 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     n_ref_sched = 3 if full_schedules else 1
     # batches the run finds: warmup runs (each primed up to two batches
     # ahead), the timed run (two ahead), the reference runs (one ahead)
-    n_finds = n_warm_sched * (warmup + 2) + steps + 2 + n_ref_sched * (n_ref + 1) + 4
+    n_finds = n_warm_sched * (warmup + 2) + steps + 2 + n_ref_sched * (n_ref + 1) + (n_ref + 2) + 4
     n_batches = n_finds if distinct else max(3, args.batches)
 
     # ---------------------------------------------------------- setup ----
@@ -372,19 +372,24 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     assert idm_st == 0 and st == 0, (idm_st, st)
 
     # ----------------------------------------------------- timed region --
-    # The library brackets every launch of the segmented-update kernel with
-    # HIP events on its stream while the trace is on.
-    rse.trace_start(rse.K_SEG_UPDATE)
     ms_total, first = timed("lookahead", steps)
-    n_seg, seg_ms = rse.trace_stop()
     ms_step = ms_total / steps
-    t_seg = seg_ms / max(n_seg, 1)
     sel = [batch_at(first + k) for k in range(steps)]
     L_sel = [b["L"] for b in sel]
     U_sel = [int(b["nu"].item()) for b in sel]          # distinct rows each step updated
     new_rows = float(np.mean([int(b["nn"].item()) for b in sel]))   # rows each step's find inserted
 
     ms_by = {"lookahead": round(ms_step, 4)}
+    # The segmented-update kernel's launch time, from a second lookahead run
+    # in which the library brackets every launch of that kernel with HIP
+    # events on its stream (timing events add work to the stream, so the
+    # headline run above goes without them)
+    rse.trace_start(rse.K_SEG_UPDATE)
+    ms_traced, first_tr = timed("lookahead", n_ref)
+    n_seg, seg_ms = rse.trace_stop()
+    t_seg = seg_ms / max(n_seg, 1)
+    ms_by["lookahead_traced"] = round(ms_traced / n_ref, 4)
+    sel_tr = [batch_at(first_tr + k) for k in range(n_ref)]
     phase = None
     rse.trace_start(rse.K_FWD)
     ms_by["serial"] = round(timed("serial", n_ref)[0] / n_ref, 4)
@@ -409,9 +414,11 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     # sorted (row, gradient-row) pairs read (8 B per lookup) + one gradient
     # row per lookup (dim * 4 B) + each touched row (weights + state) read
     # and written once
-    seg_bytes = float(np.mean([L * 8 + L * D * 4 + U * rb * 2 for L, U in zip(L_sel, U_sel)]))
+    L_tr = [b["L"] for b in sel_tr]
+    U_tr = [int(b["nu"].item()) for b in sel_tr]
+    seg_bytes = float(np.mean([L * 8 + L * D * 4 + U * rb * 2 for L, U in zip(L_tr, U_tr)]))
     # the same kernel by compulsory bytes: each bag's gradient row read once
-    seg_comp = float(np.mean([L * 8 + T * B * D * 4 + U * rb * 2 for L, U in zip(L_sel, U_sel)]))
+    seg_comp = float(np.mean([L * 8 + T * B * D * 4 + U * rb * 2 for L, U in zip(L_tr, U_tr)]))
     seg_gbs = seg_bytes / (t_seg * 1e-3) / 1e9
     TB = T * B
     w_bytes = D * (2 if cfg.wdtype == synth.BF16 else 4)

@@ -249,9 +249,16 @@ class IdMap:
 
     # ---------------------------------- admission, age, eviction, resize --
     def track_age(self, n_rows: int, stream=None):
-        """Attach zeroed per-row stamps for rows [0, n_rows); lookups write the
-        clock into them (n_rows must cover the blocks' capacity)."""
-        self.stamps = torch.zeros(max(int(n_rows), 1), dtype=torch.int32, device=self.device)   # uint32
+        """Attach per-row stamps for rows [0, n_rows); lookups write the clock
+        into them (n_rows must cover the blocks' capacity: after the blocks
+        grow, call again with the new capacity).  Stamps already attached are
+        carried over; new rows start at 0."""
+        old = getattr(self, "stamps", None)
+        new = torch.zeros(max(int(n_rows), 1), dtype=torch.int32, device=self.device)   # uint32
+        if old is not None:                     # copied on the current stream
+            k = min(old.numel(), new.numel())
+            new[:k].copy_(old[:k])
+        self.stamps = new
         check(lib.rse_idmap_set_stamps(self.handle, _ptr(self.stamps), int(n_rows)), "rse_idmap_set_stamps")
         return self
 

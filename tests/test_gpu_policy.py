@@ -283,3 +283,66 @@ def test_save_after_eviction_and_load_with_free_list(tmp_path):
     wa, sa = gpu.blocks.read_rows(offs)
     wb, sb = blk2.read_rows(offs)
     assert torch.equal(wa.view(torch.int32), wb.view(torch.int32))
+
+
+def test_admission_and_stamps_through_the_noalloc_find():
+    """Admission and age tracking through idmap_find_or_insert_noalloc (its
+    candidate lists live in the library's static scratch) equal the
+    workspace find's, call after call."""
+    import recommender_sparse_embedding_amd as rse
+
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(31)
+    objs = []
+    for _ in range(2):
+        m = rse.IdMap([1 << 16] * 2, max_load=0.7, hash_seed=4, device=dev)
+        b = rse.EmbeddingBlocks(16, rse.F32, rse.SGD, rows_per_chunk_log2=14, seed=1, device=dev).grow(4)
+        m.enable_admission(2, 2048, 3, seed=8)
+        m.track_age(b.capacity)
+        b.enable_free_list()
+        objs.append((m, b))
+    (m_a, b_a), (m_b, b_b) = objs
+    n_new_a = torch.zeros(1, dtype=torch.int64, device=dev)
+    n_new_b = torch.zeros(1, dtype=torch.int64, device=dev)
+    for call, n in enumerate((40_000, 9_000, 25_000)):
+        ids = rng.zipf(1.2, n).astype(np.int64) % 30_000
+        bounds = np.array([0, n // 2, n], np.int64)
+        t_ids, t_b = torch.from_numpy(ids).to(dev), torch.from_numpy(bounds).to(dev)
+        ro_a, ro_b = torch.empty_like(t_ids), torch.empty_like(t_ids)
+        for m in (m_a, m_b):
+            m.set_clock(call + 1)
+        rse.idmap_find_or_insert(m_a, b_a, t_ids, t_b, 1, 2, ro_a, n_new_a)
+        rse.idmap_find_or_insert_noalloc(m_b, b_b, t_ids, t_b, 1, 2, ro_b, n_new_b)
+        assert torch.equal(ro_a, ro_b) and int(n_new_a.item()) == int(n_new_b.item()), f"call {call}"
+        assert torch.equal(m_a.sketch, m_b.sketch) and torch.equal(m_a.stamps, m_b.stamps)
+        assert int((ro_a < 0).sum()) > 0                       # some keys not admitted yet
+        if call == 1:
+            m_a.evict(b_a, 2)
+            m_b.evict(b_b, 2)
+    assert m_a.status() == m_b.status() and m_a.status()[0] == 0
+
+
+def test_stamps_carried_over_when_reattached_after_grow():
+    import recommender_sparse_embedding_amd as rse
+
+    dev = torch.device("cuda")
+    m = rse.IdMap([256], max_load=0.7, device=dev)
+    b = rse.EmbeddingBlocks(8, rse.F32, rse.SGD, rows_per_chunk_log2=4, device=dev).grow(1)   # 16 rows
+    m.track_age(b.capacity)
+    m.set_clock(5)
+    n_new = torch.zeros(1, dtype=torch.int64, device=dev)
+    ids = torch.arange(10, dtype=torch.int64, device=dev)
+    bo = torch.tensor([0, 10], dtype=torch.int64, device=dev)
+    ro = torch.empty_like(ids)
+    rse.idmap_find_or_insert(m, b, ids, bo, 1, 1, ro, n_new)
+    b.grow(1)                                                   # 32 rows: the stamps no longer cover it
+    with pytest.raises(rse.RseError):
+        rse.idmap_find_or_insert(m, b, ids, bo, 1, 1, ro, n_new)
+    m.track_age(b.capacity)
+    m.set_clock(6)
+    ids2 = torch.arange(5, 25, dtype=torch.int64, device=dev)
+    bo2 = torch.tensor([0, 20], dtype=torch.int64, device=dev)
+    ro2 = torch.empty_like(ids2)
+    rse.idmap_find_or_insert(m, b, ids2, bo2, 1, 1, ro2, n_new)
+    st = m.stamps.cpu().numpy()
+    assert list(st[:5]) == [5] * 5 and list(st[5:25]) == [6] * 20 and not st[25:].any()
