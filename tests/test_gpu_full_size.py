@@ -129,7 +129,7 @@ def _compare_updated(w_g, s_g, w_prev, w_r, s_r, rtol, what):
         assert_close(s_g, s_r, np.abs(s_r.astype(np.float64)) + 1e-30, 1e-5, what + " state")
 
 
-def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float):
+def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float, neighbours: bool = False):
     wl = synth.Workload(cfg)
     L_max = max(int(wl.batch_inputs(s)[1][-1]) for s in range(steps))
     extra = int(L_max * cfg.fresh_frac * 1.05 * steps) + 1024 if cfg.fresh_frac > 0 else 0
@@ -159,6 +159,7 @@ def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float):
             if s == 0:       # rows still hold their exact initial values
                 assert np.array_equal(out_g.view(np.uint32), out_r.view(np.uint32)), f"one-hot pooled rows, step {s}"
         assert_close(out_g, out_r, pooled_magnitude(orc, ro_r, bo, cfg), rtol, f"pooled output, step {s}")
+        last_out = out_g
         del out_g, out_r
         offs = np.unique(ro_r[ro_r >= 0])
         prev_w, _ = orc.get_rows(offs)
@@ -179,14 +180,83 @@ def _whole_oracle_steps(cfg: synth.Config, steps: int, map_load: float):
         assert np.array_equal(w_g.view(np.uint32), w_r.view(np.uint32)), "never-touched rows changed"
         assert np.array_equal(s_g.view(np.uint32), s_r.view(np.uint32))
         _say(f"  step {s}: {len(ids)} lookups, {U} rows updated, all equal to the oracle")
+    if neighbours:
+        _interaction_full_size(last_out)
+        del last_out
+        _eviction_full_size(gpu, orc, wl, steps)
+
+
+def _interaction_full_size(pooled: np.ndarray):
+    """The DLRM interaction on the step's pooled output at its full shape
+    (the launch the bench times), sampled samples against the oracle."""
+    import recommender_sparse_embedding_amd as rse
+    from oracle import interaction as ointer
+
+    B, T, D = pooled.shape
+    rng = np.random.default_rng(5)
+    dense = rng.standard_normal((B, D)).astype(np.float32)
+    t_dense, t_pooled = torch.from_numpy(dense).cuda(), torch.from_numpy(pooled).cuda()
+    out = rse.dlrm_interaction_fwd(t_dense, t_pooled)
+    dout = rng.standard_normal(tuple(out.shape)).astype(np.float32)
+    dd, dp = rse.dlrm_interaction_bwd(t_dense, t_pooled, torch.from_numpy(dout).cuda())
+    sel = np.sort(rng.choice(B, 512, replace=False))
+    ref, mag = ointer.interaction_fwd(dense[sel], pooled[sel])
+    assert_close(out.cpu().numpy()[sel], ref, mag, 1e-5, "interaction forward, sampled samples")
+    rdd, rdp, mdd, mdp = ointer.interaction_bwd(dense[sel], pooled[sel], dout[sel])
+    assert_close(dd.cpu().numpy()[sel], rdd, mdd, 1e-5, "interaction dense gradient, sampled samples")
+    assert_close(dp.cpu().numpy()[sel], rdp, mdp, 1e-5, "interaction pooled gradient, sampled samples")
+    _say(f"  interaction [{B}, {T}, {D}]: 512 sampled samples equal to the oracle")
+
+
+def _eviction_full_size(gpu, orc, wl, step: int):
+    """Eviction at full size: age tracking on, one batch at clock 1, the
+    rehash with minimum clock 1 keeps that batch's keys; the map's entries
+    and the rebuilt free list (every other row, ascending) equal the
+    oracle's, and evicted keys are absent."""
+    rse, cfg, dev = gpu.rse, gpu.cfg, gpu.dev
+    gpu.map.track_age(gpu.blk.capacity)
+    gpu.blk.enable_free_list()
+    orc.set_tracking(True)
+    orc.set_recycling(True)
+    gpu.map.set_clock(1)
+    orc.set_clock(1)
+    ids, bo = wl.batch_inputs(step)
+    t_ids, t_bo = torch.from_numpy(ids).to(dev), torch.from_numpy(bo).to(dev)
+    ro = torch.empty_like(t_ids)
+    n_new = torch.zeros(1, dtype=torch.int64, device=dev)
+    rse.idmap_find_or_insert(gpu.map, gpu.blk, t_ids, t_bo, cfg.batch, cfg.n_tables, ro, n_new,
+                             ws=gpu.map.workspace(len(ids)))
+    ro_r, _ = orc.find_or_insert(ids, bo, cfg.batch)
+    assert np.array_equal(ro.cpu().numpy(), ro_r)
+    gpu.map.evict(gpu.blk, 1)
+    kept = orc.rehash(1)
+    k, t, o, cnt = gpu.map.export(kept + 16)
+    order = torch.argsort(o)
+    kr, tr, orr = orc.entries()
+    assert cnt == kept == len(kr)
+    assert np.array_equal(o[order].cpu().numpy(), orr) and np.array_equal(k[order].cpu().numpy(), kr)
+    assert np.array_equal(t[order].cpu().numpy(), tr)
+    head, left = gpu.blk.free_list()
+    left_r, head_r = orc.free_list()
+    assert head == head_r == 0 and np.array_equal(left.cpu().numpy(), left_r)
+    ids2, bo2 = wl.batch_inputs(step + 1)
+    t_ids2, t_bo2 = torch.from_numpy(ids2).to(dev), torch.from_numpy(bo2).to(dev)
+    ro2 = torch.empty_like(t_ids2)
+    rse.idmap_find_or_insert(gpu.map, gpu.blk, t_ids2, t_bo2, cfg.batch, cfg.n_tables, ro2, n_new,
+                             insert_missing=False, ws=gpu.map.workspace(len(ids2)))
+    ro2_r, _ = orc.find_or_insert(ids2, bo2, cfg.batch, insert_missing=False)
+    assert np.array_equal(ro2.cpu().numpy(), ro2_r) and (ro2_r < 0).any()
+    _say(f"  eviction: {kept} keys kept, {len(left_r)} rows freed, equal to the oracle")
 
 
 def test_click_log_full_size_whole_oracle():
     """26 one-hot tables, 55.8M live rows, batch 65,536, dim 128, Adagrad:
-    every row offset, every pooled row and every updated row of two steps."""
+    every row offset, every pooled row and every updated row of two steps;
+    then the interaction on the pooled output at its full shape (sampled)
+    and an eviction of the full map (entries and free list exactly)."""
     _free()
     try:
-        _whole_oracle_steps(synth.config(2), 2, map_load=0.5)
+        _whole_oracle_steps(synth.config(2), 2, map_load=0.5, neighbours=True)
     finally:
         _free()
 
