@@ -157,3 +157,29 @@ def test_feature_programs_validated_on_the_host(lib):
     assert create([(I64, [(MOD, 0, 0)])]) == INV                       # modulus 0
     assert create([(I64, [(7, 0, 0)])]) == INV                         # unknown operation
     assert create([(2, [])]) == INV                                    # unknown input kind
+
+
+def test_new_entry_points_reject_bad_arguments_without_gpu_work(lib):
+    """Admission / age / eviction / free list, feature transforms and the
+    interaction: null handles and impossible sizes are refused on the host."""
+    INV = -1
+    sz = ctypes.c_size_t()
+    head, cnt = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.rse_idmap_set_stamps(None, None, 0) == INV
+    assert lib.rse_idmap_set_clock(None, 3) == INV
+    assert lib.rse_idmap_set_admission(None, None, 4, 1024, 2, 0, None) == INV
+    assert lib.rse_idmap_rehash(None, None, None, 0, None, 0, None) == INV
+    assert lib.rse_idmap_rehash_workspace_size(None, None, ctypes.byref(sz)) == INV
+    assert lib.rse_blocks_set_free_list(None, None, 0, None) == INV
+    assert lib.rse_blocks_free_status(None, ctypes.byref(head), ctypes.byref(cnt), None) == INV
+    assert lib.feature_transform(None, None, 0, None, 1, None, None) == INV
+    assert lib.rse_features_mem_size(0, 0, ctypes.byref(sz)) == INV
+    assert lib.rse_features_mem_size(2, -1, ctypes.byref(sz)) == INV
+    assert lib.rse_features_mem_size(2, 10, ctypes.byref(sz)) == 0 and sz.value >= 256 + 2 * 72 + 80
+    assert lib.dlrm_interaction_fwd(None, None, -1, 3, 4, None, None) == INV
+    assert lib.dlrm_interaction_fwd(None, None, 4, 0, 4, None, None) == INV
+    assert lib.dlrm_interaction_bwd(None, None, None, 4, 3, 0, None, None, None) == INV
+    # a batch with work but null pointers
+    assert lib.dlrm_interaction_fwd(None, None, 4, 3, 4, None, None) == INV
+    # 201 fields of dim 128 exceed one sample's LDS: unsupported, not invalid
+    assert lib.dlrm_interaction_fwd(None, None, 4, 200, 128, None, None) == -2
