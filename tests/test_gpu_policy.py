@@ -346,3 +346,31 @@ def test_stamps_carried_over_when_reattached_after_grow():
     rse.idmap_find_or_insert(m, b, ids2, bo2, 1, 1, ro2, n_new)
     st = m.stamps.cpu().numpy()
     assert list(st[:5]) == [5] * 5 and list(st[5:25]) == [6] * 20 and not st[25:].any()
+
+
+def test_degenerate_cases():
+    """An empty map rehashed (free list of every row below the counter:
+    none); a call whose every absent key is below the admission threshold
+    (no new rows, free list untouched, -1 everywhere); an empty feature
+    batch."""
+    import recommender_sparse_embedding_amd as rse
+
+    dev = torch.device("cuda")
+    m = rse.IdMap([128, 128], max_load=0.7, device=dev)
+    b = rse.EmbeddingBlocks(8, rse.F32, rse.SGD, rows_per_chunk_log2=4, device=dev).grow(1)
+    b.enable_free_list()
+    m.track_age(b.capacity)
+    m.evict(b, 5)                                   # nothing to keep, nothing to free
+    assert m.status() == (0, [0, 0]) and b.free_list()[1].numel() == 0 and b.status()[0] == 0
+    m.enable_admission(1000, 64, 2)
+    ids = torch.tensor([1, 2, 2, 3, 7, 7], dtype=torch.int64, device=dev)
+    bo = torch.tensor([0, 3, 6], dtype=torch.int64, device=dev)
+    ro = torch.empty_like(ids)
+    n_new = torch.zeros(1, dtype=torch.int64, device=dev)
+    rse.idmap_find_or_insert(m, b, ids, bo, 1, 2, ro, n_new)
+    assert bool((ro == -1).all()) and int(n_new.item()) == 0 and b.status()[0] == 0
+    assert int(m.sketch.view(-1)[:64].sum().item()) == 6          # each row of the sketch counted 6 lookups
+    ft = rse.FeatureTransform([(rse.FT_INT64, [(rse.FT_MOD, 7)])] * 2, device=dev)
+    out = rse.feature_transform(ft, torch.zeros(0, dtype=torch.int64, device=dev),
+                                torch.zeros(3, dtype=torch.int64, device=dev))
+    assert out.numel() == 0 and ft.status() == 0
