@@ -67,6 +67,9 @@ def parse():
                    help="timed steps of workloads 1, 3, 4 and 5 in the default run")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--map-load", type=float, default=0.0, help="override the workload's map load")
+    p.add_argument("--ceilings", action="store_true",
+                   help="only measure plain reference kernels (torch's read, write, copy and row gathers) "
+                        "that bound what the library's kernels can reach on this GPU")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (an elementwise kernel that reads and "
                         "writes each byte once), to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -86,6 +89,51 @@ def copy_calibration():
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 10}))
+
+
+def ceilings():
+    """Bandwidth of plain kernels on this GPU (torch's own, one launch
+    each, median of 10 after warm-up): a read-only reduction, a fill, a
+    copy, and gathers of 512-byte rows (the click-log update's gradient
+    rows) in random and in sorted order of a [65536 * 26, 128] fp32 array,
+    1.7M rows gathered."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = 1 << 28                                            # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    rows = torch.randn(65536 * 26, 128, device=dev)
+    g = torch.Generator(device=dev).manual_seed(3)
+    idx = torch.randint(0, rows.shape[0], (1703936,), device=dev, generator=g)
+    idx_sorted = torch.sort(idx).values
+    out = torch.empty(idx.numel(), 128, device=dev)
+
+    def timed(fn, nbytes):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        return {"ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+    res = {
+        "read (sum of 1 GiB)": timed(lambda: a.sum(), 4 * n),
+        "write (fill of 1 GiB)": timed(lambda: b.fill_(2.0), 4 * n),
+        "copy (neg, 1 GiB read + 1 GiB written)": timed(lambda: torch.neg(a, out=b), 8 * n),
+        "gather 512 B rows, random order (872 MB read + written)":
+            timed(lambda: torch.index_select(rows, 0, idx, out=out), 2 * out.numel() * 4),
+        "gather 512 B rows, sorted order": timed(lambda: torch.index_select(rows, 0, idx_sorted, out=out),
+                                                 2 * out.numel() * 4),
+    }
+    print(json.dumps({"ceilings": res, "peak_gbs": PEAK_HBM_GBS}))
 
 
 def kernel_sources_sha() -> str:
@@ -679,6 +727,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.ceilings:
+        ceilings()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
