@@ -91,6 +91,7 @@ struct BwdArgs {
     RowsView rv;
     const uint2* pairs;          // sorted lookups: x = row, y = gradient row of its bag
     const int64_t* bag_off;
+    const double* inv_len;       // mean pooling: 1 / bag length, per gradient row
     const float* grad;           // [batch, n_tables, dim]; sorted values index its rows
     int64_t batch;
     int32_t n_tables;
@@ -239,11 +240,20 @@ __device__ __forceinline__ const float* grad_row(const BwdArgs& a, uint32_t gr, 
 // pooling only; a bag that holds a lookup is not empty).  One division per
 // lookup; each element's share is then a product (within one fp64 rounding
 // of the quotient).
-__device__ __forceinline__ double inv_bag_len(const BwdArgs& a, uint32_t gr) {
-    const uint32_t b = gr / (uint32_t)a.n_tables;
-    const uint32_t t = gr - b * (uint32_t)a.n_tables;
-    const int64_t j = (int64_t)t * a.batch + b;
-    return 1.0 / (double)(a.bag_off[j + 1] - a.bag_off[j]);
+__device__ __forceinline__ double inv_bag_len(const BwdArgs& a, uint32_t gr) { return a.inv_len[gr]; }
+
+// Mean pooling: 1 / length of every bag, indexed by the bag's gradient row
+// b * n_tables + t, computed once per bag before the update (each lookup
+// then reads one 8-byte value that stays in L2, instead of two bag offsets
+// and an fp64 division; the values are the same).
+__global__ void k_inv_len(const int64_t* bag_off, int64_t batch, int32_t n_tables, double* inv) {
+    const int64_t n_bags = batch * n_tables;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_bags;
+         j += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = j / batch, b = j - t * batch;
+        const int64_t len = bag_off[j + 1] - bag_off[j];
+        inv[b * n_tables + t] = len > 0 ? 1.0 / (double)len : 0.0;
+    }
 }
 
 template <int VEC>
@@ -894,9 +904,10 @@ struct BwdWs {
     uint2* singles;
     Multi* multis;
     void* sort_ws;
+    double* inv_len;
 };
 
-BwdWs carve(void* base, int64_t n_ids, int32_t dim, size_t* total) {
+BwdWs carve(void* base, int64_t n_ids, int64_t n_bags, int32_t dim, size_t* total) {
     Carver c(base);
     BwdWs w;
     const size_t n = (size_t)(n_ids > 0 ? n_ids : 1);
@@ -909,6 +920,7 @@ BwdWs carve(void* base, int64_t n_ids, int32_t dim, size_t* total) {
     w.singles = c.take<uint2>(n);
     w.multis = c.take<Multi>(n / 2 + 1);
     w.sort_ws = c.take<char>(sort_workspace((int64_t)n, nullptr));
+    w.inv_len = c.take<double>((size_t)(n_bags > 0 ? n_bags : 1));
     if (total) *total = c.size();
     return w;
 }
@@ -986,7 +998,7 @@ extern "C" {
 
 int rse_bwd_workspace_size(int64_t n_ids, int32_t n_tables, int64_t batch, int32_t dim, size_t* bytes_out) {
     if (!bytes_out || n_ids < 0 || n_tables <= 0 || batch < 0 || dim <= 0) return RSE_ERR_INVALID_ARG;
-    carve(nullptr, n_ids, dim, bytes_out);
+    carve(nullptr, n_ids, (int64_t)n_tables * batch, dim, bytes_out);
     return RSE_OK;
 }
 
@@ -999,7 +1011,7 @@ int embedding_bag_bwd_prepare(rse_blocks* blocks, const int64_t* d_row_off, int6
     const int64_t n_bags = (int64_t)n_tables * batch;
     if (n_ids > RSE_MAX_BWD_IDS || n_bags > (int64_t)0xFFFFFFFFll) return RSE_ERR_INVALID_ARG;
     size_t need = 0;
-    BwdWs w = carve(d_ws, n_ids, blocks->dim, &need);
+    BwdWs w = carve(d_ws, n_ids, n_bags, blocks->dim, &need);
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     SortPrep sp = sort_prep(w.sort_ws, n_ids);
@@ -1066,7 +1078,7 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
     if (opt->kind != blocks->optim) return RSE_ERR_INVALID_ARG;
     if (opt->kind == RSE_ADAM && opt->step < 1) return RSE_ERR_INVALID_ARG;
     size_t need = 0;
-    BwdWs w = carve(d_ws, n_ids, blocks->dim, &need);
+    BwdWs w = carve(d_ws, n_ids, n_bags, blocks->dim, &need);
     if (ws_bytes < need) return RSE_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     SortPrep sp = sort_prep(w.sort_ws, n_ids);
@@ -1079,6 +1091,7 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
     a.rv = blocks->view();
     a.pairs = plan->sorted_in_alt ? w.p1 : w.p0;
     a.bag_off = d_bag_offsets;
+    a.inv_len = w.inv_len;
     a.grad = d_grad;
     a.batch = batch;
     a.n_tables = n_tables;
@@ -1103,6 +1116,9 @@ int embedding_bag_bwd_apply(rse_blocks* blocks, const rse_bwd_plan* plan, const 
     a.op.omb2 = 1.0 - opt->beta2;
     a.op.inv_bc1 = opt->kind == RSE_ADAM ? 1.0 / (1.0 - std::pow(opt->beta1, (double)opt->step)) : 1.0;
     a.op.sq_inv_bc2 = opt->kind == RSE_ADAM ? std::sqrt(1.0 / (1.0 - std::pow(opt->beta2, (double)opt->step))) : 1.0;
+    if (a.mean)
+        hipLaunchKernelGGL(k_inv_len, dim3(fill_blocks(n_bags, 256, 4096)), dim3(256), 0, s, d_bag_offsets, batch,
+                           n_tables, w.inv_len);
     return dispatch(a, blocks->dim, blocks->w_dtype == RSE_BF16, opt->kind, n_ids, s);
 }
 
