@@ -256,11 +256,11 @@ __global__ void k_inv_len(const int64_t* bag_off, int64_t batch, int32_t n_table
     }
 }
 
-template <int VEC>
+template <int VEC, bool NT = false>
 __device__ __forceinline__ void load_grad(float* out, const float* src) {
 #pragma unroll
     for (int k = 0; k < VEC; k += 4) {
-        const f32x4 v = gload_f4(src + k);
+        const f32x4 v = gload_f4x<NT>(src + k);
         out[k] = v.x;
         out[k + 1] = v.y;
         out[k + 2] = v.z;
@@ -282,7 +282,7 @@ __device__ __forceinline__ void add_grad(double* acc, const float* gv, double in
 // order.  U gradient rows are loaded together (all loads issued before any
 // is used); a last step shorter than U repeats the range's last row (masked
 // out of the sum), so a ragged end costs one round trip, not one per row.
-template <int D, bool BF16, bool MEAN>
+template <int D, bool BF16, bool MEAN, bool ONCE>
 __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_vals, int x, int y, int li,
                                           double* acc) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -293,7 +293,7 @@ __device__ __forceinline__ void sum_range(const BwdArgs& a, const uint32_t* s_va
 #pragma unroll
         for (int u = 0; u < U; ++u) j[u] = s_vals[q + u < y ? q + u : y - 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
+        for (int u = 0; u < U; ++u) load_grad<VEC, ONCE>(gv[u], grad_row<D, BF16>(a, j[u], li));
         double inv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) inv[u] = MEAN ? inv_bag_len(a, j[u]) : 1.0;
@@ -342,17 +342,17 @@ struct RowRegs {
     float st1[VEC];
 };
 
-template <int D, bool BF16, int OPT>
+template <int D, bool BF16, int OPT, bool NT = false>
 __device__ __forceinline__ void load_row(const char* row, int li, RowRegs<D, BF16>& r) {
     constexpr int VEC = Geo<D, BF16>::VEC;
     constexpr int64_t W_BYTES = (int64_t)D * (BF16 ? 2 : 4);
-    r.w = gload_u4(row + li * 16);
+    r.w = gload_u4x<NT>(row + li * 16);
     const float* st0 = reinterpret_cast<const float*>(row + W_BYTES) + li * VEC;
-    if (OPT != RSE_SGD) load_grad<VEC>(r.st0, st0);
-    if (OPT == RSE_ADAM) load_grad<VEC>(r.st1, st0 + D);
+    if (OPT != RSE_SGD) load_grad<VEC, NT>(r.st0, st0);
+    if (OPT == RSE_ADAM) load_grad<VEC, NT>(r.st1, st0 + D);
 }
 
-template <int D, bool BF16, int OPT>
+template <int D, bool BF16, int OPT, bool NT = false>
 __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, const RowRegs<D, BF16>& r,
                                            const double* g) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -387,7 +387,7 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
         }
 #pragma unroll
         for (int k = 0; k < VEC; k += 4)
-            gstore_f4(st0 + k, f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]});
+            gstore_f4x<NT>(st0 + k, f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]});
     } else {
         float m[VEC], v[VEC];
 #pragma unroll
@@ -403,8 +403,8 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
         }
 #pragma unroll
         for (int k = 0; k < VEC; k += 4) {
-            gstore_f4(st0 + k, f32x4{m[k], m[k + 1], m[k + 2], m[k + 3]});
-            gstore_f4(st1 + k, f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]});
+            gstore_f4x<NT>(st0 + k, f32x4{m[k], m[k + 1], m[k + 2], m[k + 3]});
+            gstore_f4x<NT>(st1 + k, f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]});
         }
     }
     u32x4 out;
@@ -418,7 +418,7 @@ __device__ __forceinline__ void finish_row(const BwdArgs& a, char* row, int li, 
             q4[k] = (uint32_t)f64_to_bf16_rne(wn[2 * k]) | ((uint32_t)f64_to_bf16_rne(wn[2 * k + 1]) << 16);
         out = u32x4{q4[0], q4[1], q4[2], q4[3]};
     }
-    gstore_u4(row + li * 16, out);
+    gstore_u4x<NT>(row + li * 16, out);
 }
 
 // ------------------------------------------------- segmented update ------
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
 // piece's start (continuing an earlier piece) goes to carry slot 0, the part
 // of a long segment starting in the piece (continuing past it) to slot 1.
 // Returns whether slot 0 was written.
-template <int D, bool BF16, bool MEAN, int NMASK>
+template <int D, bool BF16, bool MEAN, bool ONCE, int NMASK>
 __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_keys, const uint32_t* s_vals,
                                           const unsigned long long* s_head, int wn, int64_t k, int x0, int xb,
                                           int li) {
@@ -579,7 +579,7 @@ __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_ke
             double acc[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-            sum_range<D, BF16, MEAN>(a, s_vals, x0, e < lim ? e : lim, li, acc);
+            sum_range<D, BF16, MEAN, ONCE>(a, s_vals, x0, e < lim ? e : lim, li, acc);
             carry(0, acc);
             wrote0 = true;
         }
@@ -589,7 +589,7 @@ __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_ke
         double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-        sum_range<D, BF16, MEAN>(a, s_vals, hl, xb, li, acc);
+        sum_range<D, BF16, MEAN, ONCE>(a, s_vals, hl, xb, li, acc);
         carry(1, acc);
     }
     return wrote0;
@@ -599,7 +599,7 @@ __device__ __forceinline__ bool walk_long(const BwdArgs& a, const uint32_t* s_ke
 // rows all requested before any is used; the group's next entries are
 // requested before this round's rows, so a round waits for one memory round
 // trip.
-template <int D, bool BF16, int OPT, bool MEAN, int SPG>
+template <int D, bool BF16, int OPT, bool MEAN, bool ONCE, int SPG>
 __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
                                              int64_t n_groups, int li, int64_t lo, int64_t ns) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -618,10 +618,10 @@ __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s
 #pragma unroll
         for (int u = 0; u < SPG; ++u) {
             rp[u] = a.rv.row(s_chunks, e[u].x);
-            load_row<D, BF16, OPT>(rp[u], li, rr[u]);
+            load_row<D, BF16, OPT, ONCE>(rp[u], li, rr[u]);
         }
 #pragma unroll
-        for (int u = 0; u < SPG; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, e[u].y, li));
+        for (int u = 0; u < SPG; ++u) load_grad<VEC, ONCE>(gv[u], grad_row<D, BF16>(a, e[u].y, li));
         double inv[SPG];
 #pragma unroll
         for (int u = 0; u < SPG; ++u) inv[u] = MEAN ? inv_bag_len(a, e[u].y) : 1.0;
@@ -632,7 +632,7 @@ __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
                 add_grad<VEC, MEAN>(acc, gv[u], inv[u]);
-                finish_row<D, BF16, OPT>(a, rp[u], li, rr[u], acc);
+                finish_row<D, BF16, OPT, ONCE>(a, rp[u], li, rr[u], acc);
             }
         }
 #pragma unroll
@@ -645,7 +645,7 @@ __device__ __forceinline__ void role_singles(const BwdArgs& a, const uint64_t* s
 // group's next segment descriptor is requested with this segment's row, and
 // that segment's first U bag ids before this one's update, so a segment
 // waits for one memory round trip per U lookups.
-template <int D, bool BF16, int OPT, bool MEAN>
+template <int D, bool BF16, int OPT, bool MEAN, bool ONCE>
 __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_chunks, int64_t gid,
                                             int64_t n_groups, int li, int64_t lo, int64_t nm) {
     constexpr int VEC = Geo<D, BF16>::VEC;
@@ -660,7 +660,7 @@ __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_
         const Multi mn = a.multis[inx < nm ? inx : nm - 1];
         char* rp = a.rv.row(s_chunks, m.key);
         RowRegs<D, BF16> rr;
-        load_row<D, BF16, OPT>(rp, li, rr);
+        load_row<D, BF16, OPT, ONCE>(rp, li, rr);
         double acc[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
@@ -668,7 +668,7 @@ __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_
         while (true) {
             float gv[U][VEC];
 #pragma unroll
-            for (int u = 0; u < U; ++u) load_grad<VEC>(gv[u], grad_row<D, BF16>(a, j[u], li));
+            for (int u = 0; u < U; ++u) load_grad<VEC, ONCE>(gv[u], grad_row<D, BF16>(a, j[u], li));
             double inv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) inv[u] = MEAN ? inv_bag_len(a, j[u]) : 1.0;
@@ -682,7 +682,7 @@ __device__ __forceinline__ void role_multis(const BwdArgs& a, const uint64_t* s_
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) j[u] = a.pairs[mn.start + (u < (int)mn.len ? u : mn.len - 1)].y;
-        finish_row<D, BF16, OPT>(a, rp, li, rr, acc);
+        finish_row<D, BF16, OPT, ONCE>(a, rp, li, rr, acc);
         m = mn;
     }
 }
@@ -692,7 +692,7 @@ constexpr int singles_per_group() {
     return 2;
 }
 
-template <int D, bool BF16, int OPT, bool MEAN>
+template <int D, bool BF16, int OPT, bool MEAN, bool ONCE>
 __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     using G = Geo<D, BF16>;
     constexpr int LPR = G::LPR, GPB = G::GPB, WIN = G::WIN;
@@ -731,11 +731,11 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
         const int64_t sq = r * S8 / rest, sq1 = (r + 1) * S8 / rest;
         if (sq1 > sq) {
             const int64_t ns = (int64_t)a.ctr->n_single;
-            role_singles<D, BF16, OPT, MEAN, singles_per_group<D, BF16>()>(
+            role_singles<D, BF16, OPT, MEAN, ONCE, singles_per_group<D, BF16>()>(
                 a, s_chunks, sq * GPB + g, S8 * GPB, li, xcd * ns / N_XCD, (xcd + 1) * ns / N_XCD);
         } else {
             const int64_t nm = (int64_t)a.ctr->n_multi;
-            role_multis<D, BF16, OPT, MEAN>(a, s_chunks, (r - sq1) * GPB + g, (rest - S8) * GPB, li, xcd * nm / N_XCD,
+            role_multis<D, BF16, OPT, MEAN, ONCE>(a, s_chunks, (r - sq1) * GPB + g, (rest - S8) * GPB, li, xcd * nm / N_XCD,
                                       (xcd + 1) * nm / N_XCD);
         }
         return;
@@ -773,7 +773,7 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
         if (k < n_pieces) {
             const int x0 = (int)(k * P - w0);
             const int xb = (int)((k * P + P < n ? k * P + P : n) - w0);
-            wrote0 = walk_long<D, BF16, MEAN, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
+            wrote0 = walk_long<D, BF16, MEAN, ONCE, NMASK>(a, s_keys, s_vals, s_head, wn, k, x0, xb, li);
             // no head in [x0, xb]: the segment at the piece's start fills the
             // piece and goes on into the next one
             spans = k + 1 < n_pieces && next_head<NMASK>(s_head, x0 - 1, wn) > xb;
@@ -947,11 +947,21 @@ int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     const int cblocks = fill_blocks(n_pieces, 1, 2048 * 512 / CB);
     {
         TraceScope ts(RSE_K_SEG_UPDATE, s);
-        if (a.mean)
-            hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, true>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, false>), dim3((unsigned)work_blocks), dim3(G::BLOCK), 0, s,
-                               a);
+        // With no more lookups than bags (one-hot batches), a gradient row is
+        // read about once, like every touched row: the update then reads
+        // and writes both with the nontemporal hint, so that they stream
+        // through the caches and leave in place the lines that are read
+        // again, such as the sorted pairs (click-log update 0.29 -> 0.27 ms,
+        // step 0.60 -> 0.56 ms).  With longer bags a gradient row is read
+        // once per lookup and should stay cached between its reads.
+        const dim3 grid((unsigned)work_blocks), block(G::BLOCK);
+        if (a.n <= (int64_t)a.n_tables * a.batch) {
+            if (a.mean) hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, true, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, false, true>), grid, block, 0, s, a);
+        } else {
+            if (a.mean) hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, true, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_seg_work<D, BF16, OPT, false, false>), grid, block, 0, s, a);
+        }
     }
     {
         TraceScope ts(RSE_K_COMBINE, s);

@@ -74,6 +74,25 @@ __device__ __forceinline__ u32x4 gload_u4(const void* p) { return *(const RSE_GL
 __device__ __forceinline__ f32x4 gload_f4(const void* p) { return *(const RSE_GLOBAL f32x4*)p; }
 __device__ __forceinline__ void gstore_u4(void* p, u32x4 v) { *(RSE_GLOBAL u32x4*)p = v; }
 __device__ __forceinline__ void gstore_f4(void* p, f32x4 v) { *(RSE_GLOBAL f32x4*)p = v; }
+// The same with the nontemporal hint when NT: the access streams through the
+// caches (for data read or written once, so that it does not displace lines
+// that are read again).
+template <bool NT> __device__ __forceinline__ u32x4 gload_u4x(const void* p) {
+    if (NT) return __builtin_nontemporal_load((const RSE_GLOBAL u32x4*)p);
+    return *(const RSE_GLOBAL u32x4*)p;
+}
+template <bool NT> __device__ __forceinline__ f32x4 gload_f4x(const void* p) {
+    if (NT) return __builtin_nontemporal_load((const RSE_GLOBAL f32x4*)p);
+    return *(const RSE_GLOBAL f32x4*)p;
+}
+template <bool NT> __device__ __forceinline__ void gstore_u4x(void* p, u32x4 v) {
+    if (NT) __builtin_nontemporal_store(v, (RSE_GLOBAL u32x4*)p);
+    else *(RSE_GLOBAL u32x4*)p = v;
+}
+template <bool NT> __device__ __forceinline__ void gstore_f4x(void* p, f32x4 v) {
+    if (NT) __builtin_nontemporal_store(v, (RSE_GLOBAL f32x4*)p);
+    else *(RSE_GLOBAL f32x4*)p = v;
+}
 
 // Everything a kernel needs to address rows (passed by value).  Kernels on
 // the hot path stage the chunk-pointer table in LDS (stage_chunks) so that a

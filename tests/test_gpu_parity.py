@@ -207,6 +207,20 @@ def test_update_variants(optim, wdtype):
     run_steps(cfg, 3)
 
 
+@pytest.mark.parametrize("optim", [0, 1, 2])
+@pytest.mark.parametrize("wdtype", [0, 1])
+@pytest.mark.parametrize("pooling", [0, 1])
+def test_update_read_once_batches(optim, wdtype, pooling):
+    """Batches with no more lookups than bags (bags of 0 or 1 lookups) take
+    the update's streaming path (gradient rows and touched rows read and
+    written with the nontemporal hint): every optimizer x storage type x
+    pooling, with Zipf-hot rows whose segments span many pieces."""
+    cfg = synth.config(2, n_tables=3, batch=4096, dim=32, wdtype=wdtype, optim=optim,
+                       lr=[0.05, 0.01, 1e-3][optim], cardinality=("fixed", 3000), bag=("uniform", 0, 1),
+                       pooling=pooling)
+    run_steps(cfg, 2)
+
+
 @pytest.mark.parametrize("which", ["one_hot", "short_bags", "long_bags"])
 def test_global_chunk_table_path(which):
     """Blocks of more than 512 chunks (16-row chunks here) address rows
