@@ -49,11 +49,10 @@ constexpr uint32_t SIDE_MARK = 0xFFFFFFFFu;   // slot index meaning "side slot"
 
 // Workspace of one call.
 struct Ws {
-    unsigned long long* ctr;   // [0] misses [1] overflow [2] bad input [3] ok
+    unsigned long long* ctr;   // [0] any miss [1] overflow [2] bad input [3] ok
                                // [4] rows_used before [5] new keys [6] status code
                                // [7] free-list head before [8] rows taken from it
                                // [9] admission candidates [10] admitted lookups
-    uint32_t* miss_list;       // lookup indices that missed (any order)
     uint32_t* slot_of;         // per lookup: claimed slot (SIDE_MARK for the side slot)
     uint32_t* flag;            // per lookup: 0 hit, 1 pending, 2 first sight
     uint32_t* tile_sum;        // per scan tile
@@ -72,7 +71,6 @@ Ws carve(void* base, int64_t n_ids, size_t* total) {
     const size_t n = (size_t)(n_ids > 0 ? n_ids : 1);
     const size_t tiles = (n + SCAN_TILE - 1) / SCAN_TILE;
     w.ctr = c.take<unsigned long long>(32);
-    w.miss_list = c.take<uint32_t>(n);
     w.slot_of = c.take<uint32_t>(n);
     w.flag = c.take<uint32_t>(n);
     w.tile_sum = c.take<uint32_t>(tiles + 1);
@@ -261,6 +259,8 @@ __device__ __forceinline__ void probe_full(const ProbeArgs& a, int64_t i, uint64
 __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
     latency_bound_priority();
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    __shared__ int s_any_miss;
+    if (threadIdx.x == 0) s_any_miss = 0;         // ordered by the barriers in load_bounds
     const bool ok_bounds = load_bounds(sb, a.bounds, a.stride, a.n_tables, a.n_ids);
     if (!ok_bounds) {
         if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.ctr[2] = 1;
@@ -352,16 +352,10 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
             uint64_t val = 0;
             uint32_t slot_idx = 0;
             if (has) probe_full(a, ir, key_r, region_r, key_r == EMPTY_KEY, sub, gshift, kind, val, slot_idx);
-            // write results (one lane per group) and append misses to the list
+            // write results (one lane per group); a miss is left pending,
+            // flagged for the later kernels, which find it by its flag
             const bool leader = has && sub == 0;
-            const bool is_miss = leader && kind == 1;
-            const unsigned long long mm = __ballot(is_miss);
-            unsigned long long pos0 = 0;
-            if (mm) {
-                if (lane == __ffsll((long long)mm) - 1)
-                    pos0 = atomicAdd(&a.ws.ctr[0], (unsigned long long)__popcll(mm));
-                pos0 = __shfl(pos0, __ffsll((long long)mm) - 1, WAVE);
-            }
+            if (leader && kind == 1) s_any_miss = 1;
             if (a.collect) wave_append(leader && kind == 2, (uint32_t)ir, &a.ws.ctr[9], a.ws.cand);
             if (leader) {
                 if (kind == 0) {
@@ -369,8 +363,6 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
                     a.ws.flag[ir] = 0;
                     stamp_row(a.stamps, a.n_stamps, a.clock, val);
                 } else if (kind == 1) {
-                    const unsigned long long below = mm & ((1ull << lane) - 1);
-                    a.ws.miss_list[pos0 + __popcll(below)] = (uint32_t)ir;
                     a.ws.slot_of[ir] = slot_idx;
                     a.ws.flag[ir] = 1;
                     a.row_off[ir] = -1;
@@ -382,6 +374,11 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
             }
         }
     }
+    // One store per block that saw a miss, instead of a global atomic per
+    // wave: same-address atomics from every CU serialize, and with a few
+    // misses in most waves they dominated the kernel.
+    __syncthreads();
+    if (threadIdx.x == 0 && s_any_miss) a.ws.ctr[0] = 1;
 }
 
 // ----------------------------------------------------------- mark heads --
@@ -405,50 +402,57 @@ struct MarkArgs {
     int64_t stride;
     int32_t n_tables;
     int32_t pad;
+    int64_t n_ids;
     Ws ws;
 };
 
-// A pending lookup is the first sight of its key iff the slot's pending value
-// names it.  First sights are counted per region for the load check, and per
-// tile of SCAN_TILE lookups for the ranks (one atomic add per tile per wave:
-// a wave's entries of the miss list come from few tiles).
-__global__ void k_mark(MarkArgs a) {
+// One block per tile of SCAN_TILE lookups (16 per thread, as in
+// k_rank_commit).  A pending lookup (flag 1) is the first sight of its key
+// iff the slot's pending value names it.  The block writes its tile's count
+// of first sights (no atomics: the tile is the block's) and adds its
+// per-region counts to the regions' totals for the load check, one atomic per
+// region present in the tile (usually one: lookups are table-major).
+__global__ __launch_bounds__(256) void k_mark(MarkArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
-    __shared__ uint32_t s_new[RSE_MAX_TABLES];   // per-region first sights of this block
-    const unsigned long long n_miss = a.ws.ctr[0];
-    if (n_miss == 0) return;
+    __shared__ uint32_t s_new[RSE_MAX_TABLES];   // per-region first sights of this tile
+    __shared__ uint32_t wsum[4];
+    if (a.ws.ctr[0] == 0) return;
     for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
     for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x) s_new[r] = 0;
     __syncthreads();
-    for (unsigned long long q = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_miss;
-         q += (unsigned long long)gridDim.x * blockDim.x) {
-        const uint32_t i = a.ws.miss_list[q];
-        const uint32_t s = a.ws.slot_of[i];
-        int region;
-        uint64_t v;
-        if (s == SIDE_MARK) {
-            region = a.merged ? 0 : table_of(sb, a.n_tables, i);
-            v = a.dir[region].side_val;
-        } else {
-            region = region_of_slot(a.dir, a.n_regions, s);
-            v = a.slots[s].val;
-        }
-        const bool first = v == PENDING_BASE + (uint64_t)i;
-        if (first) {
+    // The flags and claimed slots of the thread's 16 lookups are read
+    // together, then the slot values of the pending ones (the others read
+    // slot 0, masked out), so a wave waits for two round trips however many
+    // of its lookups are pending.
+    const int64_t i0 = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * 16;
+    uint32_t f[16], sl[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const bool in = i0 + k < a.n_ids;
+        f[k] = in ? a.ws.flag[i0 + k] : 0u;
+        sl[k] = in ? a.ws.slot_of[i0 + k] : 0u;
+    }
+    uint64_t sv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sv[k] = a.slots[f[k] == 1 && sl[k] != SIDE_MARK ? sl[k] : 0].val;
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (f[k] != 1) continue;
+        const int64_t i = i0 + k;
+        // the lookup's region, as the probe formed it: its table, or 0 when merged
+        const int region = a.merged ? 0 : table_of(sb, a.n_tables, i);
+        const uint64_t v = sl[k] == SIDE_MARK ? a.dir[region].side_val : sv[k];
+        if (v == PENDING_BASE + (uint64_t)i) {
             a.ws.flag[i] = 2;
             atomicAdd(&s_new[region], 1u);
-        }
-        const uint32_t tile = i / SCAN_TILE;
-        unsigned long long pend = __ballot(first);
-        while (pend) {
-            const int src = __ffsll((long long)pend) - 1;
-            const uint32_t tl = __shfl(tile, src, WAVE);
-            const unsigned long long same = __ballot(first && tile == tl) & pend;
-            if (lane_id() == src) atomicAdd(&a.ws.tile_sum[tl], (uint32_t)__popcll(same));
-            pend &= ~same;
+            ++c;
         }
     }
+    for (int o = WAVE / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, WAVE);
+    if (lane_id() == 0) wsum[threadIdx.x >> 6] = c;
     __syncthreads();
+    if (threadIdx.x == 0) a.ws.tile_sum[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     for (int r = threadIdx.x; r < a.n_regions; r += blockDim.x)
         if (s_new[r]) atomicAdd((unsigned long long*)&a.dir[r].new_keys, (unsigned long long)s_new[r]);
 }
@@ -739,31 +743,34 @@ struct FinishArgs {
     int64_t n_stamps;
     uint32_t clock;
     int32_t pad2;
+    int64_t n_ids;
     Ws ws;
 };
 
-// One grid-stride range over two kinds of items: first every pending lookup
-// (it reads its key's final offset, or -1 if the call did not commit, and
-// stamps the row), then every 16 bytes of the new rows (weights from the key
+// One grid-stride range over two kinds of items: first every lookup, of
+// which the pending ones (flag 1 or 2) read their key's final offset, or -1
+// if the call did not commit, and stamp the row; then every 16 bytes of the
+// new rows (weights from the key
 // hash, state zero; recycled rows come from the ascending free list and the
 // rest are consecutive, so the writes are mostly contiguous).
 template <bool BF16>
 __global__ void k_finish(FinishArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
-    const uint64_t n_miss = a.ws.ctr[0];
-    if (n_miss == 0) return;
+    if (a.ws.ctr[0] == 0) return;
     for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
     __syncthreads();
     const bool ok = a.ws.ctr[3] != 0;
     const uint64_t n_new = ok ? a.ws.ctr[5] : 0;
+    const uint64_t n_look = (uint64_t)a.n_ids;      // lookups scanned for pending ones
     const int64_t q_per_row = a.row_bytes / 16;
     const int64_t w_q = (int64_t)a.dim * (BF16 ? 2 : 4) / 16;   // 16-byte units of weights
     const int per_q = BF16 ? 8 : 4;
-    const uint64_t total = n_miss + n_new * (uint64_t)q_per_row;
+    const uint64_t total = n_look + n_new * (uint64_t)q_per_row;
     for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (uint64_t)gridDim.x * blockDim.x) {
-        if (e < n_miss) {
-            const uint32_t i = a.ws.miss_list[e];
+        if (e < n_look) {
+            const uint32_t i = (uint32_t)e;
+            if (a.ws.flag[i] == 0) continue;
             int64_t v = -1;
             if (ok) {
                 const uint32_t s = a.ws.slot_of[i];
@@ -778,7 +785,7 @@ __global__ void k_finish(FinishArgs a) {
             a.row_off[i] = v;
             continue;
         }
-        const uint64_t ee = e - n_miss;
+        const uint64_t ee = e - n_look;
         const uint64_t r = ee / (uint64_t)q_per_row;
         const int64_t qi = (int64_t)(ee - r * (uint64_t)q_per_row);
         char* row = a.rv.row((int64_t)new_row_of(a.ws, a.free_list, r));
@@ -1389,10 +1396,11 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     ma.stride = stride;
     ma.n_tables = n_tables;
     ma.pad = 0;
+    ma.n_ids = n_ids;
     ma.ws = ws;
-    hipLaunchKernelGGL(k_mark, dim3(miss_blocks), dim3(256), 0, s, ma);
-
     const dim3 tiles_grid((unsigned)(n_tiles > 0 ? n_tiles : 1));
+    hipLaunchKernelGGL(k_mark, tiles_grid, dim3(256), 0, s, ma);
+
     DecideArgs da;
     da.dir = pa.dir;
     da.n_regions = map->n_tables;
@@ -1439,6 +1447,7 @@ int find_or_insert_impl(rse_idmap* map, rse_blocks* blocks, const int64_t* d_ids
     fa.n_stamps = map->n_stamps;
     fa.clock = map->clock;
     fa.pad2 = 0;
+    fa.n_ids = n_ids;
     fa.ws = ws;
     const int64_t finish_work = n_ids * (1 + blocks->row_bytes / 16);
     const dim3 finish_grid(fill_blocks(finish_work, 256, 8192));
