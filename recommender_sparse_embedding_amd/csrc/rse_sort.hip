@@ -9,9 +9,9 @@
 // so 26-bit row keys take three passes); the digit histograms of every pass
 // are computed beforehand by the pair-building kernel.  A pass runs a bounded number of blocks; each
 // repeatedly:
-//   1. takes the next tile (4096 pairs) from an atomic counter, so every tile
+//   1. takes the next tile (8192 pairs) from an atomic counter, so every tile
 //      it may wait on belongs to a block that is already running;
-//   2. ranks the tile's keys stably: each wave owns 512 consecutive pairs
+//   2. ranks the tile's keys stably: each wave owns 1024 consecutive pairs
 //      and walks them 64 at a time, building a digit-match mask per lane from
 //      one ballot per digit bit and keeping wave-private running counts in
 //      LDS, so no block barrier is needed per row;
@@ -31,9 +31,9 @@ using namespace rse_host;
 namespace {
 
 constexpr int SB = 512;                         // threads per sort block
-constexpr int ITEMS = SORT_TILE / SB;           // 8 pairs per thread
+constexpr int ITEMS = SORT_TILE / SB;           // 16 pairs per thread
 constexpr int SWAVES = SB / WAVE;
-constexpr int PER_WAVE = SORT_TILE / SWAVES;    // 512 consecutive pairs per wave
+constexpr int PER_WAVE = SORT_TILE / SWAVES;    // 1024 consecutive pairs per wave
 constexpr uint32_t ST_AGG = 1u << 30;           // tile count published
 constexpr uint32_t ST_INC = 2u << 30;           // inclusive prefix published
 constexpr uint32_t ST_VAL = (1u << 30) - 1u;
