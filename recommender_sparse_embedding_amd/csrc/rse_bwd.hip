@@ -805,7 +805,8 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
 // One block per owner (grid-stride).  The pieces a long segment covers are
 // its head's piece k0 (partial in carry slot 1) and the following pieces
 // k0+1..k1 whose first key is still the segment's; they form a prefix, so
-// block-wide counts over CB_SEARCH x block size pieces at a time find k1.
+// block-wide counts over combine_search x block size pieces at a time find
+// k1.
 // The work kernel has added
 // the slot-0 partials of each of its windows' runs into the run's first piece:
 // k0+1 and every multiple of its GPB in (k0+1, k1].  Those partials are added
@@ -815,15 +816,20 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
 // address is read from the global chunk table (one row per block, nothing
 // staged in LDS).  4 groups per block (64 to 256 threads): small blocks, so
 // that every owner's block is resident at once and the kernel takes about
-// one pass of its few dependent reads; each thread checks CB_SEARCH pieces
-// per round of the end search, with all of their loads in flight (measured
-// against 16 groups and one piece per thread: click-log step 0.548-0.569 ->
-// 0.534-0.537 ms; merged and sequence workloads unchanged).
+// one pass of its few dependent reads.  A round of the end search still
+// checks as many pieces as a block of 16 groups would (64 to 512), each
+// thread taking combine_search of them with all of their loads in flight
+// (more per round only reads past the end of the typical long segment).
+// Measured against 16 groups: click-log step 0.548-0.569 -> 0.534-0.537 ms.
 constexpr int CB_GROUPS = 4;
-constexpr int CB_SEARCH = 4;
 template <int D, bool BF16>
 constexpr int combine_block() {
     return CB_GROUPS * Geo<D, BF16>::LPR < 64 ? 64 : CB_GROUPS * Geo<D, BF16>::LPR;
+}
+template <int D, bool BF16>
+constexpr int combine_search() {
+    constexpr int wide = 16 * Geo<D, BF16>::LPR < 64 ? 64 : (16 * Geo<D, BF16>::LPR > 512 ? 512 : 16 * Geo<D, BF16>::LPR);
+    return wide / combine_block<D, BF16>() > 1 ? wide / combine_block<D, BF16>() : 1;
 }
 
 template <int D, bool BF16, int OPT>
@@ -831,6 +837,7 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
     using G = Geo<D, BF16>;
     constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = combine_block<D, BF16>(), GPB = BLOCK / LPR;
     constexpr int U = 4;
+    constexpr int CB_SEARCH = combine_search<D, BF16>();
     __shared__ double s_part[GPB][D];
     if (a.ctr->bad || *a.sort_err) {
         if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_unique = 0;    // nothing was updated
