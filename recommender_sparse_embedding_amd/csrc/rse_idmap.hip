@@ -114,6 +114,36 @@ __device__ __forceinline__ void wave_append(bool me, uint32_t value, unsigned lo
     if (me) list[pos0 + __popcll(mm & ((1ull << lane_id()) - 1))] = value;
 }
 
+// Block-buffered append: a wave reserves room in the block's LDS buffer with
+// an LDS atomic and writes its entries there; entries past the buffer go to
+// the list directly (wave_append).  The block flushes its buffer with one
+// global atomic at its end (block_append_flush), so a kernel whose waves
+// nearly all append pays one same-address atomic per block, not per wave.
+constexpr int APPEND_BUF = 2048;
+
+__device__ __forceinline__ void block_append(bool me, uint32_t value, uint32_t* s_buf, uint32_t* s_n,
+                                             unsigned long long* counter, uint32_t* list) {
+    const unsigned long long mm = __ballot(me);
+    if (!mm) return;
+    const int leader = __ffsll((long long)mm) - 1;
+    uint32_t p0 = 0;
+    if (lane_id() == leader) p0 = atomicAdd(s_n, (uint32_t)__popcll(mm));
+    p0 = __shfl(p0, leader, WAVE);
+    const uint32_t p = p0 + (uint32_t)__popcll(mm & ((1ull << lane_id()) - 1));
+    if (me && p < (uint32_t)APPEND_BUF) s_buf[p] = value;
+    wave_append(me && p >= (uint32_t)APPEND_BUF, value, counter, list);
+}
+
+// All threads of the block, after every block_append of the block and a
+// barrier.
+__device__ __forceinline__ void block_append_flush(const uint32_t* s_buf, uint32_t s_n, unsigned long long* s_base,
+                                                   unsigned long long* counter, uint32_t* list) {
+    const uint32_t n = s_n < (uint32_t)APPEND_BUF ? s_n : (uint32_t)APPEND_BUF;
+    if (threadIdx.x == 0) *s_base = n ? atomicAdd(counter, (unsigned long long)n) : 0;
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < n; k += blockDim.x) list[*s_base + k] = s_buf[k];
+}
+
 __device__ __forceinline__ void stamp_row(uint32_t* stamps, int64_t n_stamps, uint32_t clock, uint64_t off) {
     if (stamps && off < (uint64_t)n_stamps) stamps[off] = clock;
 }
@@ -260,7 +290,13 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
     latency_bound_priority();
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
     __shared__ int s_any_miss;
-    if (threadIdx.x == 0) s_any_miss = 0;         // ordered by the barriers in load_bounds
+    __shared__ uint32_t s_cand[APPEND_BUF];        // admission candidates of this block
+    __shared__ uint32_t s_ncand;
+    __shared__ unsigned long long s_cbase;
+    if (threadIdx.x == 0) {                        // ordered by the barriers in load_bounds
+        s_any_miss = 0;
+        s_ncand = 0;
+    }
     const bool ok_bounds = load_bounds(sb, a.bounds, a.stride, a.n_tables, a.n_ids);
     if (!ok_bounds) {
         if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.ctr[2] = 1;
@@ -335,7 +371,7 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
             if (res == RES_BAD) a.ws.ctr[2] = 1;
             if (res < PENDING_BASE) stamp_row(a.stamps, a.n_stamps, a.clock, res);
         }
-        if (a.collect) wave_append(res == RES_ABSENT, (uint32_t)i, &a.ws.ctr[9], a.ws.cand);
+        if (a.collect) block_append(res == RES_ABSENT, (uint32_t)i, s_cand, &s_ncand, &a.ws.ctr[9], a.ws.cand);
 
         // (3) the full probe for the rest: group g takes the g-th lowest
         uint64_t slow = __ballot(res == RES_SLOW);
@@ -356,7 +392,8 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
             // flagged for the later kernels, which find it by its flag
             const bool leader = has && sub == 0;
             if (leader && kind == 1) s_any_miss = 1;
-            if (a.collect) wave_append(leader && kind == 2, (uint32_t)ir, &a.ws.ctr[9], a.ws.cand);
+            if (a.collect)
+                block_append(leader && kind == 2, (uint32_t)ir, s_cand, &s_ncand, &a.ws.ctr[9], a.ws.cand);
             if (leader) {
                 if (kind == 0) {
                     a.row_off[ir] = (int64_t)val;
@@ -379,6 +416,7 @@ __global__ __launch_bounds__(PROBE_BLOCK) void k_probe(ProbeArgs a) {
     // misses in most waves they dominated the kernel.
     __syncthreads();
     if (threadIdx.x == 0 && s_any_miss) a.ws.ctr[0] = 1;
+    if (a.collect) block_append_flush(s_cand, s_ncand, &s_cbase, &a.ws.ctr[9], a.ws.cand);
 }
 
 // ----------------------------------------------------------- mark heads --
@@ -518,9 +556,13 @@ __global__ void k_admit_count(AdmitArgs a, int32_t undo) {
 // Lists the candidates whose estimate reaches the threshold.
 __global__ void k_admit_pick(AdmitArgs a) {
     __shared__ int64_t sb[RSE_MAX_TABLES + 1];
+    __shared__ uint32_t s_buf[APPEND_BUF];
+    __shared__ uint32_t s_n;
+    __shared__ unsigned long long s_base;
     const unsigned long long n = a.ws.ctr[9];
     if (n == 0 || a.ws.ctr[2] != 0) return;
     for (int t = threadIdx.x; t <= a.n_tables; t += blockDim.x) sb[t] = a.bounds[(int64_t)t * a.stride];
+    if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
     for (unsigned long long q0 = (unsigned long long)blockIdx.x * blockDim.x; q0 < n;
          q0 += (unsigned long long)gridDim.x * blockDim.x) {
@@ -537,8 +579,10 @@ __global__ void k_admit_pick(AdmitArgs a) {
                 est = min(est, a.sketch[(int64_t)j * a.width + sketch_cell(key, region, a.salt[j], a.width)]);
             pick = est >= a.threshold;
         }
-        wave_append(pick, i, &a.ws.ctr[10], a.ws.admitted);
+        block_append(pick, i, s_buf, &s_n, &a.ws.ctr[10], a.ws.admitted);
     }
+    __syncthreads();
+    block_append_flush(s_buf, s_n, &s_base, &a.ws.ctr[10], a.ws.admitted);
 }
 
 constexpr int DECIDE_BLOCK = 256;   // small, so that it finds room beside other streams' kernels
