@@ -59,6 +59,74 @@ def _bytes(n: int, device) -> torch.Tensor:
     return t
 
 
+# Large chunks of rows are allocated physically contiguous
+# (hipExtMallocWithFlags with hipDeviceMallocContiguous): the GPU then maps
+# them with its largest page fragments, and random row accesses over tens of
+# GB miss the address-translation caches less (click-log step, 57 GB table in
+# 16 GB chunks: 0.548-0.568 ms with torch's allocations, 0.537-0.544 ms with
+# contiguous ones).  Where the driver cannot place one, torch allocates it.
+_HIP_DEVICE_MALLOC_CONTIGUOUS = 0x4
+CONTIGUOUS_MIN_BYTES = 1 << 28
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime torch has loaded (looked up by its soname, so this is
+    the same library instance, not a second runtime)."""
+    global _hip_rt
+    if _hip_rt is None:
+        h = ctypes.CDLL("libamdhip64.so.7")
+        h.hipExtMallocWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        h.hipExtMallocWithFlags.restype = ctypes.c_int
+        h.hipFree.argtypes = [ctypes.c_void_p]
+        h.hipFree.restype = ctypes.c_int
+        h.hipGetLastError.argtypes = []
+        h.hipGetLastError.restype = ctypes.c_int
+        _hip_rt = h
+    return _hip_rt
+
+
+class _ContiguousAlloc:
+    """One hipExtMallocWithFlags allocation, seen by torch as a uint8 tensor
+    through __cuda_array_interface__; the tensor keeps this owner alive, and
+    the memory is freed with the last reference."""
+
+    def __init__(self, nbytes: int, device: torch.device):
+        self.nbytes, self.device, self.ptr = int(nbytes), device, None
+        p = ctypes.c_void_p()
+        with torch.cuda.device(device):
+            rc = _hip().hipExtMallocWithFlags(ctypes.byref(p), self.nbytes, _HIP_DEVICE_MALLOC_CONTIGUOUS)
+            if rc != 0 or not p.value:
+                _hip().hipGetLastError()      # leave no error for the library's next launch check
+                raise MemoryError(f"hipExtMallocWithFlags({self.nbytes}, contiguous) returned {rc}")
+        self.ptr = p.value
+
+    @property
+    def __cuda_array_interface__(self):
+        return {"shape": (self.nbytes,), "typestr": "|u1", "data": (self.ptr, False), "version": 2}
+
+    def __del__(self):
+        if self.ptr:
+            with torch.cuda.device(self.device):
+                _hip().hipFree(self.ptr)
+            self.ptr = None
+
+
+def _chunk_bytes(n: int, device) -> torch.Tensor:
+    """Device memory of one chunk: physically contiguous when large (torch's
+    allocator if that fails)."""
+    device = torch.device(device)
+    if n >= CONTIGUOUS_MIN_BYTES and device.type == "cuda":
+        try:
+            owner = _ContiguousAlloc(n, device)
+        except MemoryError:
+            return _bytes(n, device)
+        t = torch.as_tensor(owner, device=device)
+        assert t.data_ptr() == owner.ptr and t.numel() == n and t.data_ptr() % 256 == 0
+        return t
+    return _bytes(n, device)
+
+
 def status_str(code: int) -> str:
     return lib.rse_status_str(code).decode()
 
@@ -118,9 +186,11 @@ class EmbeddingBlocks:
         return cap.value
 
     def grow(self, n_chunks: int = 1, stream=None):
-        """Allocate n_chunks chunks with torch and register them (blocks_grow)."""
+        """Allocate n_chunks chunks and register them (blocks_grow).  Chunks of
+        CONTIGUOUS_MIN_BYTES or more are physically contiguous allocations
+        where the driver can place them, the rest come from torch."""
         for _ in range(n_chunks):
-            chunk = _bytes(self.rows_per_chunk * self.row_bytes, self.device)
+            chunk = _chunk_bytes(self.rows_per_chunk * self.row_bytes, self.device)
             blocks_grow(self, chunk, stream)
         return self
 

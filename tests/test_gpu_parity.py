@@ -239,6 +239,35 @@ def test_global_chunk_table_path(which):
     assert len(gpu.blocks.chunks) > 512
 
 
+def test_contiguous_chunks():
+    """Chunks of 256 MiB or more come from physically contiguous device
+    allocations (outside torch's allocator) where the driver can place them:
+    the same parity bar on a click-log twin whose 512 MiB chunks take that
+    path, and the memory is returned when the blocks go."""
+    import recommender_sparse_embedding_amd as rse
+
+    import gc
+
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()      # torch's cached blocks are not counted either side
+    free0 = torch.cuda.mem_get_info()[0]
+    torch_before = torch.cuda.memory_allocated()
+    cfg = synth.config(2, n_tables=8, batch=2048, cardinality=("loguniform", 10, 200_000))
+    gpu, _ = run_steps(cfg, 2, rows_per_chunk_log2=19)
+    chunk_bytes = gpu.blocks.rows_per_chunk * gpu.blocks.row_bytes
+    assert chunk_bytes >= rse.CONTIGUOUS_MIN_BYTES
+    assert all(c.numel() == chunk_bytes for c in gpu.blocks.chunks)
+    # the chunks are not torch allocations
+    assert torch.cuda.memory_allocated() - torch_before < chunk_bytes
+    n = len(gpu.blocks.chunks)
+    del gpu
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    assert torch.cuda.mem_get_info()[0] > free0 - chunk_bytes // 4, f"{n} chunks not returned"
+
+
 def test_config1_multi_hot_sgd_full():
     """8 tables, dim 16, batch 1024, bags U[1,8], Zipf(1.05) over 1e5 keys,
     sum-of-squares loss, SGD 0.1, tables start empty: 10 free-running steps."""
