@@ -60,11 +60,11 @@ def _bytes(n: int, device) -> torch.Tensor:
 
 
 # Large chunks of rows are allocated physically contiguous
-# (hipExtMallocWithFlags with hipDeviceMallocContiguous): the GPU then maps
-# them with its largest page fragments, and random row accesses over tens of
-# GB miss the address-translation caches less (click-log step, 57 GB table in
-# 16 GB chunks: 0.548-0.568 ms with torch's allocations, 0.537-0.544 ms with
-# contiguous ones).  Where the driver cannot place one, torch allocates it.
+# (hipExtMallocWithFlags with hipDeviceMallocContiguous), which the GPU maps
+# with its largest page fragments.  Click-log step, 57 GB table in 16 GB
+# chunks, 7 processes each: 0.541-0.569 ms (mean 0.556) with torch's
+# allocations, 0.536-0.548 ms (mean 0.541) with contiguous ones.  Where the
+# driver cannot place one, torch allocates it.
 _HIP_DEVICE_MALLOC_CONTIGUOUS = 0x4
 CONTIGUOUS_MIN_BYTES = 1 << 28
 _hip_rt = None
@@ -112,8 +112,8 @@ class _ContiguousAlloc:
             self.ptr = None
 
 
-def _chunk_bytes(n: int, device) -> torch.Tensor:
-    """Device memory of one chunk: physically contiguous when large (torch's
+def _large_bytes(n: int, device) -> torch.Tensor:
+    """Device memory of a chunk: physically contiguous when large (torch's
     allocator if that fails)."""
     device = torch.device(device)
     if n >= CONTIGUOUS_MIN_BYTES and device.type == "cuda":
@@ -190,7 +190,7 @@ class EmbeddingBlocks:
         CONTIGUOUS_MIN_BYTES or more are physically contiguous allocations
         where the driver can place them, the rest come from torch."""
         for _ in range(n_chunks):
-            chunk = _chunk_bytes(self.rows_per_chunk * self.row_bytes, self.device)
+            chunk = _large_bytes(self.rows_per_chunk * self.row_bytes, self.device)
             blocks_grow(self, chunk, stream)
         return self
 
@@ -281,6 +281,8 @@ class IdMap:
         arr = (ctypes.c_int64 * len(slots))(*slots)
         sz = ctypes.c_size_t()
         check(lib.rse_idmap_mem_size(len(slots), arr, ctypes.byref(sz)), "rse_idmap_mem_size")
+        # torch's memory: with a physically contiguous map (tried) the
+        # click-log step was in its slower mode in about half of the runs
         self.mem = _bytes(sz.value, self.device)
         h = ctypes.c_void_p()
         check(lib.rse_idmap_create(ctypes.byref(h), _ptr(self.mem), sz.value, len(slots), arr, max_load,

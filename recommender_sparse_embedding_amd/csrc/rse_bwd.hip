@@ -19,7 +19,8 @@
 // 2..LONG_T lookups ("short"), or longer ("long", whose head is listed as
 // owner); the first two kinds go to lists.  The work kernel then runs three
 // kinds of blocks side by side:
-//   - long: the sorted lookups are cut into pieces of P = 64; each piece
+//   - long: the sorted lookups are cut into pieces of P = 32 or 64 lookups
+//     (32 for fp32 rows of dim 16 and less, 64 otherwise); each piece
 //     sums the part of a long segment it holds (at its start, continuing an
 //     earlier piece, and/or at its end, continuing past it) into a carry
 //     slot, 4-8 gradient rows in flight, in lookup order, in fp64;
@@ -43,7 +44,9 @@ using namespace rse_host;
 
 namespace {
 
-constexpr int P = 64;            // lookups per piece
+// Lookups per piece: Geo<D, BF16>::P (below), never less than P_MIN (the
+// workspace's carry slots are sized for P_MIN).
+constexpr int P_MIN = 32;
 // Longest segment reduced by one group.  At least P - 1, so that a longer
 // segment cannot lie strictly inside one piece (the long role handles the
 // segments at a piece's start and at its last head only).
@@ -117,6 +120,13 @@ struct Geo {
     static constexpr int LPR = D / VEC;
     static constexpr int BLOCK = (64 * LPR < 256) ? 64 * LPR : 256;
     static constexpr int GPB = BLOCK / LPR;      // pieces (groups) per block, <= 64
+    // Lookups per piece.  fp32 rows of at most 4 lanes (dim 16 and less)
+    // take 32: more, shorter pieces spread a small batch's hot-row gathers
+    // over more groups (multi-hot dim-16 update 0.032 -> 0.024 ms).  Other
+    // rows take 64 (measured with 32: bf16 dim-32 update +3.5%, click-log
+    // step +2%).
+    static constexpr int P = (!BF16 && LPR <= 4) ? 32 : 64;
+    static_assert(P >= P_MIN && LONG_T >= P - 1, "piece length");
     static constexpr int WIN = GPB * P + 2 * HALO;
     // gradient rows a group keeps in flight: 128 bytes per lane either way
     // (a bf16 row holds 8 elements per lane, so its fp32 gradient row takes
@@ -695,7 +705,7 @@ constexpr int singles_per_group() {
 template <int D, bool BF16, int OPT, bool MEAN, bool ONCE>
 __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
     using G = Geo<D, BF16>;
-    constexpr int LPR = G::LPR, GPB = G::GPB, WIN = G::WIN;
+    constexpr int LPR = G::LPR, GPB = G::GPB, WIN = G::WIN, P = G::P;
     constexpr int NMASK = (WIN + 63) / 64;
     __shared__ uint32_t s_keys[WIN];
     __shared__ uint32_t s_vals[WIN];
@@ -838,6 +848,7 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
     constexpr int VEC = G::VEC, LPR = G::LPR, BLOCK = combine_block<D, BF16>(), GPB = BLOCK / LPR;
     constexpr int U = 4;
     constexpr int CB_SEARCH = combine_search<D, BF16>();
+    constexpr int P = G::P;
     __shared__ double s_part[GPB][D];
     if (a.ctr->bad || *a.sort_err) {
         if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_unique = 0;    // nothing was updated
@@ -931,7 +942,7 @@ BwdWs carve(void* base, int64_t n_ids, int64_t n_bags, int32_t dim, size_t* tota
     Carver c(base);
     BwdWs w;
     const size_t n = (size_t)(n_ids > 0 ? n_ids : 1);
-    const size_t n_pieces = (n + P - 1) / P;
+    const size_t n_pieces = (n + P_MIN - 1) / P_MIN;    // carry slots for any piece length
     w.ctr = c.take<Ctr>(1);
     w.p0 = c.take<uint2>(n);
     w.p1 = c.take<uint2>(n);
@@ -948,7 +959,7 @@ BwdWs carve(void* base, int64_t n_ids, int64_t n_bags, int32_t dim, size_t* tota
 template <int D, bool BF16, int OPT>
 int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     using G = Geo<D, BF16>;
-    const int64_t n_pieces = (n_ids + P - 1) / P;
+    const int64_t n_pieces = (n_ids + G::P - 1) / G::P;
     // long pieces: one block per GPB pieces; one-lookup and short segments:
     // grid-stride pools (their counts are only known on the device), sized
     // for a few passes when one lookup in ~16 starts a segment
