@@ -240,8 +240,9 @@ def test_global_chunk_table_path(which):
 
 
 def test_contiguous_chunks():
-    """Chunks of 256 MiB or more come from physically contiguous device
-    allocations (outside torch's allocator) where the driver can place them:
+    """Chunks of 256 MiB or more, of rows that fill whole 128-byte lines,
+    come from physically contiguous device allocations (outside torch's
+    allocator) where the driver can place them:
     the same parity bar on a click-log twin whose 512 MiB chunks take that
     path, and the memory is returned when the blocks go."""
     import recommender_sparse_embedding_amd as rse
@@ -256,7 +257,7 @@ def test_contiguous_chunks():
     cfg = synth.config(2, n_tables=8, batch=2048, cardinality=("loguniform", 10, 200_000))
     gpu, _ = run_steps(cfg, 2, rows_per_chunk_log2=19)
     chunk_bytes = gpu.blocks.rows_per_chunk * gpu.blocks.row_bytes
-    assert chunk_bytes >= rse.CONTIGUOUS_MIN_BYTES
+    assert chunk_bytes >= rse.CONTIGUOUS_MIN_BYTES and gpu.blocks.row_bytes % 128 == 0
     assert all(c.numel() == chunk_bytes for c in gpu.blocks.chunks)
     # the chunks are not torch allocations
     assert torch.cuda.memory_allocated() - torch_before < chunk_bytes
