@@ -86,14 +86,30 @@ def _hip():
         h.hipFree.restype = ctypes.c_int
         h.hipGetLastError.argtypes = []
         h.hipGetLastError.restype = ctypes.c_int
+        h.hipGetDevice.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        h.hipGetDevice.restype = ctypes.c_int
+        h.hipSetDevice.argtypes = [ctypes.c_int]
+        h.hipSetDevice.restype = ctypes.c_int
         _hip_rt = h
     return _hip_rt
+
+
+def _free_contiguous(ptr: int, index: int):
+    """hipFree on the allocation's device (HIP calls only, so that it also
+    runs at interpreter exit)."""
+    h = _hip()
+    cur = ctypes.c_int(index)
+    h.hipGetDevice(ctypes.byref(cur))
+    h.hipSetDevice(index)
+    h.hipFree(ctypes.c_void_p(ptr))
+    h.hipSetDevice(cur.value)
 
 
 class _ContiguousAlloc:
     """One hipExtMallocWithFlags allocation, seen by torch as a uint8 tensor
     through __cuda_array_interface__; the tensor keeps this owner alive, and
-    the memory is freed with the last reference."""
+    the memory is freed with the last reference, or at interpreter exit
+    (weakref.finalize runs before modules are torn down)."""
 
     def __init__(self, nbytes: int, device: torch.device):
         self.nbytes, self.device, self.ptr = int(nbytes), device, None
@@ -104,16 +120,12 @@ class _ContiguousAlloc:
                 _hip().hipGetLastError()      # leave no error for the library's next launch check
                 raise MemoryError(f"hipExtMallocWithFlags({self.nbytes}, contiguous) returned {rc}")
         self.ptr = p.value
+        index = device.index if device.index is not None else torch.cuda.current_device()
+        self._free = weakref.finalize(self, _free_contiguous, p.value, index)
 
     @property
     def __cuda_array_interface__(self):
         return {"shape": (self.nbytes,), "typestr": "|u1", "data": (self.ptr, False), "version": 2}
-
-    def __del__(self):
-        if self.ptr:
-            with torch.cuda.device(self.device):
-                _hip().hipFree(self.ptr)
-            self.ptr = None
 
 
 def _chunk_bytes(n: int, row_bytes: int, device) -> torch.Tensor:
