@@ -372,14 +372,16 @@ def test_split_backward_overlapping_forward(which):
         run_steps(cfg, 3, split=True)
 
 
-@pytest.mark.parametrize("schedule", ["pipelined", "lookahead"])
+@pytest.mark.parametrize("schedule", ["pipelined", "lookahead", "lookahead3"])
 @pytest.mark.parametrize("which", ["click_log", "fresh_keys_adam"])
 def test_pipelined_next_find_overlaps_apply(which, schedule):
     """Two-stream schedules.  pipelined: the find and sort of batch s+1 on a
     second stream run while batch s's forward and apply run on the first (the
     forward of s+1 waits for both).  lookahead: the second stream sorts batch
     s+1 (found a step earlier) and then finds batch s+2 while batch s runs.
-    Every step matches the oracle run in plain order, including new keys
+    lookahead3: the same with the finds on a third stream, beside the sorts
+    (a sort waits for its batch's find, a find for the apply two batches
+    back).  Every step matches the oracle run in plain order, including new keys
     inserted while earlier batches' rows are being updated."""
     if which == "click_log":
         cfg = synth.config(2, batch=2048, cardinality=("loguniform", 10, 200_000))
@@ -398,6 +400,7 @@ def test_pipelined_next_find_overlaps_apply(which, schedule):
     dev = gpu.dev
     main = torch.cuda.current_stream(dev)
     side = torch.cuda.Stream(device=dev)
+    finder = torch.cuda.Stream(device=dev) if schedule == "lookahead3" else side
     inputs = []
     for s in range(steps):
         ids, bo = wl.batch_inputs(s)
@@ -417,13 +420,17 @@ def test_pipelined_next_find_overlaps_apply(which, schedule):
 
     def find(s):
         x = inputs[s]
+        if schedule == "lookahead3":
+            finder.wait_event(applied[s % 2])
         rse.idmap_find_or_insert(gpu.map, gpu.blocks, x["ids"], x["bo"], cfg.batch, cfg.n_tables, x["ro"], n_new,
-                                 ws=fws, stream=side)
-        found[s % 3].record(side)
+                                 ws=fws, stream=finder)
+        found[s % 3].record(finder)
 
     def prepare(s):
         x = inputs[s]
         side.wait_event(applied[s % 2])
+        if schedule == "lookahead3":
+            side.wait_event(found[s % 3])
         plans[s % 2] = rse.embedding_bag_bwd_prepare(gpu.blocks, x["ro"], x["bo"], cfg.n_tables, cfg.batch,
                                                      ws[s % 2], stream=side)
         fronted[s % 2].record(side)
@@ -440,11 +447,16 @@ def test_pipelined_next_find_overlaps_apply(which, schedule):
             if s + 1 < steps:
                 find(s + 1)
                 prepare(s + 1)
-        else:
+        elif schedule == "lookahead":
             if s + 1 < steps:
                 prepare(s + 1)
             if s + 2 < steps:
                 find(s + 2)
+        else:
+            if s + 2 < steps:
+                find(s + 2)
+            if s + 1 < steps:
+                prepare(s + 1)
         x = inputs[s]
         main.wait_event(found[s % 3])
         rse.embedding_bag_fwd(gpu.blocks, x["ro"], x["bo"], cfg.n_tables, cfg.batch, cfg.pooling, x["out"])
