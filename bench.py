@@ -235,7 +235,8 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     # to two batches ahead), the two lookahead calibration runs, the timed
     # run (two ahead), the traced run and the other lookahead (two ahead),
     # the other reference runs (one ahead)
-    n_finds = ((n_warm_sched + 1) * (warmup + 2) + 2 * (warmup + 2) + steps + 2
+    n_cal = max(3, warmup)
+    n_finds = ((n_warm_sched + 1) * (warmup + 2) + 2 * (n_cal + 2) + steps + 2
                + n_ref_sched * (n_ref + 1) + 2 * (n_ref + 2) + 4)
     n_batches = n_finds if distinct else max(3, args.batches)
 
@@ -485,7 +486,7 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     # The step's schedule: two streams, or three (finds beside the sorts)
     # where that is clearly faster, from one run of each after the warm-up;
     # the timed region then runs that schedule only.
-    cal = {name: timed(name, warmup)[0] for name in ("lookahead", "lookahead3")}
+    cal = {name: timed(name, n_cal)[0] for name in ("lookahead", "lookahead3")}
     sched = "lookahead3" if cal["lookahead3"] < 0.97 * cal["lookahead"] else "lookahead"
     other = "lookahead" if sched == "lookahead3" else "lookahead3"
 
@@ -567,7 +568,7 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
         "step_logical_bytes": int(logical),
         "step_logical_gbs": round(logical / (ms_step * 1e-3) / 1e9, 1),
         "schedule": sched,
-        "schedule_calibration_ms": {k: round(v / warmup, 4) for k, v in cal.items()},
+        "schedule_calibration_ms": {k: round(v / n_cal, 4) for k, v in cal.items()},
         "ms_per_step_by_schedule": ms_by,
         "host_enqueue_ms_per_step": {k: round(v, 4) for k, v in host_ms.items()},
         "roofline": roofline,
