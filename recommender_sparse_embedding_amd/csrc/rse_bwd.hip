@@ -90,6 +90,13 @@ struct Multi {                   // a segment of 2..LONG_T lookups
     uint32_t pad;
 };
 
+struct Owner {                   // a long segment (more than LONG_T lookups)
+    uint32_t head;               // position of its first lookup in the sorted order
+    uint32_t len;                // its length if the index kernel saw its end, else 0
+    uint32_t key;                // its row
+    uint32_t pad;
+};
+
 struct BwdArgs {
     RowsView rv;
     const uint2* pairs;          // sorted lookups: x = row, y = gradient row of its bag
@@ -105,7 +112,7 @@ struct BwdArgs {
     int32_t s_blocks;            // the next s_blocks one-lookup segments, the rest short ones
     Ctr* ctr;
     double* carry;               // [n_pieces][2][dim]
-    uint32_t* owners;            // head positions of long segments
+    Owner* owners;               // long segments
     uint2* singles;              // (row, gradient row) of one-lookup segments
     Multi* multis;
     int64_t* n_unique;
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
             const bool ends_here = e < wn || w1 == n;
             const int l = e - x;
             cls[u] = (!ends_here || l > LONG_T) ? 2 : (l == 1 ? 0 : 1);
-            len[u] = l;
+            len[u] = ends_here ? l : 0;      // a long segment's length only if it ends in the window
             cnt += 1ull << (16 * cls[u]);
         }
     }
@@ -556,7 +563,12 @@ __global__ __launch_bounds__(IX_BLOCK) void k_seg_index(BwdArgs a) {
             m.pad = 0;
             a.multis[pos[1]++] = m;
         } else if (cls[u] == 2) {
-            a.owners[pos[2]++] = p;
+            Owner ow;
+            ow.head = p;
+            ow.len = (uint32_t)len[u];
+            ow.key = s_keys[x];
+            ow.pad = 0;
+            a.owners[pos[2]++] = ow;
         }
     }
 }
@@ -812,25 +824,30 @@ __global__ __launch_bounds__((Geo<D, BF16>::BLOCK)) void k_seg_work(BwdArgs a) {
 }
 
 // ------------------------------------------------- long segment combine --
-// One block per owner (grid-stride).  The pieces a long segment covers are
-// its head's piece k0 (partial in carry slot 1) and the following pieces
-// k0+1..k1 whose first key is still the segment's; they form a prefix, so
-// block-wide counts over combine_search x block size pieces at a time find
-// k1.
-// The work kernel has added
-// the slot-0 partials of each of its windows' runs into the run's first piece:
-// k0+1 and every multiple of its GPB in (k0+1, k1].  Those partials are added
-// round-robin per group (U loads in flight, in list order) then in group
-// order, so the sum is the same on every run.  Block 0 also writes the
-// number of distinct rows (one-lookup + short + long segments).  The row
-// address is read from the global chunk table (one row per block, nothing
-// staged in LDS).  4 groups per block (64 to 256 threads): small blocks, so
-// that every owner's block is resident at once and the kernel takes about
-// one pass of its few dependent reads.  A round of the end search still
-// checks as many pieces as a block of 16 groups would (64 to 512), each
-// thread taking combine_search of them with all of their loads in flight
-// (more per round only reads past the end of the typical long segment).
-// Measured against 16 groups: click-log step 0.548-0.569 -> 0.534-0.537 ms.
+// The pieces a long segment covers are its head's piece k0 (partial in
+// carry slot 1) and the following pieces k0+1..k1 whose first position lies
+// in the segment.  The work kernel has added the slot-0 partials of each of
+// its windows' runs into the run's first piece: k0+1 and every multiple of
+// its GPB in (k0+1, k1].  Blocks take chunks of owners, one per group:
+//  - a segment whose length the index kernel saw (it ended inside the index
+//    window: nearly every segment of up to a few thousand lookups) is
+//    finished by its group alone: k1 follows from head and length, its row
+//    is requested with its first partials, the partials are added in list
+//    order (U loads in flight) and the row is updated;
+//  - the others (the hottest rows) are then taken one at a time by the
+//    whole block: k1 from block-wide counts over combine_search x block size
+//    piece heads at a time (the pieces of a segment form a prefix), the
+//    partials added round-robin per group (U loads in flight, in list
+//    order) then in group order, and the row updated by group 0.
+// Either way a segment's sum has one fixed order, the same on every run.
+// Block 0 also writes the number of distinct rows (one-lookup + short + long
+// segments).  Row addresses are read from the global chunk table.  A chunk
+// is one owner per group for rows of up to 8 lanes (a block of 16 groups
+// used to take one owner at a time, though most long segments have only 2-3
+// partials: merged-table combine 150 -> 58 us alone) and one owner per
+// block for wider rows (click-log and behaviour-sequence: their hottest
+// rows, of unknown length, would otherwise wait in line behind the other
+// owners of their block; sequence combine 15 -> 22 us with 4 per block).
 constexpr int CB_GROUPS = 4;
 template <int D, bool BF16>
 constexpr int combine_block() {
@@ -842,6 +859,11 @@ constexpr int combine_search() {
     return wide / combine_block<D, BF16>() > 1 ? wide / combine_block<D, BF16>() : 1;
 }
 
+template <int D, bool BF16>
+constexpr int combine_owners_per_block() {
+    return Geo<D, BF16>::LPR <= 8 ? combine_block<D, BF16>() / Geo<D, BF16>::LPR : 1;
+}
+
 template <int D, bool BF16, int OPT>
 __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs a) {
     using G = Geo<D, BF16>;
@@ -849,7 +871,10 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
     constexpr int U = 4;
     constexpr int CB_SEARCH = combine_search<D, BF16>();
     constexpr int P = G::P;
+    constexpr int64_t WG = G::GPB;          // the work kernel's pieces per window
+    constexpr int OPB = combine_owners_per_block<D, BF16>();
     __shared__ double s_part[GPB][D];
+    __shared__ int64_t s_coop[GPB];         // owners of the chunk left to the whole block
     if (a.ctr->bad || *a.sort_err) {
         if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_unique = 0;    // nothing was updated
         return;
@@ -860,67 +885,109 @@ __global__ __launch_bounds__((combine_block<D, BF16>())) void k_combine(BwdArgs 
     const int li = threadIdx.x % LPR;
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *a.n_unique = (int64_t)(a.ctr->n_single + a.ctr->n_multi + (unsigned long long)n_owners);
-    for (int64_t o = blockIdx.x; o < n_owners; o += gridDim.x) {
-        __syncthreads();       // s_part of the previous owner has been read
-        const int64_t h = a.owners[o];
-        const uint32_t key = a.pairs[h].x;
-        const int64_t k0 = h / P;
-        int64_t k1 = k0;
-        for (int64_t kb = k0 + 1;; kb += BLOCK * CB_SEARCH) {
-            uint32_t kk[CB_SEARCH];
+    // partial t of a segment's list: t = 0 slot 1 of k0, t = 1 slot 0 of
+    // k0+1, t >= 2 slot 0 of the (t-1)-th multiple of WG after k0+1
+    auto item = [&](int64_t k0, int64_t t) -> const double* {
+        const int64_t k = t == 0 ? k0 : (t == 1 ? k0 + 1 : ((k0 + 1) / WG + t - 1) * WG);
+        return a.carry + (k * 2 + (t == 0 ? 1 : 0)) * D + li * VEC;
+    };
+    auto n_items_of = [&](int64_t k0, int64_t k1) -> int64_t {
+        return k1 > k0 ? 2 + (k1 / WG - (k0 + 1) / WG) : 1;
+    };
+    for (int64_t ob = (int64_t)blockIdx.x * OPB; ob < n_owners; ob += (int64_t)gridDim.x * OPB) {
+        __syncthreads();       // s_coop and s_part of the previous chunk have been read
+        const int64_t o = ob + g;
+        bool coop = false;
+        if (g < OPB && o < n_owners) {
+            const Owner ow = a.owners[o];
+            if (ow.len == 0) {
+                coop = true;
+            } else {
+                const int64_t h = ow.head;
+                const int64_t k0 = h / P;
+                const int64_t n_items = n_items_of(k0, (h + (int64_t)ow.len - 1) / P);
+                char* row = a.rv.row(ow.key);
+                RowRegs<D, BF16> rr;
+                load_row<D, BF16, OPT>(row, li, rr);
+                double acc[VEC];
 #pragma unroll
-            for (int u = 0; u < CB_SEARCH; ++u) {
-                const int64_t k = kb + u * BLOCK + threadIdx.x;
-                kk[u] = a.pairs[(k < n_pieces ? k : n_pieces - 1) * P].x;
+                for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+                for (int64_t t0 = 0; t0 < n_items; t0 += U) {
+                    double src[U][VEC];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const double* p = item(k0, t0 + u < n_items ? t0 + u : n_items - 1);
+#pragma unroll
+                        for (int c = 0; c < VEC; ++c) src[u][c] = p[c];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (t0 + u < n_items)
+#pragma unroll
+                            for (int c = 0; c < VEC; ++c) acc[c] += src[u][c];
+                }
+                finish_row<D, BF16, OPT>(a, row, li, rr, acc);
             }
-            int cnt = 0;
-#pragma unroll
-            for (int u = 0; u < CB_SEARCH; ++u)
-                cnt += __syncthreads_count(kb + u * BLOCK + threadIdx.x < n_pieces && kk[u] == key);
-            k1 += cnt;
-            if (cnt < BLOCK * CB_SEARCH) break;
         }
-        // partial t of the list: t = 0 slot 1 of k0, t = 1 slot 0 of k0+1,
-        // t >= 2 slot 0 of the (t-1)-th multiple of WG after k0+1
-        constexpr int64_t WG = G::GPB;
-        const int64_t base = (k0 + 1) / WG;
-        const int64_t n_items = k1 > k0 ? 2 + (k1 / WG - base) : 1;
-        auto item = [&](int64_t t) -> const double* {
-            const int64_t k = t == 0 ? k0 : (t == 1 ? k0 + 1 : (base + t - 1) * WG);
-            return a.carry + (k * 2 + (t == 0 ? 1 : 0)) * D + li * VEC;
-        };
-        double acc[VEC];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
-        for (int64_t tq = g; tq < n_items; tq += U * GPB) {
-            double src[U][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const double* p = item(tq + u * GPB < n_items ? tq + u * GPB : n_items - 1);
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) src[u][c] = p[c];
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (tq + u * GPB < n_items)
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) acc[c] += src[u][c];
-        }
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) s_part[g][li * VEC + c] = acc[c];
+        if (li == 0) s_coop[g] = coop ? o : -1;
         __syncthreads();
-        if (g == 0) {
-            double tot[VEC];
+        for (int q = 0; q < OPB; ++q) {
+            const int64_t oc = s_coop[q];      // the same for every thread of the block
+            if (oc < 0) continue;
+            __syncthreads();                   // s_part of the previous owner has been read
+            const Owner ow = a.owners[oc];
+            const int64_t h = ow.head;
+            const uint32_t key = ow.key;
+            const int64_t k0 = h / P;
+            int64_t k1 = k0;
+            for (int64_t kb = k0 + 1;; kb += BLOCK * CB_SEARCH) {
+                uint32_t kk[CB_SEARCH];
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) tot[c] = s_part[0][li * VEC + c];
+                for (int u = 0; u < CB_SEARCH; ++u) {
+                    const int64_t k = kb + u * BLOCK + threadIdx.x;
+                    kk[u] = a.pairs[(k < n_pieces ? k : n_pieces - 1) * P].x;
+                }
+                int cnt = 0;
+#pragma unroll
+                for (int u = 0; u < CB_SEARCH; ++u)
+                    cnt += __syncthreads_count(kb + u * BLOCK + threadIdx.x < n_pieces && kk[u] == key);
+                k1 += cnt;
+                if (cnt < BLOCK * CB_SEARCH) break;
+            }
+            const int64_t n_items = n_items_of(k0, k1);
+            double acc[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) acc[c] = 0.0;
+            for (int64_t tq = g; tq < n_items; tq += U * GPB) {
+                double src[U][VEC];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const double* p = item(k0, tq + u * GPB < n_items ? tq + u * GPB : n_items - 1);
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) src[u][c] = p[c];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (tq + u * GPB < n_items)
+#pragma unroll
+                        for (int c = 0; c < VEC; ++c) acc[c] += src[u][c];
+            }
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) s_part[g][li * VEC + c] = acc[c];
+            __syncthreads();
+            if (g == 0) {
+                double tot[VEC];
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) tot[c] = s_part[0][li * VEC + c];
 #pragma unroll 1
-            for (int q = 1; q < GPB; ++q)
+                for (int q2 = 1; q2 < GPB; ++q2)
 #pragma unroll
-                for (int c = 0; c < VEC; ++c) tot[c] += s_part[q][li * VEC + c];
-            char* row = a.rv.row(key);
-            RowRegs<D, BF16> rr;
-            load_row<D, BF16, OPT>(row, li, rr);
-            finish_row<D, BF16, OPT>(a, row, li, rr, tot);
+                    for (int c = 0; c < VEC; ++c) tot[c] += s_part[q2][li * VEC + c];
+                char* row = a.rv.row(key);
+                RowRegs<D, BF16> rr;
+                load_row<D, BF16, OPT>(row, li, rr);
+                finish_row<D, BF16, OPT>(a, row, li, rr, tot);
+            }
         }
     }
 }
@@ -931,7 +998,7 @@ struct BwdWs {
     uint2* p0;
     uint2* p1;
     double* carry;
-    uint32_t* owners;
+    Owner* owners;
     uint2* singles;
     Multi* multis;
     void* sort_ws;
@@ -947,7 +1014,7 @@ BwdWs carve(void* base, int64_t n_ids, int64_t n_bags, int32_t dim, size_t* tota
     w.p0 = c.take<uint2>(n);
     w.p1 = c.take<uint2>(n);
     w.carry = c.take<double>(n_pieces * 2 * (size_t)dim);
-    w.owners = c.take<uint32_t>(n / (LONG_T + 1) + 1);
+    w.owners = c.take<Owner>(n / (LONG_T + 1) + 1);
     w.singles = c.take<uint2>(n);
     w.multis = c.take<Multi>(n / 2 + 1);
     w.sort_ws = c.take<char>(sort_workspace((int64_t)n, nullptr));
@@ -975,7 +1042,8 @@ int launch_update(BwdArgs a, int64_t n_ids, hipStream_t s) {
     const int m_blocks = N_XCD * ((fill_blocks(n_ids, G::GPB * 16, POOL_CAP) + N_XCD - 1) / N_XCD);
     const int64_t work_blocks = (int64_t)a.l_blocks + a.s_blocks + m_blocks;
     constexpr int CB = combine_block<D, BF16>();
-    const int cblocks = fill_blocks(n_pieces, 1, 2048 * 512 / CB);
+    // one chunk of owners per block; at most n / (LONG_T + 1) + 1 owners
+    const int cblocks = fill_blocks(n_ids / (LONG_T + 1) + 1, combine_owners_per_block<D, BF16>(), 2048 * 512 / CB);
     {
         TraceScope ts(RSE_K_SEG_UPDATE, s);
         // With no more lookups than bags (one-hot batches), a gradient row is
