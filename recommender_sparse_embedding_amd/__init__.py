@@ -2,7 +2,8 @@
 
 Every step of the path runs in the HIP library (include/rse.h); this module
 only marshals arguments: torch tensors provide device memory and the current
-HIP stream.  The functions keep the C ABI's names:
+HIP stream (large chunks of rows are physically contiguous HIP allocations,
+seen by torch as tensors).  The functions keep the C ABI's names:
 
     idmap_find_or_insert, embedding_bag_fwd, embedding_bag_bwd_update, blocks_grow
 
@@ -17,6 +18,7 @@ missing (there is no CPU fallback).
 from __future__ import annotations
 
 import ctypes
+import os
 import weakref
 from dataclasses import dataclass
 
@@ -63,8 +65,9 @@ def _bytes(n: int, device) -> torch.Tensor:
 # physically contiguous (hipExtMallocWithFlags with
 # hipDeviceMallocContiguous), which the GPU maps with its largest page
 # fragments.  Click-log step, 57 GB table of 1 KB rows in 16 GB chunks, 7
-# processes each: 0.541-0.569 ms (mean 0.556) with torch's allocations,
-# 0.536-0.548 ms (mean 0.541) with contiguous ones.  Rows that straddle
+# processes each on two GPUs: 0.541-0.569 ms (mean 0.556) with torch's
+# allocations, 0.536-0.548 ms (mean 0.541) with contiguous ones (on other
+# GPUs some processes still ran at the slower 0.555-0.568).  Rows that straddle
 # 128-byte lines stay on torch's memory: the merged-table update (192-byte
 # rows) wrote 4.3 GB per launch into contiguous chunks against 2.7 GB into
 # torch's, and ran 3% longer.  Where the driver cannot place a chunk, torch
@@ -75,11 +78,22 @@ _hip_rt = None
 
 
 def _hip():
-    """The HIP runtime torch has loaded (looked up by its soname, so this is
-    the same library instance, not a second runtime)."""
+    """The HIP runtime torch has loaded: the libamdhip64 already mapped into
+    this process, opened by its path (the same library instance, never a
+    second runtime)."""
     global _hip_rt
     if _hip_rt is None:
-        h = ctypes.CDLL("libamdhip64.so.7")
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                name = line.rstrip().split(" ")[-1]
+                if os.path.basename(name).startswith("libamdhip64.so"):
+                    path = name
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        h = ctypes.CDLL(path)
         h.hipExtMallocWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
         h.hipExtMallocWithFlags.restype = ctypes.c_int
         h.hipFree.argtypes = [ctypes.c_void_p]
