@@ -385,11 +385,13 @@ def run_workload(n: int, args, full_schedules: bool, steps: int, warmup: int) ->
     # short dependent kernels) run side by side instead of one after the
     # other.  Finds still run in batch order (one stream); a prepare waits
     # for its batch's find; the find of batch i+2 waits for the apply of
-    # batch i-2, the last reader of the offsets buffer it overwrites (4
-    # batches cycle), which also bounds how far the finds run ahead.
+    # batch i-1, as in the two-stream schedule (there through the sort that
+    # precedes it): the offsets buffer it overwrites was last read by the
+    # forward and the sort of batch i+2-nb (nb >= 3 batches cycle), both
+    # done before that apply.  This also bounds how far the finds run ahead.
 
     def la3_find(k):
-        finder.wait_event(applied[k % 2])             # the apply of batch k-4 (k-2 when primed) is done
+        finder.wait_event(applied[(k - 1) % 2])       # the apply of batch k-3 (recorded at step k-3)
         find(batch_at(k), finder)
         ready[k % 3].record(finder)
 

@@ -380,8 +380,8 @@ def test_pipelined_next_find_overlaps_apply(which, schedule):
     forward of s+1 waits for both).  lookahead: the second stream sorts batch
     s+1 (found a step earlier) and then finds batch s+2 while batch s runs.
     lookahead3: the same with the finds on a third stream, beside the sorts
-    (a sort waits for its batch's find, a find for the apply two batches
-    back).  Every step matches the oracle run in plain order, including new keys
+    (a sort waits for its batch's find, the find of batch s+2 for the apply
+    of batch s-1).  Every step matches the oracle run in plain order, including new keys
     inserted while earlier batches' rows are being updated."""
     if which == "click_log":
         cfg = synth.config(2, batch=2048, cardinality=("loguniform", 10, 200_000))
@@ -421,7 +421,7 @@ def test_pipelined_next_find_overlaps_apply(which, schedule):
     def find(s):
         x = inputs[s]
         if schedule == "lookahead3":
-            finder.wait_event(applied[s % 2])
+            finder.wait_event(applied[(s - 1) % 2])     # the apply of batch s-3
         rse.idmap_find_or_insert(gpu.map, gpu.blocks, x["ids"], x["bo"], cfg.batch, cfg.n_tables, x["ro"], n_new,
                                  ws=fws, stream=finder)
         found[s % 3].record(finder)
